@@ -1,0 +1,355 @@
+// C ABI of the IceCache library: argument checks, layout sizing and the
+// entry points declared in include/ice.h. Every check runs on the host before
+// anything is enqueued; device work goes to the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+
+#include "ice_launch.h"
+
+using namespace ice;
+
+namespace ice {
+size_t select_lds_bytes(int G, int budget);
+}
+
+struct ice_index {
+  ice_params p;
+  DevLayout L;
+  WsLayout W;
+  void* blob;
+  size_t blob_bytes;
+  int32_t n_tokens;
+  bool built;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ICE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_params(const ice_params* p) {
+  if (!p) return fail(ICE_ERR_ARG, "params is null");
+  if (p->n_heads < 1) return fail(ICE_ERR_ARG, "n_heads must be >= 1");
+  if (p->group < 1 || p->group > ICE_MAX_GROUP) return fail(ICE_ERR_ARG, "group must be in [1, %d]", ICE_MAX_GROUP);
+  if (p->d != 64 && p->d != 128) return fail(ICE_ERR_DTYPE, "d must be 64 or 128");
+  if (p->dtype != ICE_F32 && p->dtype != ICE_BF16) return fail(ICE_ERR_DTYPE, "dtype must be ICE_F32 or ICE_BF16");
+  if (p->page_cap != ICE_PAGE_CAP) return fail(ICE_ERR_ARG, "page_cap must be %d", ICE_PAGE_CAP);
+  if (p->levels < 1 || p->levels > ICE_MAX_LEVELS) return fail(ICE_ERR_ARG, "levels must be in [1, %d]", ICE_MAX_LEVELS);
+  if (p->promote_log2 < 1 || p->promote_log2 > 16) return fail(ICE_ERR_ARG, "promote_log2 must be in [1, 16]");
+  if (p->capacity < 1 || p->capacity > (1 << 28)) return fail(ICE_ERR_ARG, "capacity must be in [1, 2^28]");
+  return ICE_OK;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+struct Cursor {
+  int64_t off = 0;
+  int64_t take(int64_t bytes) {
+    const int64_t o = off;
+    off = align256(off + std::max<int64_t>(bytes, 0));
+    return o;
+  }
+};
+
+// Page bound of one table: every owner's pages are full except its last, so
+// pages = sum over owners of ceil(c/16) <= (points + 15 * owners) / 16.
+int32_t page_bound(int64_t points, int64_t owners) {
+  return (int32_t)((points + 15 * std::max<int64_t>(owners, 1) + 15) / 16);
+}
+
+void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
+  memset(L, 0, sizeof(*L));
+  memset(W, 0, sizeof(*W));
+  L->H = p->n_heads;
+  L->G = p->group;
+  L->d = p->d;
+  L->dtype = p->dtype;
+  L->L = p->levels;
+  L->plog2 = p->promote_log2;
+  L->cap = p->capacity;
+  L->ntab = std::max(1, p->levels - 1);
+  L->seed = p->seed;
+  L->elt = p->dtype == ICE_BF16 ? 2 : 4;
+  // level counts over every position a head can ever hold
+  L->ncap[0] = p->capacity;
+  for (int h = 0; h < p->n_heads; ++h) {
+    int32_t c[ICE_MAX_LEVELS] = {0, 0, 0, 0};
+    for (int t = 0; t < p->capacity; ++t) {
+      const int lv = draw_level(p->seed, h, t, p->levels, p->promote_log2);
+      for (int l = 1; l <= lv; ++l) ++c[l];
+    }
+    for (int l = 1; l < p->levels; ++l) L->ncap[l] = std::max(L->ncap[l], c[l]);
+  }
+  for (int l = 0; l < L->ntab; ++l) {
+    const int64_t owners = l + 1 < p->levels ? L->ncap[l + 1] : 0;
+    L->pcap[l] = page_bound(L->ncap[l], owners);
+  }
+  L->topcap = p->levels >= 2 ? std::max(L->ncap[1], 1) : 0;
+  const int64_t d = p->d, elt = L->elt, cap = p->capacity;
+  Cursor c;
+  L->off_hdr = c.take(sizeof(Hdr));
+  L->off_lev = c.take(cap);
+  L->off_e = c.take(cap * 4);
+  for (int l = 0; l < L->ntab; ++l) L->off_parent[l] = c.take(cap * 4);
+  for (int l = 0; l < L->ntab; ++l) {
+    const int64_t P = L->pcap[l];
+    L->off_pg_tok[l] = c.take(P * ICE_PAGE_CAP * 4);
+    L->off_pg_cnt[l] = c.take(P * 4);
+    L->off_pg_next[l] = c.take(P * 4);
+    L->off_pg_owner[l] = c.take(P * 4);
+    L->off_first[l] = c.take((cap + 1) * 4);
+    L->off_tail[l] = c.take((cap + 1) * 4);
+    L->off_pgK[l] = c.take(P * ICE_PAGE_CAP * d * elt);
+    if (l == 0) L->off_pgV = c.take(P * ICE_PAGE_CAP * d * elt);
+    else L->off_pgE[l] = c.take(P * ICE_PAGE_CAP * 4);
+  }
+  L->off_top_tok = c.take((int64_t)L->topcap * 4);
+  L->off_top_K = c.take((int64_t)L->topcap * d * elt);
+  L->off_top_E = c.take((int64_t)L->topcap * 4);
+  L->head_bytes = c.off;
+
+  // build workspace per head
+  W->kp = p->dtype == ICE_BF16 ? p->d + 16 : p->d + 4;
+  Cursor w;
+  W->off_n2 = w.take(cap * 8);
+  for (int l = 1; l < p->levels; ++l) W->off_rank[l] = w.take(cap * 4);
+  for (int l = 1; l < p->levels; ++l) W->off_pts[l] = w.take((int64_t)L->ncap[l] * 4);
+  for (int l = 0; l < p->levels; ++l) W->off_exact[l] = w.take((int64_t)L->ncap[l] * 4);
+  W->off_cnts = w.take(2 * ICE_MAX_LEVELS * 4);
+  const int64_t n1 = p->levels >= 2 ? L->ncap[1] : 0;
+  W->off_opA = w.take(n1 * W->kp * elt);
+  W->off_s1 = w.take(cap * 4);
+  W->off_s2 = w.take(cap * 4);
+  W->off_oloc = w.take(cap * 4);
+  W->off_cnt = w.take((n1 + 1) * 4);
+  W->off_fill = w.take((n1 + 1) * 4);
+  W->off_cbase = w.take((n1 + 1) * 4);
+  W->off_pbase = w.take((n1 + 1) * 4);
+  W->off_btok = w.take(cap * 4);
+  W->off_bkey = w.take(cap * 4);
+  W->off_bown = w.take(cap * 4);
+  W->head_bytes = w.off;
+  W->build_bytes = W->head_bytes * p->n_heads;
+}
+
+int64_t attend_ws_bytes(const DevLayout& L, int uni_stride) {
+  return align256((int64_t)L.H * attend_splits(uni_stride) * L.G * (L.d + 2) * 4);
+}
+
+int check_budget(const ice_index* idx, int32_t budget) {
+  if (budget < ICE_PAGE_CAP || budget % ICE_PAGE_CAP != 0 || budget > ICE_MAX_BEAM * ICE_PAGE_CAP)
+    return fail(ICE_ERR_ARG, "budget_tokens must be a positive multiple of %d, at most %d", ICE_PAGE_CAP,
+                ICE_MAX_BEAM * ICE_PAGE_CAP);
+  (void)idx;
+  return ICE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ice_last_error(void) { return g_err.c_str(); }
+
+size_t ice_index_bytes(const ice_params* p) {
+  if (check_params(p) != ICE_OK) return 0;
+  DevLayout L;
+  WsLayout W;
+  make_layout(p, &L, &W);
+  return (size_t)(L.head_bytes * p->n_heads);
+}
+
+size_t ice_workspace_bytes(const ice_params* p, int32_t max_budget_tokens) {
+  if (check_params(p) != ICE_OK) return 0;
+  if (max_budget_tokens < ICE_PAGE_CAP || max_budget_tokens % ICE_PAGE_CAP != 0 ||
+      max_budget_tokens > ICE_MAX_BEAM * ICE_PAGE_CAP) {
+    fail(ICE_ERR_ARG, "max_budget_tokens must be a positive multiple of %d", ICE_PAGE_CAP);
+    return 0;
+  }
+  DevLayout L;
+  WsLayout W;
+  make_layout(p, &L, &W);
+  const int64_t att = attend_ws_bytes(L, p->group * (max_budget_tokens / ICE_PAGE_CAP));
+  return (size_t)std::max<int64_t>(W.build_bytes, att);
+}
+
+int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_index** out) {
+  if (!out) return fail(ICE_ERR_ARG, "out is null");
+  *out = nullptr;
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!index_dev) return fail(ICE_ERR_ARG, "index blob is null");
+  if (((uintptr_t)index_dev & 255u) != 0) return fail(ICE_ERR_ARG, "index blob must be 256-byte aligned");
+  ice_index* idx = new (std::nothrow) ice_index;
+  if (!idx) return fail(ICE_ERR_ARG, "out of host memory");
+  idx->p = *p;
+  make_layout(p, &idx->L, &idx->W);
+  if (index_bytes < (size_t)(idx->L.head_bytes * p->n_heads)) {
+    delete idx;
+    return fail(ICE_ERR_CAPACITY, "index blob has %zu bytes, needs %lld", index_bytes,
+                (long long)(idx->L.head_bytes * p->n_heads));
+  }
+  idx->blob = index_dev;
+  idx->blob_bytes = index_bytes;
+  idx->n_tokens = 0;
+  idx->built = false;
+  *out = idx;
+  return ICE_OK;
+}
+
+void ice_destroy(ice_index* idx) { delete idx; }
+
+int32_t ice_n_tokens(const ice_index* idx) { return idx ? idx->n_tokens : -1; }
+
+int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, void* ws,
+              size_t ws_bytes, void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (n_tokens < 0) return fail(ICE_ERR_ARG, "n_tokens must be >= 0");
+  if (n_tokens > idx->p.capacity)
+    return fail(ICE_ERR_CAPACITY, "n_tokens %d exceeds capacity %d", n_tokens, idx->p.capacity);
+  if (n_tokens > 0) {
+    if (!K || !V) return fail(ICE_ERR_ARG, "K or V is null");
+    if (head_stride < (int64_t)n_tokens * idx->p.d) return fail(ICE_ERR_ARG, "head_stride smaller than n_tokens*d");
+    if (!aligned16(K) || !aligned16(V) || (head_stride * idx->L.elt) % 16 != 0)
+      return fail(ICE_ERR_ARG, "K, V and the head stride must be 16-byte aligned");
+  }
+  if (!ws || ws_bytes < (size_t)idx->W.build_bytes)
+    return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, build needs %lld", ws_bytes,
+                (long long)idx->W.build_bytes);
+  if (((uintptr_t)ws & 255u) != 0) return fail(ICE_ERR_ARG, "workspace must be 256-byte aligned");
+  hipError_t e = launch_build(idx->L, idx->W, idx->blob, K, V, n_tokens, head_stride, ws,
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ice_build launch");
+  idx->n_tokens = n_tokens;
+  idx->built = true;
+  return ICE_OK;
+}
+
+int ice_insert(ice_index* idx, const void* k_new, const void* v_new, int32_t n_new, void* ws, size_t ws_bytes,
+               void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (!idx->built) return fail(ICE_ERR_STATE, "insert before build");
+  if (n_new < 0) return fail(ICE_ERR_ARG, "n_new must be >= 0");
+  if (n_new == 0) return ICE_OK;
+  if (!k_new || !v_new) return fail(ICE_ERR_ARG, "k_new or v_new is null");
+  if ((int64_t)idx->n_tokens + n_new > idx->p.capacity)
+    return fail(ICE_ERR_CAPACITY, "insert of %d tokens exceeds capacity %d (holds %d)", n_new, idx->p.capacity,
+                idx->n_tokens);
+  hipError_t e = launch_insert(idx->L, idx->blob, k_new, v_new, n_new, idx->n_tokens,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ice_insert launch");
+  idx->n_tokens += n_new;
+  return ICE_OK;
+}
+
+int ice_select(const ice_index* idx, const void* Q, int32_t budget_tokens, int32_t beam, int32_t* sel,
+               int32_t* uni, int32_t* n_uni, int32_t* trace, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (!idx->built) return fail(ICE_ERR_STATE, "select before build");
+  int rc = check_budget(idx, budget_tokens);
+  if (rc) return rc;
+  if (beam < 1 || beam > ICE_MAX_BEAM) return fail(ICE_ERR_ARG, "beam must be in [1, %d]", ICE_MAX_BEAM);
+  if (!Q || !sel || !uni || !n_uni) return fail(ICE_ERR_ARG, "Q, sel, uni or n_uni is null");
+  if (!aligned16(Q)) return fail(ICE_ERR_ARG, "Q must be 16-byte aligned");
+  hipError_t e = launch_select(idx->L, idx->blob, Q, budget_tokens, beam, sel, uni, n_uni, trace,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ice_select launch");
+  return ICE_OK;
+}
+
+int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const int32_t* n_uni, int32_t uni_stride,
+               float scale, float* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (!idx->built) return fail(ICE_ERR_STATE, "attend before build");
+  if (!Q || !uni || !n_uni || !O) return fail(ICE_ERR_ARG, "Q, uni, n_uni or O is null");
+  if (uni_stride < 1 || uni_stride > ICE_MAX_GROUP * ICE_MAX_BEAM)
+    return fail(ICE_ERR_ARG, "uni_stride must be in [1, %d]", ICE_MAX_GROUP * ICE_MAX_BEAM);
+  const int64_t need = attend_ws_bytes(idx->L, uni_stride);
+  if (!ws || ws_bytes < (size_t)need)
+    return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, attend needs %lld", ws_bytes, (long long)need);
+  hipError_t e = launch_attend(idx->L, idx->blob, Q, uni, n_uni, uni_stride, scale, O, lse, ws,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ice_attend launch");
+  return ICE_OK;
+}
+
+size_t ice_export_bytes(const ice_index* idx, int32_t what, int32_t level) {
+  if (!idx) return 0;
+  const DevLayout& L = idx->L;
+  const int64_t cap = L.cap, elt = L.elt, d = L.d;
+  const bool tab_ok = level >= 0 && level < L.ntab;
+  switch (what) {
+    case ICE_EXP_LEVEL: return cap;
+    case ICE_EXP_LIFT: return cap * 4;
+    case ICE_EXP_PARENT: return tab_ok ? cap * 4 : 0;
+    case ICE_EXP_PAGE_TOK: return tab_ok ? (size_t)L.pcap[level] * ICE_PAGE_CAP * 4 : 0;
+    case ICE_EXP_PAGE_CNT:
+    case ICE_EXP_PAGE_NEXT:
+    case ICE_EXP_PAGE_OWNER: return tab_ok ? (size_t)L.pcap[level] * 4 : 0;
+    case ICE_EXP_OWNER_FIRST:
+    case ICE_EXP_OWNER_TAIL: return tab_ok ? (cap + 1) * 4 : 0;
+    case ICE_EXP_TOP: return (size_t)L.topcap * 4;
+    case ICE_EXP_PAGE_K: return tab_ok ? (size_t)L.pcap[level] * ICE_PAGE_CAP * d * elt : 0;
+    case ICE_EXP_PAGE_V: return level == 0 ? (size_t)L.pcap[0] * ICE_PAGE_CAP * d * elt : 0;
+    case ICE_EXP_HEADER: return sizeof(ice_head_stats);
+    default: return 0;
+  }
+}
+
+int ice_export(const ice_index* idx, int32_t head, int32_t what, int32_t level, void* dst, size_t dst_bytes,
+               void* stream) {
+  if (!idx || !dst) return fail(ICE_ERR_ARG, "index or dst is null");
+  if (head < 0 || head >= idx->p.n_heads) return fail(ICE_ERR_ARG, "head out of range");
+  const size_t n = ice_export_bytes(idx, what, level);
+  if (n == 0) return fail(ICE_ERR_ARG, "nothing to export for what=%d level=%d", what, level);
+  if (dst_bytes < n) return fail(ICE_ERR_ARG, "dst has %zu bytes, needs %zu", dst_bytes, n);
+  const DevLayout& L = idx->L;
+  int64_t off = 0;
+  switch (what) {
+    case ICE_EXP_LEVEL: off = L.off_lev; break;
+    case ICE_EXP_LIFT: off = L.off_e; break;
+    case ICE_EXP_PARENT: off = L.off_parent[level]; break;
+    case ICE_EXP_PAGE_TOK: off = L.off_pg_tok[level]; break;
+    case ICE_EXP_PAGE_CNT: off = L.off_pg_cnt[level]; break;
+    case ICE_EXP_PAGE_NEXT: off = L.off_pg_next[level]; break;
+    case ICE_EXP_PAGE_OWNER: off = L.off_pg_owner[level]; break;
+    case ICE_EXP_OWNER_FIRST: off = L.off_first[level]; break;
+    case ICE_EXP_OWNER_TAIL: off = L.off_tail[level]; break;
+    case ICE_EXP_TOP: off = L.off_top_tok; break;
+    case ICE_EXP_PAGE_K: off = L.off_pgK[level]; break;
+    case ICE_EXP_PAGE_V: off = L.off_pgV; break;
+    case ICE_EXP_HEADER: off = L.off_hdr; break;
+    default: return fail(ICE_ERR_ARG, "unknown export %d", what);
+  }
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ice_export sync");
+  const char* src = static_cast<const char*>(idx->blob) + (int64_t)head * L.head_bytes + off;
+  e = hipMemcpy(dst, src, n, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "ice_export copy");
+  return ICE_OK;
+}
+
+}  // extern "C"

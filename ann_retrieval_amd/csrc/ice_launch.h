@@ -1,0 +1,29 @@
+// Host-side launchers of the HIP kernels, one group per source file.
+#pragma once
+
+#include "ice_common.h"
+
+namespace ice {
+
+// k_build.hip
+hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
+                        int n_tokens, int64_t head_stride, void* ws, hipStream_t s);
+// k_gemm.hip: nearest parent of every level-`level` point among the level-(level+1) points
+hipError_t launch_parent_gemm(const DevLayout& L, const WsLayout& W, void* blob, const void* K,
+                              int64_t head_stride, void* ws, int level, hipStream_t s);
+// k_insert.hip
+hipError_t launch_insert(const DevLayout& L, void* blob, const void* k_new, const void* v_new, int n_new,
+                         int t0, hipStream_t s);
+// k_select.hip
+hipError_t launch_select(const DevLayout& L, const void* blob, const void* Q, int budget, int beam,
+                         int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace, hipStream_t s);
+// k_attend.hip
+int attend_splits(int uni_stride);
+hipError_t launch_attend(const DevLayout& L, const void* blob, const void* Q, const int32_t* uni,
+                         const int32_t* n_uni, int uni_stride, float scale, float* O, float* lse, void* ws,
+                         hipStream_t s);
+// fills `n` int32 words at byte offset `off` of every head region
+hipError_t launch_fill_heads(void* base, int64_t head_bytes, int H, int64_t off, int64_t n, int32_t value,
+                             hipStream_t s);
+
+}  // namespace ice

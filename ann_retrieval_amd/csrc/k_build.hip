@@ -1,0 +1,502 @@
+// Index build kernels: key norms and promotion levels, the lift and the
+// level lists, the parent-GEMM operand, the deterministic page pack and the
+// row copies into the page pool.
+//
+// What is computed follows the aitangshan.cn IceCache article, section 3
+// (lift keys so inner product becomes Euclidean distance; random promotion
+// into a pyramid of levels; each point's parent is its most similar point one
+// level up; points sharing a parent share a page) and the papernotes.org
+// IceCache notes, key designs 1-2 (each node is one physical page).
+#include "ice_launch.h"
+
+#include <math.h>
+
+namespace ice {
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+// Exclusive prefix sum over the 1024 threads of a block. `total` receives the
+// block sum. `lds` needs 16 ints.
+__device__ inline int block_scan_excl(int v, int* lds, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int y = __shfl_up(x, m, 64);
+    if (lane >= m) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    const int s = lds[w];
+    if (w < wave) before += s;
+    all += s;
+  }
+  __syncthreads();
+  total = all;
+  return before + x - v;
+}
+
+__global__ void k_fill_heads(void* base, int64_t head_bytes, int64_t off, int64_t n, int32_t value) {
+  int32_t* p = at<int32_t>(static_cast<char*>(base) + (int64_t)blockIdx.y * head_bytes, off);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+// |k|^2 in fp64 (exact products for bf16 and fp32 inputs), the promotion
+// level, and the per-head maximum M^2. One block covers 64 tokens of a head.
+template <int D, class T>
+__global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, void* blob, const T* K,
+                                                    int64_t hstride, int n, void* ws) {
+  using G = RowGeo<D, T>;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const T* Kh = K + (int64_t)h * hstride;
+  void* hb = head_base(blob, L, h);
+  double* n2 = at<double>(static_cast<char*>(ws) + (int64_t)h * W.head_bytes, W.off_n2);
+  int8_t* lev = at<int8_t>(hb, L.off_lev);
+  double mx = 0.0;
+  const int base = blockIdx.x * 64 + wave * 16;
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += G::RPP) {
+    const int t = base + r0 + lane / G::LPR;
+    double acc = 0.0;
+    if (t < n) {
+      const V4 v = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Kh + (int64_t)t * D) +
+                                                (lane % G::LPR) * 16);
+      float f[G::EPL];
+      Elt<T>::unpack(v, f);
+#pragma unroll
+      for (int i = 0; i < G::EPL; ++i) acc += (double)f[i] * (double)f[i];
+    }
+    acc = group_sum_d<G::LPR>(acc);
+    if (t < n && (lane % G::LPR) == 0) {
+      n2[t] = acc;
+      lev[t] = (int8_t)draw_level(L.seed, h, t, L.L, L.plog2);
+      mx = fmax(mx, acc);
+    }
+  }
+  __shared__ double red[4];
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double b = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    // Non-negative doubles order like their bit patterns.
+    if (b > 0.0)
+      atomicMax(reinterpret_cast<unsigned long long*>(&at<Hdr>(hb, L.off_hdr)->M2),
+                (unsigned long long)__double_as_longlong(b));
+  }
+}
+
+// Lift coordinate e = sqrt(max(0, M^2 - |k|^2)) and the stable level lists:
+// pts[l] (level >= l, ascending), rank[l], exact[l] (level == l). One block
+// of 1024 threads per head walks the tokens in order.
+__global__ __launch_bounds__(kScanThreads) void k_lift_compact(DevLayout L, WsLayout W, void* blob, void* ws,
+                                                              int n) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  Hdr* hdr = at<Hdr>(hb, L.off_hdr);
+  const double M2 = hdr->M2;
+  const double* n2 = at<double>(wh, W.off_n2);
+  const int8_t* lev = at<int8_t>(hb, L.off_lev);
+  float* e = at<float>(hb, L.off_e);
+  constexpr int NFMAX = 2 * ICE_MAX_LEVELS;
+  __shared__ int wsum[16][NFMAX];
+  __shared__ int run[NFMAX];
+  const int NL = L.L;
+  if (tid < NFMAX) run[tid] = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += kScanThreads) {
+    const int t = base + tid;
+    const bool valid = t < n;
+    const int lv = valid ? lev[t] : -1;
+    if (valid) e[t] = (float)sqrt(fmax(0.0, M2 - n2[t]));
+    uint64_t masks[NFMAX];
+#pragma unroll
+    for (int f = 0; f < NFMAX; ++f) {
+      bool fl = false;
+      if (f < NL) fl = lv >= f;
+      else if (f >= ICE_MAX_LEVELS && f - ICE_MAX_LEVELS < NL) fl = lv == f - ICE_MAX_LEVELS;
+      masks[f] = __ballot(fl);
+      if (lane == 0) wsum[wave][f] = __popcll(masks[f]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < NFMAX; ++f) {
+      int off = run[f];
+      for (int w = 0; w < wave; ++w) off += wsum[w][f];
+      const int pos = off + __popcll(masks[f] & ((1ull << lane) - 1ull));
+      const bool fl = (masks[f] >> lane) & 1ull;
+      if (f >= 1 && f < NL) {
+        if (fl) at<int32_t>(wh, W.off_pts[f])[pos] = t;
+        if (valid) at<int32_t>(wh, W.off_rank[f])[t] = fl ? pos : -1;
+      } else if (f >= ICE_MAX_LEVELS && fl) {
+        at<int32_t>(wh, W.off_exact[f - ICE_MAX_LEVELS])[pos] = t;
+      }
+    }
+    __syncthreads();
+    if (tid < NFMAX) {
+      int s = 0;
+      for (int w = 0; w < 16; ++w) s += wsum[w][tid];
+      run[tid] += s;
+    }
+    __syncthreads();
+  }
+  int Ltop = 0;
+  for (int l = 1; l < NL; ++l)
+    if (run[l] > 0) Ltop = l;
+  if (tid == 0) {
+    int32_t* cnts = at<int32_t>(wh, W.off_cnts);
+    for (int l = 0; l < ICE_MAX_LEVELS; ++l) {
+      cnts[l] = l < NL ? run[l] : 0;
+      cnts[ICE_MAX_LEVELS + l] = l < NL ? run[ICE_MAX_LEVELS + l] : 0;
+    }
+    hdr->n_tokens = n;
+    hdr->top_level = Ltop;
+    hdr->n_top = Ltop >= 1 ? run[Ltop] : 0;
+  }
+  if (Ltop >= 1) {
+    const int32_t* pts = at<int32_t>(wh, W.off_pts[Ltop]);
+    int32_t* top = at<int32_t>(hb, L.off_top_tok);
+    for (int i = tid; i < run[Ltop]; i += kScanThreads) top[i] = pts[i];
+  }
+}
+
+// Operand rows of the candidate parents (points of level `level`+1):
+// bf16: [key (D) | e0 e1 e0 e2 e0 e1 | 0 ...] with e = e0+e1+e2 split in
+// bf16 parts, so that one extra MFMA step adds e_child * e_parent to the
+// key inner product; fp32: [key | e | 0 0 0].
+template <int D, class T>
+__global__ void k_gather_opA(DevLayout L, WsLayout W, const void* blob, const T* K, int64_t hstride, void* ws,
+                             int level) {
+  const int h = blockIdx.y;
+  const void* hb = head_base(blob, L, h);
+  if (level >= at<Hdr>(hb, L.off_hdr)->top_level) return;
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const int n_cand = at<int32_t>(wh, W.off_cnts)[level + 1];
+  const int32_t* pts = at<int32_t>(wh, W.off_pts[level + 1]);
+  const float* e = at<float>(hb, L.off_e);
+  T* opA = at<T>(wh, W.off_opA);
+  const T* Kh = K + (int64_t)h * hstride;
+  const int kp = W.kp;
+  const int64_t total = (int64_t)n_cand * kp;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(i / kp), c = (int)(i % kp);
+    const int tok = pts[r];
+    T out;
+    if (c < D) {
+      out = Kh[(int64_t)tok * D + c];
+    } else if constexpr (sizeof(T) == 4) {
+      out = (c == D) ? e[tok] : 0.0f;
+    } else {
+      const float ev = e[tok];
+      const uint16_t p0 = f32_to_bf16(ev);
+      const float r1 = ev - bf16_to_f32(p0);
+      const uint16_t p1 = f32_to_bf16(r1);
+      const uint16_t p2 = f32_to_bf16(r1 - bf16_to_f32(p1));
+      const int j = c - D;
+      out = j == 0 || j == 2 || j == 4 ? p0 : j == 1 || j == 5 ? p1 : j == 3 ? p2 : (uint16_t)0;
+    }
+    opA[i] = out;
+  }
+}
+
+// ---- page pack -------------------------------------------------------------
+// Level-`level` points are grouped by owner (their level-(level+1) parent),
+// owners walked in ascending token id; inside an owner the owner itself comes
+// first, then its children by descending parent score (= ascending lifted
+// distance), equal scores by ascending token id; every owner's run is cut into
+// pages of 16 with consecutive ids. With no promoted point (root mode) a
+// virtual root owns every token in token order.
+
+struct PackView {
+  bool skip, root;
+  int n_pts, n_own;
+  const int32_t* pts;   // nullptr at level 0 (point index = token id)
+};
+
+__device__ inline PackView pack_view(const DevLayout& L, const WsLayout& W, const void* hb, const char* wh,
+                                     int level) {
+  PackView v;
+  const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
+  const int Ltop = hdr->top_level;
+  v.root = Ltop == 0;
+  v.skip = v.root ? level != 0 : level >= Ltop;
+  const int32_t* cnts = at<int32_t>(wh, W.off_cnts);
+  v.n_pts = level == 0 ? hdr->n_tokens : cnts[level];
+  v.n_own = v.root ? 1 : cnts[level + 1];
+  v.pts = level == 0 ? nullptr : at<int32_t>(wh, W.off_pts[level]);
+  return v;
+}
+
+__global__ void k_pack_count(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const PackView v = pack_view(L, W, hb, wh, level);
+  if (v.skip) return;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= v.n_pts) return;
+  const int t = v.pts ? v.pts[i] : i;
+  int o = 0;
+  if (!v.root) {
+    int32_t* parent = at<int32_t>(hb, L.off_parent[level]);
+    const int8_t* lev = at<int8_t>(hb, L.off_lev);
+    int ow;
+    if (lev[t] >= level + 1) {
+      ow = t;
+      parent[t] = t;
+      at<float>(wh, W.off_s1)[t] = INFINITY;   // the owner leads its own run
+    } else {
+      ow = parent[t];
+    }
+    o = at<int32_t>(wh, W.off_rank[level + 1])[ow];
+  }
+  at<int32_t>(wh, W.off_oloc)[i] = o;
+  atomicAdd(at<int32_t>(wh, W.off_cnt) + o, 1);
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_pack_scan(DevLayout L, WsLayout W, void* blob, void* ws,
+                                                           int level) {
+  const int h = blockIdx.x;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const PackView v = pack_view(L, W, hb, wh, level);
+  if (v.skip) return;
+  __shared__ int lds[16];
+  const int32_t* cnt = at<int32_t>(wh, W.off_cnt);
+  int32_t* cbase = at<int32_t>(wh, W.off_cbase);
+  int32_t* pbase = at<int32_t>(wh, W.off_pbase);
+  int32_t* fill = at<int32_t>(wh, W.off_fill);
+  const int32_t* owners = v.root ? nullptr : at<int32_t>(wh, W.off_pts[level + 1]);
+  int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[level]);
+  int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[level]);
+  int32_t* pg_next = at<int32_t>(hb, L.off_pg_next[level]);
+  int32_t* pg_owner = at<int32_t>(hb, L.off_pg_owner[level]);
+  int32_t* first = at<int32_t>(hb, L.off_first[level]);
+  int32_t* tail = at<int32_t>(hb, L.off_tail[level]);
+  int runc = 0, runp = 0;
+  for (int base = 0; base < v.n_own; base += kScanThreads) {
+    const int o = base + threadIdx.x;
+    const int c = o < v.n_own ? cnt[o] : 0;
+    const int np = (c + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP;
+    int totc, totp;
+    const int cb = runc + block_scan_excl(c, lds, totc);
+    const int pb = runp + block_scan_excl(np, lds, totp);
+    if (o < v.n_own) {
+      cbase[o] = cb;
+      pbase[o] = pb;
+      fill[o] = 0;
+      const int tok = v.root ? ICE_ROOT : owners[o];
+      const int slot = v.root ? L.cap : tok;
+      first[slot] = np ? pb : -1;
+      tail[slot] = np ? pb + np - 1 : -1;
+      for (int j = 0; j < np; ++j) {
+        const int p = pb + j;
+        const int pc = min(ICE_PAGE_CAP, c - j * ICE_PAGE_CAP);
+        pg_owner[p] = tok;
+        pg_next[p] = j + 1 < np ? p + 1 : -1;
+        pg_cnt[p] = pc;
+        for (int s = pc; s < ICE_PAGE_CAP; ++s) pg_tok[(int64_t)p * ICE_PAGE_CAP + s] = -1;
+      }
+    }
+    runc += totc;
+    runp += totp;
+  }
+  if (threadIdx.x == 0) at<Hdr>(hb, L.off_hdr)->n_pages[level] = runp;
+}
+
+__global__ void k_pack_scatter(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const PackView v = pack_view(L, W, hb, wh, level);
+  if (v.skip) return;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= v.n_pts) return;
+  const int t = v.pts ? v.pts[i] : i;
+  const int o = at<int32_t>(wh, W.off_oloc)[i];
+  const int pos = at<int32_t>(wh, W.off_cbase)[o] + atomicAdd(at<int32_t>(wh, W.off_fill) + o, 1);
+  at<int32_t>(wh, W.off_btok)[pos] = t;
+  at<float>(wh, W.off_bkey)[pos] = v.root ? 0.0f : at<float>(wh, W.off_s1)[t];
+  at<int32_t>(wh, W.off_bown)[pos] = o;
+}
+
+// Final slot of every bucketed point = its rank inside the owner's bucket by
+// (score desc, token asc). Consecutive positions share a bucket, so the lanes
+// of a wave mostly loop over the same bucket.
+__global__ void k_pack_place(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const PackView v = pack_view(L, W, hb, wh, level);
+  if (v.skip) return;
+  const int pos = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pos >= v.n_pts) return;
+  const int32_t* btok = at<int32_t>(wh, W.off_btok);
+  const float* bkey = at<float>(wh, W.off_bkey);
+  const int o = at<int32_t>(wh, W.off_bown)[pos];
+  const int b = at<int32_t>(wh, W.off_cbase)[o];
+  const int c = at<int32_t>(wh, W.off_cnt)[o];
+  const float key = bkey[pos];
+  const int t = btok[pos];
+  int r = 0;
+  for (int j = b; j < b + c; ++j) {
+    const float kj = bkey[j];
+    const int tj = btok[j];
+    r += (kj > key) || (kj == key && tj < t);
+  }
+  const int page = at<int32_t>(wh, W.off_pbase)[o] + r / ICE_PAGE_CAP;
+  at<int32_t>(hb, L.off_pg_tok[level])[(int64_t)page * ICE_PAGE_CAP + r % ICE_PAGE_CAP] = t;
+}
+
+// Rows of the page table into its key (and, at level 0, value) pool; empty
+// slots are zero. Upper tables also keep each point's lift coordinate.
+template <int D, class T>
+__global__ __launch_bounds__(256) void k_copy_pages(DevLayout L, const T* K, const T* V, int64_t hstride,
+                                                    void* blob, int level) {
+  using G = RowGeo<D, T>;
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
+  const bool root = hdr->top_level == 0;
+  if (root ? level != 0 : level >= hdr->top_level) return;
+  const int n_pages = hdr->n_pages[level];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[level]);
+  T* pk = at<T>(hb, L.off_pgK[level]);
+  T* pv = level == 0 ? at<T>(hb, L.off_pgV) : nullptr;
+  float* pe = level == 0 ? nullptr : at<float>(hb, L.off_pgE[level]);
+  const float* e = at<float>(hb, L.off_e);
+  const T* Kh = K + (int64_t)h * hstride;
+  const T* Vh = V + (int64_t)h * hstride;
+  const int nrows = n_pages * ICE_PAGE_CAP;
+  for (int r0 = (blockIdx.x * 4 + wave) * G::RPP; r0 < nrows; r0 += gridDim.x * 4 * G::RPP) {
+    const int r = r0 + lane / G::LPR;
+    if (r >= nrows) continue;
+    const int tok = pg_tok[r];
+    const int64_t so = (lane % G::LPR) * 16;
+    V4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+    if (tok >= 0) {
+      kv = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Kh + (int64_t)tok * D) + so);
+      if (pv) vv = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Vh + (int64_t)tok * D) + so);
+    }
+    *reinterpret_cast<V4*>(reinterpret_cast<char*>(pk + (int64_t)r * D) + so) = kv;
+    if (pv) *reinterpret_cast<V4*>(reinterpret_cast<char*>(pv + (int64_t)r * D) + so) = vv;
+    if (pe && (lane % G::LPR) == 0) pe[r] = tok >= 0 ? e[tok] : 0.0f;
+  }
+}
+
+template <int D, class T>
+__global__ __launch_bounds__(256) void k_copy_top(DevLayout L, const T* K, int64_t hstride, void* blob) {
+  using G = RowGeo<D, T>;
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
+  const int n_top = hdr->n_top;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t* top = at<int32_t>(hb, L.off_top_tok);
+  T* tk = at<T>(hb, L.off_top_K);
+  float* te = at<float>(hb, L.off_top_E);
+  const float* e = at<float>(hb, L.off_e);
+  const T* Kh = K + (int64_t)h * hstride;
+  for (int r0 = (blockIdx.x * 4 + wave) * G::RPP; r0 < n_top; r0 += gridDim.x * 4 * G::RPP) {
+    const int r = r0 + lane / G::LPR;
+    if (r >= n_top) continue;
+    const int tok = top[r];
+    const int64_t so = (lane % G::LPR) * 16;
+    *reinterpret_cast<V4*>(reinterpret_cast<char*>(tk + (int64_t)r * D) + so) =
+        *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Kh + (int64_t)tok * D) + so);
+    if ((lane % G::LPR) == 0) te[r] = e[tok];
+  }
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per < 1 ? 1 : (n + per - 1) / per); }
+
+template <int D, class T>
+hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const void* Kv, const void* Vv,
+                       int n, int64_t hstride, void* ws, hipStream_t s) {
+  const T* K = static_cast<const T*>(Kv);
+  const T* V = static_cast<const T*>(Vv);
+  const unsigned H = (unsigned)L.H;
+  hipError_t err;
+#define ICE_CHECK()                                  \
+  do {                                               \
+    if ((err = hipGetLastError()) != hipSuccess) return err; \
+  } while (0)
+  // fresh header, parent links and owner heads
+  if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_hdr, sizeof(Hdr) / 4, 0, s))) return err;
+  for (int l = 0; l < L.ntab; ++l) {
+    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_parent[l], L.cap, -1, s))) return err;
+    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_first[l], L.cap + 1, -1, s))) return err;
+    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_tail[l], L.cap + 1, -1, s))) return err;
+  }
+  if (n > 0) {
+    k_norm_level<D, T><<<dim3(blocks_for(n, 64), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws);
+    ICE_CHECK();
+  }
+  k_lift_compact<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
+  ICE_CHECK();
+  const int last = L.L >= 2 ? L.L - 2 : 0;
+  for (int level = 0; level <= last; ++level) {
+    const int npts = L.ncap[level];
+    if (L.L >= 2 && n > 0) {
+      k_gather_opA<D, T><<<dim3(blocks_for((int64_t)L.ncap[level + 1] * W.kp, 256 * 8), H), 256, 0, s>>>(
+          L, W, blob, K, hstride, ws, level);
+      ICE_CHECK();
+      if ((err = launch_parent_gemm(L, W, blob, Kv, hstride, ws, level, s))) return err;
+    }
+    const int nown = (L.L >= 2 ? L.ncap[level + 1] : 0) + 1;
+    if ((err = launch_fill_heads(ws, W.head_bytes, L.H, W.off_cnt, nown, 0, s))) return err;
+    if (n > 0) {
+      k_pack_count<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
+      ICE_CHECK();
+    }
+    k_pack_scan<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, level);
+    ICE_CHECK();
+    if (n > 0) {
+      k_pack_scatter<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
+      ICE_CHECK();
+      k_pack_place<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
+      ICE_CHECK();
+      using G = RowGeo<D, T>;
+      k_copy_pages<D, T><<<dim3(blocks_for((int64_t)L.pcap[level] * ICE_PAGE_CAP, 4 * G::RPP * 8), H), 256, 0,
+                           s>>>(L, K, V, hstride, blob, level);
+      ICE_CHECK();
+    }
+  }
+  if (L.L >= 2 && n > 0) {
+    using G = RowGeo<D, T>;
+    k_copy_top<D, T><<<dim3(blocks_for(L.topcap, 4 * G::RPP * 4), H), 256, 0, s>>>(L, K, hstride, blob);
+    ICE_CHECK();
+  }
+#undef ICE_CHECK
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_fill_heads(void* base, int64_t head_bytes, int H, int64_t off, int64_t n, int32_t value,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_fill_heads<<<dim3(blocks_for(n, 256 * 4), (unsigned)H), 256, 0, s>>>(base, head_bytes, off, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
+                        int n_tokens, int64_t head_stride, void* ws, hipStream_t s) {
+  if (L.dtype == ICE_BF16) {
+    if (L.d == 128) return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, s);
+    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, s);
+  }
+  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, s);
+  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, s);
+}
+
+}  // namespace ice

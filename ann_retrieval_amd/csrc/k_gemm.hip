@@ -1,0 +1,244 @@
+// Nearest parent of every level-l point among the level-(l+1) points: a
+// distance GEMM on the matrix cores fused with a running argmax.
+//
+// The aitangshan.cn IceCache article (section 3) gives every point the most
+// similar point one level up as its parent, after a lift that turns inner
+// product into Euclidean distance. For lifted keys x = [k, e] with |x| = M,
+// |x_i - x_j|^2 = 2M^2 - 2 s_ij with s_ij = k_i.k_j + e_i e_j, so the nearest
+// parent is the argmax of s over the candidates; ties go to the lower token
+// id (the candidates are in ascending token order).
+//
+// Layout (bf16, gfx950 v_mfma_f32_32x32x16_bf16): candidate parents are the
+// MFMA rows (A operand, streamed through LDS in tiles of 32), children the
+// columns (B operand, kept in registers for the whole sweep). Each lane then
+// owns one child column and 16 parent rows of every tile, so the argmax runs
+// inside the lane's accumulators with one cross-lane step at the end. The
+// e_i e_j term rides in one extra k-step: e is split into three bf16 parts
+// and six of the products are laid out as extra columns (the dropped terms
+// are below 2^-24 relative).
+#include "ice_launch.h"
+
+namespace ice {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kChildPerBlock = 128;  // 4 waves x 32 children
+
+struct GemmView {
+  bool skip;
+  int n_child, n_cand;
+  const int32_t* exact;
+  const int32_t* pts;
+  char* wh;
+  Hdr* hdr;
+};
+
+__device__ inline GemmView gemm_view(const DevLayout& L, const WsLayout& W, void* blob, void* ws, int level) {
+  GemmView v;
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  v.hdr = at<Hdr>(hb, L.off_hdr);
+  v.wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  v.skip = level >= v.hdr->top_level;
+  const int32_t* cnts = at<int32_t>(v.wh, W.off_cnts);
+  v.n_child = cnts[ICE_MAX_LEVELS + level];
+  v.n_cand = cnts[level + 1];
+  v.exact = at<int32_t>(v.wh, W.off_exact[level]);
+  v.pts = at<int32_t>(v.wh, W.off_pts[level + 1]);
+  return v;
+}
+
+// Running best / runner-up over the lane's rows. Rows arrive in increasing
+// order, so a strict comparison keeps the lowest index among equal scores.
+struct ArgMax {
+  float best = -INFINITY, second = -INFINITY;
+  int idx = 0x7fffffff;
+  __device__ inline void push(float s, int p) {
+    if (s > best) {
+      second = best;
+      best = s;
+      idx = p;
+    } else {
+      second = fmaxf(second, s);
+    }
+  }
+  // Combine with the other half-wave holding the same child column.
+  __device__ inline void merge_halves() {
+    const float ob = __shfl_xor(best, 32, 64);
+    const float os = __shfl_xor(second, 32, 64);
+    const int oi = __shfl_xor(idx, 32, 64);
+    if (ob > best || (ob == best && oi < idx)) {
+      second = fmaxf(best, os);
+      best = ob;
+      idx = oi;
+    } else {
+      second = fmaxf(second, ob);
+    }
+  }
+};
+
+__device__ inline void write_parent(const DevLayout& L, const WsLayout& W, const GemmView& v, void* blob,
+                                    int level, int ctok, const ArgMax& a) {
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  at<int32_t>(hb, L.off_parent[level])[ctok] = v.pts[a.idx];
+  at<float>(v.wh, W.off_s1)[ctok] = a.best;
+  at<float>(v.wh, W.off_s2)[ctok] = a.second;
+  // lifted distances D = 2(M^2 - s): near-tie when D2 - D1 < 1e-4 D2
+  const float M2 = (float)v.hdr->M2;
+  if (a.second > -INFINITY && (a.best - a.second) < 1e-4f * (M2 - a.second)) atomicAdd(&v.hdr->near_ties, 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, void* blob, const uint16_t* K,
+                                                     int64_t hstride, void* ws, int level) {
+  constexpr int KP = D + 16;            // operand row length (elements)
+  constexpr int KS = KP / 16;           // k-steps of 16
+  constexpr int ROWB = KP * 2;          // operand row bytes
+  constexpr int LDSB = ROWB + 16;       // padded LDS row stride
+  constexpr int TILE = 32;
+  __shared__ __attribute__((aligned(16))) char tile[TILE * LDSB];
+
+  const GemmView v = gemm_view(L, W, blob, ws, level);
+  if (v.skip) return;
+  const int c0 = blockIdx.x * kChildPerBlock;
+  if (c0 >= v.n_child) return;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* e = at<float>(head_base(blob, L, h), L.off_e);
+  const uint16_t* Kh = K + (int64_t)h * hstride;
+  const char* opA = reinterpret_cast<const char*>(at<uint16_t>(v.wh, W.off_opA));
+
+  // child operand: column lane%32, k elements 8*(lane/32) .. +7 of each step
+  const int ci = c0 + wave * 32 + (lane & 31);
+  const bool cvalid = ci < v.n_child;
+  const int ctok = cvalid ? v.exact[ci] : 0;
+  const int half = lane >> 5;
+  bf16x8 bfr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS - 1; ++ks) {
+    V4 x = {0, 0, 0, 0};
+    if (cvalid) x = *reinterpret_cast<const V4*>(Kh + (int64_t)ctok * D + ks * 16 + half * 8);
+    bfr[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+  {
+    V4 x = {0, 0, 0, 0};
+    if (cvalid && half == 0) {
+      const float ev = e[ctok];
+      const uint16_t a0 = f32_to_bf16(ev);
+      const float r1 = ev - bf16_to_f32(a0);
+      const uint16_t a1 = f32_to_bf16(r1);
+      const uint16_t a2 = f32_to_bf16(r1 - bf16_to_f32(a1));
+      // child side of the six lift products: c0 c0 c1 c0 c2 c1
+      x.x = (uint32_t)a0 | ((uint32_t)a0 << 16);
+      x.y = (uint32_t)a1 | ((uint32_t)a0 << 16);
+      x.z = (uint32_t)a2 | ((uint32_t)a1 << 16);
+    }
+    bfr[KS - 1] = __builtin_bit_cast(bf16x8, x);
+  }
+
+  ArgMax am;
+  constexpr int CHUNKS = TILE * ROWB / 16;
+  for (int p0 = 0; p0 < v.n_cand; p0 += TILE) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < CHUNKS; c += 256) {
+      const int r = c / (ROWB / 16), q = c % (ROWB / 16);
+      V4 x = {0, 0, 0, 0};
+      if (p0 + r < v.n_cand) x = *reinterpret_cast<const V4*>(opA + (int64_t)(p0 + r) * ROWB + q * 16);
+      *reinterpret_cast<V4*>(tile + r * LDSB + q * 16) = x;
+    }
+    __syncthreads();
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const V4 a = *reinterpret_cast<const V4*>(tile + (lane & 31) * LDSB + ks * 32 + half * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bfr[ks], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int p = p0 + 8 * (j >> 2) + 4 * half + (j & 3);
+      if (p < v.n_cand) am.push(acc[j], p);
+    }
+  }
+  am.merge_halves();
+  if (lane < 32 && cvalid) write_parent(L, W, v, blob, level, ctok, am);
+}
+
+// fp32 inputs: v_mfma_f32_32x32x2f32, operand rows [key | e | 0 0 0].
+template <int D>
+__global__ __launch_bounds__(256) void k_parent_f32(DevLayout L, WsLayout W, void* blob, const float* K,
+                                                    int64_t hstride, void* ws, int level) {
+  constexpr int KP = D + 4;
+  constexpr int KS = (D + 2) / 2;       // k-steps of 2 over [key | e | 0]
+  constexpr int LDSW = KP + 1;          // padded LDS row stride (floats)
+  constexpr int TILE = 32;
+  __shared__ float tile[TILE * LDSW];
+
+  const GemmView v = gemm_view(L, W, blob, ws, level);
+  if (v.skip) return;
+  const int c0 = blockIdx.x * kChildPerBlock;
+  if (c0 >= v.n_child) return;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* e = at<float>(head_base(blob, L, h), L.off_e);
+  const float* Kh = K + (int64_t)h * hstride;
+  const float* opA = at<float>(v.wh, W.off_opA);
+
+  const int ci = c0 + wave * 32 + (lane & 31);
+  const bool cvalid = ci < v.n_child;
+  const int ctok = cvalid ? v.exact[ci] : 0;
+  const int half = lane >> 5;
+  float bfr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int col = 2 * ks + half;
+    float x = 0.0f;
+    if (cvalid) x = col < D ? Kh[(int64_t)ctok * D + col] : (col == D ? e[ctok] : 0.0f);
+    bfr[ks] = x;
+  }
+  ArgMax am;
+  for (int p0 = 0; p0 < v.n_cand; p0 += TILE) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < TILE * KP; c += 256) {
+      const int r = c / KP, q = c % KP;
+      tile[r * LDSW + q] = p0 + r < v.n_cand ? opA[(int64_t)(p0 + r) * KP + q] : 0.0f;
+    }
+    __syncthreads();
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float a = tile[(lane & 31) * LDSW + 2 * ks + half];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bfr[ks], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int p = p0 + 8 * (j >> 2) + 4 * half + (j & 3);
+      if (p < v.n_cand) am.push(acc[j], p);
+    }
+  }
+  am.merge_halves();
+  if (lane < 32 && cvalid) write_parent(L, W, v, blob, level, ctok, am);
+}
+
+}  // namespace
+
+hipError_t launch_parent_gemm(const DevLayout& L, const WsLayout& W, void* blob, const void* K,
+                              int64_t head_stride, void* ws, int level, hipStream_t s) {
+  const int n_child_max = L.ncap[level];
+  const dim3 grid((unsigned)((n_child_max + kChildPerBlock - 1) / kChildPerBlock), (unsigned)L.H);
+  if (grid.x == 0) return hipSuccess;
+  if (L.dtype == ICE_BF16) {
+    const uint16_t* Kb = static_cast<const uint16_t*>(K);
+    if (L.d == 128) k_parent_bf16<128><<<grid, 256, 0, s>>>(L, W, blob, Kb, head_stride, ws, level);
+    else k_parent_bf16<64><<<grid, 256, 0, s>>>(L, W, blob, Kb, head_stride, ws, level);
+  } else {
+    const float* Kf = static_cast<const float*>(K);
+    if (L.d == 128) k_parent_f32<128><<<grid, 256, 0, s>>>(L, W, blob, Kf, head_stride, ws, level);
+    else k_parent_f32<64><<<grid, 256, 0, s>>>(L, W, blob, Kf, head_stride, ws, level);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ice

@@ -1,0 +1,184 @@
+/*
+ * ice.h - C ABI of the IceCache hot path on MI355X (gfx950).
+ *
+ * What the calls compute follows the IceCache method pages:
+ *   - papernotes.org, "IceCache: Memory-Efficient KV-cache Management for
+ *     Long-Sequence LLMs", section "Overall framework": (1) index - at prefill
+ *     (or when window tokens are offloaded) build one DCI tree per attention
+ *     head that clusters tokens by key similarity, each node one physical
+ *     page; (2) page selection - at decode every head picks its own top-k
+ *     pages with an M-DCI nearest-neighbour search; (3) bulk loading + sparse
+ *     attention over the picked pages.
+ *   - aitangshan.cn IceCache article, section 3 (the DCI tree: key lift,
+ *     random promotion, nearest parent one level up, same parent = same page,
+ *     incremental insert without rebuild) and section 6 (TK/TQ transform, the
+ *     union of pages over a GQA group).
+ *
+ * Model of the data. A "head" is one independent index: one (sequence,
+ * layer, KV head). All heads of one index object share the parameters and
+ * the token count. Keys, values and queries share one element type, fp32 or
+ * bf16 (raw IEEE bfloat16 bits). Every device buffer is owned by the caller;
+ * the library never allocates device memory. Every call that takes a
+ * `stream` (a hipStream_t; NULL = the default stream) only enqueues work and
+ * returns; results are ready when the stream reaches them. All argument and
+ * capacity checks run on the host before anything is enqueued, so a call that
+ * returns an error has changed nothing. Nothing throws across the ABI.
+ * Calls on one index object must be issued from one host thread at a time.
+ */
+#ifndef ICE_H_
+#define ICE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define ICE_OK            0
+#define ICE_ERR_ARG      -1  /* null pointer, bad size, bad budget or beam      */
+#define ICE_ERR_DTYPE    -2  /* unsupported element type / head dimension        */
+#define ICE_ERR_STATE    -3  /* select / insert / attend before build            */
+#define ICE_ERR_CAPACITY -4  /* tokens beyond `capacity`, workspace too small    */
+#define ICE_ERR_HIP      -5  /* a HIP runtime call failed (message has details) */
+
+/* ---- element types ----------------------------------------------------- */
+#define ICE_F32  0
+#define ICE_BF16 1
+
+/* ---- limits ------------------------------------------------------------ */
+#define ICE_PAGE_CAP   16   /* tokens per page (the article's section 2 example) */
+#define ICE_MAX_LEVELS 4
+#define ICE_MAX_GROUP  16   /* query heads per KV head                          */
+#define ICE_MAX_BEAM   256  /* beam width and pages per query                    */
+
+typedef struct ice_params {
+  int32_t  n_heads;       /* H >= 1: independent indexes (sequence x layer x KV head)     */
+  int32_t  group;         /* G in [1, ICE_MAX_GROUP]: query heads sharing one KV head      */
+  int32_t  d;             /* head dimension: 64 or 128                                    */
+  int32_t  dtype;         /* ICE_F32 or ICE_BF16, for K, V and Q                          */
+  int32_t  page_cap;      /* must be ICE_PAGE_CAP                                         */
+  int32_t  levels;        /* L in [1, ICE_MAX_LEVELS]: levels 0..L-1, bottom included      */
+  int32_t  promote_log2;  /* promotion probability per level = 2^-promote_log2, in [1,16] */
+  int32_t  capacity;      /* max tokens per head, build plus inserts, >= 1                */
+  uint64_t seed;          /* seed of the promotion draws                                  */
+} ice_params;
+
+typedef struct ice_index ice_index;   /* opaque host-side handle */
+
+/* Device bytes of the index blob for these parameters. The sizes come from
+ * the promotion draws of every position 0..capacity-1 of every head, so the
+ * blob bounds every page table exactly; 0 on invalid parameters. */
+size_t ice_index_bytes(const ice_params* p);
+
+/* Device bytes of the workspace that ice_build, ice_insert, ice_select and
+ * ice_attend need for queries up to `max_budget_tokens` (a multiple of
+ * page_cap) per query head. One workspace may be shared by successive calls
+ * on one stream; it holds nothing between calls. 0 on invalid arguments. */
+size_t ice_workspace_bytes(const ice_params* p, int32_t max_budget_tokens);
+
+/* Creates a host handle over a caller-allocated device blob of at least
+ * ice_index_bytes(p) bytes (256-byte aligned). The blob stays owned by the
+ * caller and must outlive the handle. */
+int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_index** out);
+void ice_destroy(ice_index* idx);
+
+/* Index build at prefill (the framework's step 1; the article's section 3).
+ * K, V: device, [H][n_tokens][d] with `head_stride` elements between heads
+ * (>= n_tokens*d). For every head: lift keys to [k, sqrt(M^2-|k|^2)] with M^2
+ * the head's largest squared key norm; draw every token's promotion level;
+ * give every point of level l its nearest point of level l+1 as parent
+ * (lifted Euclidean distance, ties to the lower token id); store the points
+ * sharing a parent together, ordered by distance and cut into pages of 16;
+ * copy K and V rows into the page pool. Replaces any earlier content.
+ * 0 <= n_tokens <= capacity. ws: workspace of ice_workspace_bytes. */
+int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Incremental insert (the article's section 3: no rebuild; the notes' key
+ * design 2: a node over the page size splits off a new page). k_new, v_new:
+ * device, [H][n_new][d] contiguous. Tokens are inserted one after another at
+ * the next positions: each draws its level (capped at the build's top level),
+ * takes the nearest point of the next level as parent, and is appended to
+ * its owner's last page, or to a newly split page if that one is full.
+ * Resident tokens never move. ICE_ERR_CAPACITY if the count would exceed
+ * capacity (nothing is inserted). */
+int ice_insert(ice_index* idx, const void* k_new, const void* v_new, int32_t n_new,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* Page selection (the notes' key designs 2 and 3). Q: device [H][G][d].
+ * Per query head: score the top level by q.k, keep the `beam` best; score the
+ * children of the kept points one level down, keep `beam`; ...; at level 0
+ * rank every page of the kept level-1 points by its best token score and keep
+ * k = budget_tokens/16 pages (score descending, then page id ascending).
+ *   sel   [H][G][k]   page ids in rank order, -1 padded (device)
+ *   uni   [H][G*k]    union over the group, ascending, -1 padded (device)
+ *   n_uni [H]         union sizes (device)
+ *   trace [H][G][L][beam] nullable: kept point ids per cut, top level first
+ *                     (cuts that do not exist are -1); for parity checks.
+ * budget_tokens: positive multiple of 16, <= the workspace's max budget and
+ * <= ICE_MAX_BEAM*16; beam in [1, ICE_MAX_BEAM]. */
+int ice_select(const ice_index* idx, const void* Q, int32_t budget_tokens, int32_t beam,
+               int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse attention over the selected pages (the notes' key design 1: the
+ * weight of token j is s_j exp(q.k_j/sqrt d) normalised over the selected
+ * tokens). For every (h, g): o = sum_j softmax_j(scale * q.k_j) v_j over the
+ * valid tokens of pages uni[h][0..n_uni[h]). O: device [H][G][d] fp32;
+ * lse: device [H][G] fp32 log-sum-exp of the scaled logits, nullable. A head
+ * with no selected token gets o = 0, lse = -inf. uni_stride: ints between
+ * heads in `uni` (>= the max n_uni), at most the workspace's budget times G
+ * over 16. */
+int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const int32_t* n_uni,
+               int32_t uni_stride, float scale, float* O, float* lse,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* ---- inspection (synchronise the stream; for parity tests and stats) ---- */
+
+/* Arrays of one head that ice_export copies to host memory. */
+#define ICE_EXP_LEVEL      0   /* int8  [capacity]          level used by the index        */
+#define ICE_EXP_LIFT       1   /* f32   [capacity]          extra lift coordinate e        */
+#define ICE_EXP_PARENT     2   /* int32 [capacity] level `level`: parent token (-1 none)   */
+#define ICE_EXP_PAGE_TOK   3   /* int32 [pages][16] level `level` page table, -1 = empty   */
+#define ICE_EXP_PAGE_CNT   4   /* int32 [pages]                                            */
+#define ICE_EXP_PAGE_NEXT  5   /* int32 [pages] next page of the same owner, -1 = last     */
+#define ICE_EXP_PAGE_OWNER 6   /* int32 [pages] owner token, -1 = virtual root             */
+#define ICE_EXP_OWNER_FIRST 7  /* int32 [capacity+1] first page per owner (+ root), -1     */
+#define ICE_EXP_OWNER_TAIL 8   /* int32 [capacity+1] last page per owner (+ root), -1      */
+#define ICE_EXP_TOP        9   /* int32 [top capacity] top-level points in order           */
+#define ICE_EXP_PAGE_K     10  /* dtype [pages][16][d] page-pool keys (level 0) / copies   */
+#define ICE_EXP_PAGE_V     11  /* dtype [pages][16][d] page-pool values (level 0 only)     */
+#define ICE_EXP_HEADER     12  /* ice_head_stats                                           */
+
+typedef struct ice_head_stats {
+  int32_t n_tokens;        /* tokens in the head                                  */
+  int32_t top_level;       /* highest non-empty level at build (L_top)            */
+  int32_t n_top;           /* points in the top list                              */
+  int32_t n_pages[ICE_MAX_LEVELS]; /* pages per page table (level 0 = KV pages)    */
+  int32_t clamps;          /* inserted keys longer than the build's M (lift = 0)   */
+  int32_t splits;          /* pages split off by inserts (all levels)              */
+  int32_t near_ties;       /* parent choices whose two best lifted distances were
+                              within 1e-4 relative, build and insert              */
+  int32_t pad;
+  double  M2;              /* largest squared key norm at build                   */
+} ice_head_stats;
+
+/* Bytes of one export array for this index (per head), 0 if not applicable. */
+size_t ice_export_bytes(const ice_index* idx, int32_t what, int32_t level);
+/* Copies array `what` of `head` (page tables: of `level`) into host memory
+ * `dst` of at least ice_export_bytes bytes. Synchronises `stream` first. */
+int ice_export(const ice_index* idx, int32_t head, int32_t what, int32_t level, void* dst,
+               size_t dst_bytes, void* stream);
+
+/* Number of tokens per head as tracked by the handle. */
+int32_t ice_n_tokens(const ice_index* idx);
+
+/* Message of the last error on this thread ("" if none). */
+const char* ice_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ICE_H_ */

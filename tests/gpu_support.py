@@ -1,0 +1,196 @@
+"""Helpers of the GPU parity tests: read a head's layout out of the library,
+rebuild the oracle's view of the same head, and compare the two under the
+near-tie protocol.
+
+Comparison protocol (near-tie band 1e-4 relative, from the method's parity
+contract):
+
+* promotion levels, the top list and page ids must match exactly;
+* a parent may differ from the oracle's only when the GPU's choice is within
+  the band of the best lifted distance (``(D_gpu - D1) <= 1e-4 * D_gpu``); such
+  choices are counted, and the oracle then continues with the GPU's choice;
+* inside an owner, slots may differ only between tokens whose distances to the
+  owner are within the band (counted);
+* a selection cut may keep a different set only through near-tied items
+  (counted); the oracle then continues from the GPU's kept set, so ``sel`` and
+  ``uni`` must match exactly afterwards;
+* attention: max_i |o_gpu - o_ref| / max_i |o_ref| per (head, query head)
+  within 2e-3 for bf16 K/V and 1e-5 for fp32.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+from oracle import icecache as ic
+from ann_retrieval_amd import _lib as L
+
+BAND = ic.NEAR_TIE_REL
+ATOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+def to64(x: torch.Tensor) -> np.ndarray:
+    return x.detach().float().cpu().double().numpy()
+
+
+@dataclasses.dataclass
+class GpuHead:
+    n: int
+    L_top: int
+    n_top: int
+    lev: np.ndarray
+    e: np.ndarray
+    parent: list
+    tables: list          # per table: dict(pages, owner, first, next, cnt)
+    top: list
+    stats: dict
+
+
+def read_head(ix, h: int) -> GpuHead:
+    st = ix.stats(h)
+    n, Lt = st["n_tokens"], st["top_level"]
+    lev = ix.export(h, L.ICE_EXP_LEVEL, np_dtype=np.int8)[:n].astype(np.int64)
+    e = ix.export(h, L.ICE_EXP_LIFT, np_dtype=np.float32)[:n].astype(np.float64)
+    ntab = max(1, ix.levels - 1)
+    parent = [ix.export(h, L.ICE_EXP_PARENT, l)[:n].astype(np.int64) for l in range(min(Lt, ntab))]
+    tables = []
+    for l in range(ntab):
+        P = st["n_pages"][l]
+        tok = ix.export(h, L.ICE_EXP_PAGE_TOK, l).reshape(-1, L.ICE_PAGE_CAP)[:P]
+        cnt = ix.export(h, L.ICE_EXP_PAGE_CNT, l)[:P]
+        tables.append(dict(
+            tok=tok, cnt=cnt, pages=[[int(x) for x in tok[p, :cnt[p]]] for p in range(P)],
+            next=ix.export(h, L.ICE_EXP_PAGE_NEXT, l)[:P], owner=ix.export(h, L.ICE_EXP_PAGE_OWNER, l)[:P],
+            first=ix.export(h, L.ICE_EXP_OWNER_FIRST, l), tail=ix.export(h, L.ICE_EXP_OWNER_TAIL, l)))
+    top = [int(x) for x in ix.export(h, L.ICE_EXP_TOP)[:st["n_top"]]]
+    return GpuHead(n=n, L_top=Lt, n_top=st["n_top"], lev=lev, e=e, parent=parent, tables=tables, top=top,
+                   stats=st)
+
+
+def owner_chain(tab: dict, owner_slot: int) -> list:
+    out, p = [], int(tab["first"][owner_slot])
+    while p >= 0:
+        out.append(p)
+        p = int(tab["next"][p])
+    return out
+
+
+def check_table_structure(g: GpuHead, cap: int):
+    """Chains, owners and counts of every table are self-consistent."""
+    for l, tab in enumerate(g.tables):
+        P = len(tab["pages"])
+        seen = np.zeros(P, dtype=np.int64)
+        owners = set(int(o) for o in tab["owner"])
+        for o in owners:
+            slot = cap if o == ic.ROOT else o
+            chain = owner_chain(tab, slot)
+            assert chain, f"table {l}: owner {o} has no chain"
+            assert int(tab["tail"][slot]) == chain[-1]
+            for i, p in enumerate(chain):
+                seen[p] += 1
+                assert int(tab["owner"][p]) == o
+                assert 1 <= tab["cnt"][p] <= L.ICE_PAGE_CAP
+                if i + 1 < len(chain):
+                    assert tab["cnt"][p] == L.ICE_PAGE_CAP, "only an owner's last page may be partly filled"
+        assert np.all(seen == 1), f"table {l}: a page is on no chain or on two"
+        for p in range(P):
+            assert np.all(tab["tok"][p, tab["cnt"][p]:] == -1)
+
+
+def validate_parents(ref: ic.HeadIndex, g: GpuHead):
+    """Compares parents level by level. Returns (parents to replay, near-tie count)."""
+    X = ref.X()
+    replay, ties = [], 0
+    for l in range(ref.L_top):
+        po, pg = ref.parent[l], g.parent[l]
+        par = po.copy()
+        diff = np.nonzero(po != pg)[0]
+        for i in diff:
+            i = int(i)
+            assert ref.lev[i] == l, f"level {l}: token {i} (level {ref.lev[i]}) has parent {pg[i]} != {po[i]}"
+            j = int(pg[i])
+            assert 0 <= j < ref.n and ref.lev[j] >= l + 1, f"level {l}: parent {j} of {i} is not a level-{l+1} point"
+            dg = float(((X[i] - X[j]) ** 2).sum())
+            d1 = float(ref.dist[l][i])
+            assert dg - d1 <= BAND * dg, (f"level {l}: token {i} parent {j} (D={dg:.9g}) vs oracle {po[i]} "
+                                          f"(D={d1:.9g}) outside the near-tie band")
+            par[i] = j
+            ties += 1
+        replay.append(par)
+    return replay, ties
+
+
+def oracle_replay(K64, V64, h, seed, levels, plog2, replay_parents):
+    return ic.build_head(K64, V64, h, seed, levels, plog2, 16, parents=replay_parents)
+
+
+def compare_layout(ref: ic.HeadIndex, g: GpuHead, cap: int) -> int:
+    """Exact page ids / owners / top list; slot differences only between
+    near-equal distances. Returns the number of such slot differences."""
+    assert g.L_top == ref.L_top
+    assert g.top == ref.top
+    swaps = 0
+    tab = g.tables[0]
+    assert len(tab["pages"]) == len(ref.pages), f"{len(tab['pages'])} pages vs oracle {len(ref.pages)}"
+    assert [int(o) for o in tab["owner"]] == [int(o) for o in ref.page_owner]
+    for owner, pids in ref.owner_pages.items():
+        slot = cap if owner == ic.ROOT else owner
+        assert owner_chain(tab, slot) == list(pids), f"owner {owner}: page chain differs"
+        seq_o = [t for p in pids for t in ref.pages[p]]
+        seq_g = [t for p in pids for t in tab["pages"][p]]
+        assert sorted(seq_o) == sorted(seq_g), f"owner {owner}: different members"
+        if seq_o != seq_g:
+            d = ref.dist[0] if ref.L_top >= 1 else None
+            for a, b in zip(seq_o, seq_g):
+                if a != b:
+                    assert d is not None, "root pages must be in token order"
+                    da, db = float(d[a]), float(d[b])
+                    assert abs(da - db) <= BAND * max(da, db), f"owner {owner}: slot order {a} vs {b} not a near-tie"
+                    swaps += 1
+    for l in range(1, ref.L_top):
+        tl = g.tables[l]
+        for owner, kids in ref.children[l].items():
+            got = [t for p in owner_chain(tl, owner) for t in tl["pages"][p]]
+            assert sorted(got) == sorted(kids), f"level {l} owner {owner}: different children"
+            if got != kids:
+                for a, b in zip(kids, got):
+                    if a != b:
+                        da, db = float(ref.dist[l][a]), float(ref.dist[l][b])
+                        assert abs(da - db) <= BAND * max(da, db)
+                        swaps += 1
+    return swaps
+
+
+def adopt_gpu_slots(ref: ic.HeadIndex, g: GpuHead):
+    """After compare_layout accepted near-tie slot swaps, take the GPU's slots
+    so the selection and attention checks see the same page contents."""
+    ref.pages = [list(p) for p in g.tables[0]["pages"]]
+    for l in range(1, ref.L_top):
+        tl = g.tables[l]
+        for owner in list(ref.children[l].keys()):
+            ref.children[l][owner] = [t for p in owner_chain(tl, owner) for t in tl["pages"][p]]
+
+
+def compare_selection(ref: ic.HeadIndex, q64, budget, beam, sel_g, trace_g):
+    """Oracle select, continuing from the GPU's kept sets where they differ by
+    near-ties only. Returns 1 if any cut needed that, else 0."""
+    n_cuts = ref.L_top if ref.n > 0 else 0
+    got = [int(x) for x in sel_g if x >= 0]
+    kept_g = [[int(x) for x in trace_g[c] if x >= 0] for c in range(n_cuts)]
+    free = ic.select(ref, q64, budget, beam)
+    if free["kept"] == kept_g and free["sel"] == got:
+        return 0
+    r = ic.select(ref, q64, budget, beam, forced=kept_g + [None])
+    assert r["admissible"], f"kept sets {kept_g} vs oracle {free['kept']} beyond the near-tie band"
+    if got != r["sel"]:
+        r2 = ic.select(ref, q64, budget, beam, forced=kept_g + [got])
+        assert r2["admissible"], f"sel {got} vs oracle {r['sel']} beyond the near-tie band"
+    return 1
+
+
+def attn_error(o_gpu: np.ndarray, o_ref: np.ndarray) -> float:
+    den = np.abs(o_ref).max()
+    return float(np.abs(o_gpu - o_ref).max() / den) if den > 0 else float(np.abs(o_gpu).max())

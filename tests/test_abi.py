@@ -1,0 +1,101 @@
+"""The C-ABI library on the host (no GPU calls): it loads, exports every
+function ``include/ice.h`` declares, sizes its blobs from the promotion draws,
+and rejects bad arguments before enqueuing anything.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+from ann_retrieval_amd import _lib as L
+from ann_retrieval_amd.api import make_params
+from oracle import icecache as ic
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = L.header_functions()
+    assert {"ice_build", "ice_insert", "ice_select", "ice_attend"} <= set(names)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_declares_every_function():
+    assert set(L.header_functions()) == set(L._SIGNATURES)
+
+
+def _fake_handle(lib, p):
+    h = ctypes.c_void_p()
+    n = lib.ice_index_bytes(ctypes.byref(p))
+    rc = lib.ice_create(ctypes.byref(p), ctypes.c_void_p(1 << 20), n, ctypes.byref(h))
+    assert rc == L.ICE_OK
+    return h
+
+
+@pytest.mark.parametrize("H,cap,levels,plog2", [(3, 5000, 3, 4), (2, 777, 4, 2), (1, 100, 1, 4), (4, 33, 2, 3)])
+def test_page_tables_are_sized_by_the_promotion_draws(lib, H, cap, levels, plog2):
+    p = make_params(H, 2, 128, "bf16", cap, levels, plog2, seed=11)
+    h = _fake_handle(lib, p)
+    try:
+        # level counts from the oracle's own draws over every position
+        lev = np.stack([ic.draw_levels(11, hh, 0, cap, levels, plog2) for hh in range(H)])
+        ncap = [cap] + [int((lev >= l).sum(axis=1).max()) for l in range(1, levels)]
+        ntab = max(1, levels - 1)
+        for t in range(ntab):
+            owners = ncap[t + 1] if t + 1 < levels else 0
+            bound = (ncap[t] + 15 * max(owners, 1) + 15) // 16
+            assert lib.ice_export_bytes(h, L.ICE_EXP_PAGE_TOK, t) == bound * 16 * 4
+            assert lib.ice_export_bytes(h, L.ICE_EXP_PAGE_K, t) == bound * 16 * 128 * 2
+        assert lib.ice_export_bytes(h, L.ICE_EXP_PAGE_TOK, ntab) == 0
+        assert lib.ice_export_bytes(h, L.ICE_EXP_TOP, 0) == (max(ncap[1], 1) * 4 if levels >= 2 else 0)
+    finally:
+        lib.ice_destroy(h)
+
+
+def test_invalid_params_give_zero_sizes(lib):
+    for kw in [dict(d=96), dict(group=0), dict(group=17), dict(capacity=0), dict(levels=5)]:
+        base = dict(n_heads=2, group=4, d=128, dtype="bf16", capacity=100)
+        base.update(kw)
+        p = make_params(**base)
+        assert lib.ice_index_bytes(ctypes.byref(p)) == 0
+    p = make_params(2, 4, 128, "bf16", 100)
+    assert lib.ice_workspace_bytes(ctypes.byref(p), 24) == 0
+    assert lib.ice_workspace_bytes(ctypes.byref(p), 256) > 0
+    p.page_cap = 8
+    assert lib.ice_index_bytes(ctypes.byref(p)) == 0
+    assert b"page_cap" in lib.ice_last_error()
+
+
+def test_argument_checks_run_before_any_launch(lib):
+    p = make_params(1, 2, 64, "f32", 64)
+    h = _fake_handle(lib, p)
+    try:
+        fake = ctypes.c_void_p(1 << 20)
+        ws_bytes = lib.ice_workspace_bytes(ctypes.byref(p), 64)
+        # select / insert / attend before a build
+        assert lib.ice_select(h, fake, 64, 4, fake, fake, fake, None, fake, ws_bytes, None) == L.ICE_ERR_STATE
+        assert lib.ice_insert(h, fake, fake, 1, fake, ws_bytes, None) == L.ICE_ERR_STATE
+        assert lib.ice_attend(h, fake, fake, fake, 8, 0.125, fake, None, fake, ws_bytes, None) == L.ICE_ERR_STATE
+        # build: too many tokens, null inputs, small workspace, misaligned inputs
+        assert lib.ice_build(h, fake, fake, 65, 65 * 64, fake, ws_bytes, None) == L.ICE_ERR_CAPACITY
+        assert lib.ice_build(h, None, fake, 10, 640, fake, ws_bytes, None) == L.ICE_ERR_ARG
+        assert lib.ice_build(h, fake, fake, 10, 640, fake, 16, None) == L.ICE_ERR_CAPACITY
+        assert lib.ice_build(h, ctypes.c_void_p((1 << 20) + 4), fake, 10, 640, fake, ws_bytes, None) == L.ICE_ERR_ARG
+        assert lib.ice_build(h, fake, fake, 10, 100, fake, ws_bytes, None) == L.ICE_ERR_ARG
+        assert lib.ice_build(h, fake, fake, -1, 640, fake, ws_bytes, None) == L.ICE_ERR_ARG
+        assert lib.ice_n_tokens(h) == 0
+    finally:
+        lib.ice_destroy(h)
+
+
+def test_create_rejects_small_or_misaligned_blobs(lib):
+    p = make_params(2, 2, 128, "bf16", 1000)
+    n = lib.ice_index_bytes(ctypes.byref(p))
+    h = ctypes.c_void_p()
+    assert lib.ice_create(ctypes.byref(p), ctypes.c_void_p(1 << 20), n - 1, ctypes.byref(h)) == L.ICE_ERR_CAPACITY
+    assert lib.ice_create(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 64), n, ctypes.byref(h)) == L.ICE_ERR_ARG
+    assert lib.ice_create(ctypes.byref(p), None, n, ctypes.byref(h)) == L.ICE_ERR_ARG
