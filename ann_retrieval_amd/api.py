@@ -51,7 +51,10 @@ class IceIndex:
     def __init__(self, n_heads: int, group: int, d: int, dtype: str, capacity: int, levels: int = 3,
                  promote_log2: int = 4, seed: int = 0, max_budget: int = 256, device="cuda"):
         self.lib = _lib.load()
-        self.device = torch.device(device)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
         self.dtype = dtype
         self.tdtype = _DT[dtype][1]
         self.p = make_params(n_heads, group, d, dtype, capacity, levels, promote_log2, seed)

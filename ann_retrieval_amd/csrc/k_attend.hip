@@ -44,7 +44,8 @@ __global__ __launch_bounds__(256) void k_attend_part(DevLayout L, const void* bl
   const T* pgK = at<T>(hb, L.off_pgK[0]);
   const T* pgV = at<T>(hb, L.off_pgV);
   const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
-  const int nu = n_uni[h];
+  const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
+  const int nu = min(n_uni[h], uni_stride);
   const int pbeg = split * kPagesPerSplit;
   const int pend = min(nu, pbeg + kPagesPerSplit);
 
@@ -64,7 +65,8 @@ __global__ __launch_bounds__(256) void k_attend_part(DevLayout L, const void* bl
     const int npg = min(kBatchPages, pend - pb);
     __syncthreads();
     if (threadIdx.x < kBatchPages) {
-      const int pg = threadIdx.x < npg ? uni[(int64_t)h * uni_stride + pb + threadIdx.x] : -1;
+      int pg = threadIdx.x < npg ? uni[(int64_t)h * uni_stride + pb + threadIdx.x] : -1;
+      if (pg >= n_pages) pg = -1;   // ids outside the page table are ignored
       rowpg[threadIdx.x] = pg;
       rowcnt[threadIdx.x] = pg >= 0 ? pg_cnt[pg] : 0;
     }

@@ -83,7 +83,10 @@ __device__ inline void write_parent(const DevLayout& L, const WsLayout& W, const
                                     int level, int ctok, const ArgMax& a) {
   const int h = blockIdx.y;
   void* hb = head_base(blob, L, h);
-  at<int32_t>(hb, L.off_parent[level])[ctok] = v.pts[a.idx];
+  // a.idx is unset only if every score was NaN (non-finite input): fall back
+  // to the first candidate rather than index out of range
+  const int pi = (a.idx >= 0 && a.idx < v.n_cand) ? a.idx : 0;
+  at<int32_t>(hb, L.off_parent[level])[ctok] = v.pts[pi];
   at<float>(v.wh, W.off_s1)[ctok] = a.best;
   at<float>(v.wh, W.off_s2)[ctok] = a.second;
   // lifted distances D = 2(M^2 - s): near-tie when D2 - D1 < 1e-4 D2

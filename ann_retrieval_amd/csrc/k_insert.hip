@@ -52,7 +52,7 @@ __device__ bool place_token(const DevLayout& L, void* hb, Hdr* hdr, int tb, int 
   hdr->n_pages[tb] = p + 1;
   if (tl >= 0) {
     pg_next[tl] = p;
-    hdr->splits += 1;
+    if (tb == 0) hdr->splits += 1;   // a KV page split off; upper tables only chain storage blocks
   } else {
     first[os] = p;
   }
@@ -179,6 +179,17 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
           }
         }
         p = btok;
+        if (p < 0 || p >= t || lev[p] < lam + 1) {
+          // only when every score was NaN (non-finite input): take any point
+          // of the next level instead of indexing out of range
+          const int tb = lam + 1;
+          if (tb == Ltop) {
+            p = at<int32_t>(hb, L.off_top_tok)[0];
+          } else {
+            const int32_t* toks = at<int32_t>(hb, L.off_pg_tok[tb]);
+            p = toks[0];
+          }
+        }
         const float m2f = (float)M2;
         if (second > -INFINITY && (best - second) < 1e-4f * (m2f - second)) hdr->near_ties += 1;
       }

@@ -158,7 +158,7 @@ typedef struct ice_head_stats {
   int32_t n_top;           /* points in the top list                              */
   int32_t n_pages[ICE_MAX_LEVELS]; /* pages per page table (level 0 = KV pages)    */
   int32_t clamps;          /* inserted keys longer than the build's M (lift = 0)   */
-  int32_t splits;          /* pages split off by inserts (all levels)              */
+  int32_t splits;          /* KV pages split off by inserts (level-0 page table)   */
   int32_t near_ties;       /* parent choices whose two best lifted distances were
                               within 1e-4 relative, build and insert              */
   int32_t pad;

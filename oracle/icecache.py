@@ -307,7 +307,9 @@ def pack(lev: np.ndarray, L_top: int, parent: list, dist: list, page_cap: int):
         for t in np.nonzero(lev >= l)[0]:
             members[int(parent[l][t])].append(int(t))
         children[l] = {p: sorted(m, key=lambda t: (dist[l][t], t)) for p, m in members.items()}
-    top = [int(t) for t in np.nonzero(lev >= L_top)[0]] if n else []
+    # with no promoted point the virtual root owns the pages and there is no
+    # top level of points to search
+    top = [int(t) for t in np.nonzero(lev >= L_top)[0]] if L_top >= 1 else []
     return pages, page_owner, owner_pages, children, top
 
 
@@ -432,7 +434,7 @@ def insert(idx: HeadIndex, k, v, lev_override: int | None = None, parent_overrid
             idx.children[l][t] = [t]
         elif lam == l:
             idx.children[l][p].append(t)
-    if lam == idx.L_top:
+    if idx.L_top >= 1 and lam == idx.L_top:
         idx.top.append(t)
     return lam, p
 

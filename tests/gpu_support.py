@@ -65,7 +65,7 @@ def read_head(ix, h: int) -> GpuHead:
             tok=tok, cnt=cnt, pages=[[int(x) for x in tok[p, :cnt[p]]] for p in range(P)],
             next=ix.export(h, L.ICE_EXP_PAGE_NEXT, l)[:P], owner=ix.export(h, L.ICE_EXP_PAGE_OWNER, l)[:P],
             first=ix.export(h, L.ICE_EXP_OWNER_FIRST, l), tail=ix.export(h, L.ICE_EXP_OWNER_TAIL, l)))
-    top = [int(x) for x in ix.export(h, L.ICE_EXP_TOP)[:st["n_top"]]]
+    top = [int(x) for x in ix.export(h, L.ICE_EXP_TOP)[:st["n_top"]]] if st["n_top"] > 0 else []
     return GpuHead(n=n, L_top=Lt, n_top=st["n_top"], lev=lev, e=e, parent=parent, tables=tables, top=top,
                    stats=st)
 
