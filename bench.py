@@ -1,0 +1,283 @@
+"""Benchmark of the IceCache hot path on one MI355X.
+
+Workload (default): a 36,000-token context for 32 layers x 8 KV heads (256
+independent indexes), 4 query heads per KV head, d = 128, bf16 K/V, keys from
+512-component Gaussian mixtures per head with a random rotation per head.
+A timed step is one decode step of every layer: ``ice_select`` (beam descent,
+top-k pages, GQA union) + ``ice_attend`` (page gather + sparse attention)
+for all 256 heads at a 256-token budget. The index build (keys/s) and the
+insert of one token per head are timed separately and reported beside it.
+
+Prints ONE JSON line (see the fields below). ``--gpus N`` with N > 1 exits:
+the library runs on one GPU and no multi-GPU figure is produced.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s (select+gather+attend) & index keys/s at 36k ctx; % roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    # name: (layers*kv_heads, G, N, d, dtype, centres, rotate, description)
+    "ctx36k": (256, 4, 36000, 128, "bf16", 512, True,
+               "36k-token context, 32 layers x 8 KV heads x 4 query heads, d=128 bf16, 512-component "
+               "Gaussian-mixture keys with per-head rotations"),
+    "llama-layer": (8, 4, 32768, 128, "bf16", 512, False,
+                    "one 32k-token layer, 8 KV heads x 4 query heads, d=128 bf16, 512-component mixtures"),
+    "tiny": (1, 1, 2048, 64, "f32", 32, False, "1 head, 2048 tokens, d=64 fp32, 32-component mixture"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ctx36k", choices=sorted(WORKLOADS))
+    ap.add_argument("--budget", type=int, default=256)
+    ap.add_argument("--budgets", default="64,128,256")
+    ap.add_argument("--builds", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle's timed sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(ix, trace, uni_n, n_uni, d, elt, G):
+    """Bytes the method itself must move for one decode step, from the run's
+    own selections: per head the top-level keys, the keys of the unique
+    level-1 candidates, the keys of the valid rows of the unique candidate
+    pages (scoring), their list entries, plus Q in; for attend the K and V
+    rows of the union pages, Q in and O out."""
+    from ann_retrieval_amd import _lib as L
+    H = trace.shape[0]
+    sel_b = att_b = 0
+    for h in range(H):
+        m = ix.meta[h]
+        Lt = m["L_top"]
+        rows_top = m["n_top"] if Lt >= 1 else 0
+        c1_rows = blocks = pages = page_rows = 0
+        if Lt == 2:
+            kept2 = np.unique(trace[h, :, 0][trace[h, :, 0] >= 0])
+            kept1 = np.unique(trace[h, :, 1][trace[h, :, 1] >= 0])
+            c1_rows = int(m["kids1"][kept2].sum())
+            blocks = int(m["blocks1"][kept2].sum())
+        elif Lt == 1:
+            kept1 = np.unique(trace[h, :, 0][trace[h, :, 0] >= 0])
+        else:
+            kept1 = None
+        if kept1 is not None:
+            pages = int(m["npages0"][kept1].sum())
+            page_rows = int(m["rows0"][kept1].sum())
+        else:
+            pages, page_rows = m["P0"], m["n"]
+        sel_b += (rows_top + c1_rows + page_rows) * d * elt + blocks * (16 * 4 + 8) + pages * 8
+        u = uni_n[h][: n_uni[h]]
+        att_b += 2 * int(m["cnt0"][u].sum()) * d * elt + len(u) * 8
+    q = H * G * d * elt
+    return sel_b + q, att_b + q + H * G * d * 4 + H * G * 4
+
+
+def head_meta(ix, H, cap):
+    """Per-head owner -> (children, blocks, pages, rows) maps for the byte count."""
+    from ann_retrieval_amd import _lib as L
+    meta = []
+    for h in range(H):
+        st = ix.stats(h)
+        m = dict(L_top=st["top_level"], n_top=st["n_top"], n=st["n_tokens"], P0=st["n_pages"][0])
+        own0 = ix.export(h, L.ICE_EXP_PAGE_OWNER, 0)[: st["n_pages"][0]]
+        cnt0 = ix.export(h, L.ICE_EXP_PAGE_CNT, 0)[: st["n_pages"][0]]
+        m["cnt0"] = cnt0
+        ok = own0 >= 0
+        m["npages0"] = np.bincount(own0[ok], minlength=cap + 1)
+        m["rows0"] = np.bincount(own0[ok], weights=cnt0[ok], minlength=cap + 1).astype(np.int64)
+        if st["top_level"] >= 2:
+            P1 = st["n_pages"][1]
+            own1 = ix.export(h, L.ICE_EXP_PAGE_OWNER, 1)[:P1]
+            cnt1 = ix.export(h, L.ICE_EXP_PAGE_CNT, 1)[:P1]
+            m["kids1"] = np.bincount(own1, weights=cnt1, minlength=cap + 1).astype(np.int64)
+            m["blocks1"] = np.bincount(own1, minlength=cap + 1)
+        meta.append(m)
+    ix.meta = meta
+
+
+def cpu_baseline(w, Qs, budget, beam, heads, seed):
+    """The fp64 oracle as it stands, on the host cores, on a bounded sample:
+    its own index build of `heads` heads, then select + attend of those heads
+    for every query of the first steps. Scaled to all heads of the workload."""
+    import threadpoolctl
+    from oracle import icecache as ic
+    K = w.K[:len(heads)].float().cpu().double().numpy()
+    V = w.V[:len(heads)].float().cpu().double().numpy()
+    t0 = time.perf_counter()
+    refs = [ic.build_head(K[i], V[i], h, seed) for i, h in enumerate(heads)]
+    t_build = time.perf_counter() - t0
+    n_steps = 3
+    t0 = time.perf_counter()
+    for s in range(n_steps):
+        Q = Qs[s][:len(heads)].float().cpu().double().numpy()
+        for i, ref in enumerate(refs):
+            sels = [ic.select(ref, Q[i, g], budget, beam)["sel"] for g in range(Q.shape[1])]
+            uni = ic.gqa_union(sels)
+            for g in range(Q.shape[1]):
+                ic.attend(ref, Q[i, g], uni, 1.0 / math.sqrt(Q.shape[2]))
+    t_dec = (time.perf_counter() - t0) / n_steps
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    return t_build, t_dec, threads
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU; no multi-GPU figure is produced",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    from ann_retrieval_amd import synth
+    from ann_retrieval_amd.api import IceIndex
+
+    H, G, N, d, dtype, C, rotate, desc = WORKLOADS[a.workload]
+    budgets = [int(b) for b in a.budgets.split(",")]
+    if a.budget not in budgets:
+        budgets.append(a.budget)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload={a.workload} H={H} G={G} N={N} d={d} {dtype}", file=sys.stderr, flush=True)
+    w, gen = synth.clustered_kv(H, N, d, C, dtype, a.seed, device=dev, rotate=rotate)
+    elt = 2 if dtype == "bf16" else 4
+    n_ins = a.steps + a.warmup
+    ix = IceIndex(H, G, d, dtype, N + n_ins, seed=a.seed, max_budget=max(budgets), device=dev)
+
+    # ---- index build: median of a few full builds
+    bt = []
+    for i in range(a.builds + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        ix.ice_build(w.K, w.V)
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            bt.append(e0.elapsed_time(e1))
+    build_ms = float(np.median(bt))
+    print(f"[bench] build {build_ms:.2f} ms", file=sys.stderr, flush=True)
+    head_meta(ix, H, N + n_ins)
+
+    # ---- decode steps
+    Qs = [synth.decode_queries(w, G, gen, device=dev) for _ in range(a.warmup + a.steps)]
+    results = {}
+    for budget in budgets:
+        k = budget // 16
+        beam = k
+        sel = torch.empty(H, G, k, dtype=torch.int32, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+        for s in range(a.warmup):
+            _, uni, nuni = ix.ice_select(Qs[s], budget, beam)
+            ix.ice_attend(Qs[s], uni, nuni)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for s in range(a.steps):
+            q = Qs[a.warmup + s]
+            ev[s][0].record()
+            _, uni, nuni = ix.ice_select(q, budget, beam)
+            ev[s][1].record()
+            ix.ice_attend(q, uni, nuni)
+            ev[s][2].record()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_step = g0.elapsed_time(g1) / a.steps
+        sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        # algorithmic bytes from the same selections (replayed with a trace)
+        nb = min(a.steps, 4)
+        sb = ab = 0
+        for s in range(nb):
+            q = Qs[a.warmup + s]
+            _, uni, nuni, tr = ix.ice_select(q, budget, beam, trace=True)
+            b1, b2 = algorithmic_bytes(ix, tr.cpu().numpy(), uni.cpu().numpy(), nuni.cpu().numpy(), d, elt, G)
+            sb += b1
+            ab += b2
+        sb /= nb
+        ab /= nb
+        results[budget] = dict(ms_per_step=ms_step, steps_per_s=1000.0 / ms_step, wall_s=wall,
+                               select_ms=sel_ms, attend_ms=att_ms, select_bytes=sb, attend_bytes=ab,
+                               select_gbs=sb / sel_ms / 1e6, attend_gbs=ab / att_ms / 1e6)
+        print(f"[bench] T={budget}: {ms_step*1000:.1f} us/step select {sel_ms*1000:.1f} us "
+              f"({sb/sel_ms/1e6:.0f} GB/s) attend {att_ms*1000:.1f} us ({ab/att_ms/1e6:.0f} GB/s)",
+              file=sys.stderr, flush=True)
+
+    # ---- insert: one token per head per step
+    knew = [synth.new_tokens(w, gen, device=dev) for _ in range(n_ins)]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k_, v_ in knew:
+        ix.ice_insert(k_, v_)
+    e1.record()
+    torch.cuda.synchronize()
+    insert_ms = e0.elapsed_time(e1) / n_ins
+
+    head = results[a.budget]
+    dom = "select" if head["select_ms"] >= head["attend_ms"] else "attend"
+    dom_bytes = head[f"{dom}_bytes"]
+    dom_ms = head[f"{dom}_ms"]
+    achieved = dom_bytes / dom_ms / 1e6
+    out = {
+        "metric": METRIC,
+        "value": head["steps_per_s"],
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": desc, "heads": H, "group": G, "context": N, "d": d, "budget_tokens": a.budget,
+                   "beam": a.budget // 16, "levels": 3, "promote": "1/16", "page": 16},
+        "roofline": {"bound": "hbm", "kernel": f"k_{dom}", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
+        "index_keys_per_s": H * N / (build_ms / 1000.0),
+        "build_ms": build_ms,
+        "insert_ms_per_step": insert_ms,
+        "per_budget": {str(b): {k2: (round(v, 6) if isinstance(v, float) else v) for k2, v in r.items()}
+                       for b, r in results.items()},
+    }
+    if not a.no_cpu:
+        heads = list(range(min(a.cpu_heads, H)))
+        t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(3)], a.budget, a.budget // 16,
+                                               heads, a.seed)
+        per_head_step = t_dec / len(heads)
+        out["cpu_baseline"] = {
+            "value": 1.0 / (per_head_step * H), "unit": "decode steps/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 oracle on {len(heads)} of {H} heads ({N} tokens each): its own index build, then "
+                       f"select+attend for {G} query heads over 3 steps at T={a.budget}; per-head time scaled to "
+                       f"{H} heads"),
+            "index_keys_per_s": len(heads) * N / t_build,
+            "cpu": platform.processor() or platform.machine(),
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
