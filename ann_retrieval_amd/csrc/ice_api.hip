@@ -13,10 +13,6 @@
 
 using namespace ice;
 
-namespace ice {
-size_t select_lds_bytes(int G, int budget);
-}
-
 struct ice_index {
   ice_params p;
   DevLayout L;
