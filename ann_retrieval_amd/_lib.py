@@ -21,7 +21,7 @@ ICE_F32, ICE_BF16 = 0, 1
 ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM = 16, 4, 16, 256
 (ICE_EXP_LEVEL, ICE_EXP_LIFT, ICE_EXP_PARENT, ICE_EXP_PAGE_TOK, ICE_EXP_PAGE_CNT, ICE_EXP_PAGE_NEXT,
  ICE_EXP_PAGE_OWNER, ICE_EXP_OWNER_FIRST, ICE_EXP_OWNER_TAIL, ICE_EXP_TOP, ICE_EXP_PAGE_K, ICE_EXP_PAGE_V,
- ICE_EXP_HEADER) = range(13)
+ ICE_EXP_HEADER, ICE_EXP_OWNER_RUN, ICE_EXP_OWNER_COUNT) = range(15)
 
 
 class IceParams(ctypes.Structure):
@@ -31,7 +31,8 @@ class IceParams(ctypes.Structure):
 
 class IceHeadStats(ctypes.Structure):
     _fields_ = [("n_tokens", c_i32), ("top_level", c_i32), ("n_top", c_i32), ("n_pages", c_i32 * ICE_MAX_LEVELS),
-                ("clamps", c_i32), ("splits", c_i32), ("near_ties", c_i32), ("pad", c_i32), ("M2", ctypes.c_double)]
+                ("clamps", c_i32), ("splits", c_i32), ("near_ties", c_i32), ("overflow", c_i32),
+                ("reserved0", c_i32), ("reserved1", c_i32), ("M2", ctypes.c_double)]
 
 
 _SIGNATURES = {

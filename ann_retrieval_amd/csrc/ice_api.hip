@@ -113,6 +113,8 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
     L->off_pg_owner[l] = c.take(P * 4);
     L->off_first[l] = c.take((cap + 1) * 4);
     L->off_tail[l] = c.take((cap + 1) * 4);
+    L->off_orun[l] = c.take((cap + 1) * 4);
+    L->off_ocnt[l] = c.take((cap + 1) * 4);
     L->off_pgK[l] = c.take(P * ICE_PAGE_CAP * d * elt);
     if (l == 0) L->off_pgV = c.take(P * ICE_PAGE_CAP * d * elt);
     else L->off_pgE[l] = c.take(P * ICE_PAGE_CAP * 4);
@@ -306,7 +308,9 @@ size_t ice_export_bytes(const ice_index* idx, int32_t what, int32_t level) {
     case ICE_EXP_PAGE_NEXT:
     case ICE_EXP_PAGE_OWNER: return tab_ok ? (size_t)L.pcap[level] * 4 : 0;
     case ICE_EXP_OWNER_FIRST:
-    case ICE_EXP_OWNER_TAIL: return tab_ok ? (cap + 1) * 4 : 0;
+    case ICE_EXP_OWNER_TAIL:
+    case ICE_EXP_OWNER_RUN:
+    case ICE_EXP_OWNER_COUNT: return tab_ok ? (cap + 1) * 4 : 0;
     case ICE_EXP_TOP: return (size_t)L.topcap * 4;
     case ICE_EXP_PAGE_K: return tab_ok ? (size_t)L.pcap[level] * ICE_PAGE_CAP * d * elt : 0;
     case ICE_EXP_PAGE_V: return level == 0 ? (size_t)L.pcap[0] * ICE_PAGE_CAP * d * elt : 0;
@@ -334,6 +338,8 @@ int ice_export(const ice_index* idx, int32_t head, int32_t what, int32_t level, 
     case ICE_EXP_PAGE_OWNER: off = L.off_pg_owner[level]; break;
     case ICE_EXP_OWNER_FIRST: off = L.off_first[level]; break;
     case ICE_EXP_OWNER_TAIL: off = L.off_tail[level]; break;
+    case ICE_EXP_OWNER_RUN: off = L.off_orun[level]; break;
+    case ICE_EXP_OWNER_COUNT: off = L.off_ocnt[level]; break;
     case ICE_EXP_TOP: off = L.off_top_tok; break;
     case ICE_EXP_PAGE_K: off = L.off_pgK[level]; break;
     case ICE_EXP_PAGE_V: off = L.off_pgV; break;

@@ -23,7 +23,9 @@ struct Hdr {
   int32_t clamps;
   int32_t splits;
   int32_t near_ties;
-  int32_t pad;
+  int32_t overflow;        // page table full (ruled out within capacity)
+  int32_t reserved0;
+  int32_t reserved1;
   double M2;
 };
 static_assert(sizeof(Hdr) == sizeof(ice_head_stats), "header mirrors ice_head_stats");
@@ -45,6 +47,9 @@ struct DevLayout {
   int64_t off_parent[ICE_MAX_LEVELS];
   int64_t off_pg_tok[ICE_MAX_LEVELS], off_pg_cnt[ICE_MAX_LEVELS], off_pg_next[ICE_MAX_LEVELS];
   int64_t off_pg_owner[ICE_MAX_LEVELS], off_first[ICE_MAX_LEVELS], off_tail[ICE_MAX_LEVELS];
+  // per owner slot: pages in the contiguous run that starts at first[], and
+  // the owner's member count (its pages are all full except the last)
+  int64_t off_orun[ICE_MAX_LEVELS], off_ocnt[ICE_MAX_LEVELS];
   int64_t off_pgK[ICE_MAX_LEVELS], off_pgE[ICE_MAX_LEVELS], off_pgV;
   int64_t off_top_tok, off_top_K, off_top_E;
 };

@@ -281,6 +281,8 @@ __global__ __launch_bounds__(kScanThreads) void k_pack_scan(DevLayout L, WsLayou
   int32_t* pg_owner = at<int32_t>(hb, L.off_pg_owner[level]);
   int32_t* first = at<int32_t>(hb, L.off_first[level]);
   int32_t* tail = at<int32_t>(hb, L.off_tail[level]);
+  int32_t* orun = at<int32_t>(hb, L.off_orun[level]);
+  int32_t* ocnt = at<int32_t>(hb, L.off_ocnt[level]);
   int runc = 0, runp = 0;
   for (int base = 0; base < v.n_own; base += kScanThreads) {
     const int o = base + threadIdx.x;
@@ -297,6 +299,8 @@ __global__ __launch_bounds__(kScanThreads) void k_pack_scan(DevLayout L, WsLayou
       const int slot = v.root ? L.cap : tok;
       first[slot] = np ? pb : -1;
       tail[slot] = np ? pb + np - 1 : -1;
+      orun[slot] = np;
+      ocnt[slot] = c;
       for (int j = 0; j < np; ++j) {
         const int p = pb + j;
         const int pc = min(ICE_PAGE_CAP, c - j * ICE_PAGE_CAP);
@@ -436,6 +440,8 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
     if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_parent[l], L.cap, -1, s))) return err;
     if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_first[l], L.cap + 1, -1, s))) return err;
     if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_tail[l], L.cap + 1, -1, s))) return err;
+    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_orun[l], L.cap + 1, 0, s))) return err;
+    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_ocnt[l], L.cap + 1, 0, s))) return err;
   }
   if (n > 0) {
     k_norm_level<D, T><<<dim3(blocks_for(n, 64), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws);

@@ -38,9 +38,12 @@ __device__ bool place_token(const DevLayout& L, void* hb, Hdr* hdr, int tb, int 
   int32_t* pg_owner = at<int32_t>(hb, L.off_pg_owner[tb]);
   int32_t* first = at<int32_t>(hb, L.off_first[tb]);
   int32_t* tail = at<int32_t>(hb, L.off_tail[tb]);
+  int32_t* orun = at<int32_t>(hb, L.off_orun[tb]);
+  int32_t* ocnt = at<int32_t>(hb, L.off_ocnt[tb]);
   const int os = owner == ICE_ROOT ? L.cap : owner;
   const int tl = tail[os];
   if (tl >= 0 && pg_cnt[tl] < ICE_PAGE_CAP) {
+    ocnt[os] += 1;
     page = tl;
     slot = pg_cnt[tl];
     pg_cnt[tl] = slot + 1;
@@ -53,9 +56,13 @@ __device__ bool place_token(const DevLayout& L, void* hb, Hdr* hdr, int tb, int 
   if (tl >= 0) {
     pg_next[tl] = p;
     if (tb == 0) hdr->splits += 1;   // a KV page split off; upper tables only chain storage blocks
+    // the contiguous run grows while the new page directly follows it
+    if (tl == first[os] + orun[os] - 1 && p == tl + 1) orun[os] += 1;
   } else {
     first[os] = p;
+    orun[os] = 1;
   }
+  ocnt[os] += 1;
   tail[os] = p;
   pg_owner[p] = owner;
   pg_next[p] = -1;
@@ -217,7 +224,7 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
       }
       lev[t] = (int8_t)lam;
       eall[t] = et;
-      if (!ok) hdr->pad = 1;   // page table overflow (ruled out by the capacity bound)
+      if (!ok) hdr->overflow = 1;   // page table overflow (ruled out by the capacity bound)
       e_sh = et;
     }
     __syncthreads();

@@ -9,32 +9,38 @@
 // lifted as [q, 0], the lifted distance |q|^2 + M^2 - 2 q.k ranks exactly like
 // q.k descending, which is what is scored. A page scores its best token.
 //
-// One block of 16 waves per head; each query head gets W = 16/G waves. At
-// every level the candidate rows are split over the query's waves: a wave
-// scores 16 rows per pass with 4 lanes per row (bf16 dot2 on gfx950), with
-// the loads of several 16-row groups in flight before any arithmetic, and
-// folds every 64 candidate keys into its own top list in LDS. The W wave lists
-// of a query are then merged by rank (binary search in the other sorted
-// lists). Keys pack (score, ~id) into 64 bits, so "score descending, id
-// ascending" is plain unsigned order.
+// k_select: one block of 4 waves per (head, query head); the blocks of a head
+// are mapped to one XCD (workgroups go round-robin over the 8 XCDs) so they
+// share its L2. At every level the candidate rows are split over the waves: a
+// wave scores 16 rows per pass with 4 lanes per row (bf16 dot2 on gfx950),
+// issuing the loads of several 16-row groups before any arithmetic. Keys pack
+// (score, ~id) into 64 bits, so "score descending, id ascending" is plain
+// unsigned order. Each wave keeps its top list in registers, one key per lane:
+// a chunk of 64 candidates is bitonic-sorted across the wave and merged by
+// taking max(list[i], chunk[63-i]) (the 64 largest of both, as a bitonic
+// sequence) followed by a 6-step bitonic merge; the lists of the 4 waves are
+// merged the same way. Lists longer than 64 keys (beams or budgets beyond 64
+// entries) use a slower LDS list instead.
+// k_union: the union of a head's selected pages, ascending page id.
 #include "ice_launch.h"
+
+#include <type_traits>
 
 namespace ice {
 namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 16;
-constexpr int kChainBatch = 64;
+constexpr int kWaves = 4;           // waves per (head, query head) block
+constexpr int kChainBatch = 64;     // pages gathered per round
 
-// Scoring geometry: 4 lanes per row, 16 rows per wave pass; each lane holds a
-// quarter of the query and reads a quarter of every row.
+// ---- scoring geometry: 4 lanes per row, 16 rows per wave pass -------------
 template <int D, class T>
 struct Quarter {
   static constexpr int ROWB = D * (int)sizeof(T);
   static constexpr int PB = ROWB / 4;                 // bytes per lane per row
   static constexpr int NL = PB / 16;                  // 16-byte loads per lane per row
-  static constexpr int GB = NL >= 16 ? 1 : 16 / NL;   // row groups per load batch
+  static constexpr int GB = NL >= 8 ? 2 : 4;          // row groups per load batch
   V4 q[NL];
   int part;
 
@@ -44,7 +50,7 @@ struct Quarter {
     for (int i = 0; i < NL; ++i)
       q[i] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(qrow) + part * PB + i * 16);
   }
-  // loads this lane's quarter of `row`, or zeros when `ok` is false
+  // this lane's quarter of `row`, or zeros when `ok` is false
   __device__ inline void fetch(bool ok, const T* row, V4* out) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -87,87 +93,141 @@ __device__ inline float rows_max(float s) {
   return s;
 }
 
-// ---- LDS layout (bytes), shared by the launcher and the kernel --------------
+__device__ inline uint64_t shfl64(uint64_t v, int src) {
+  const int lo = __shfl((int)(uint32_t)v, src, 64), hi = __shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ inline uint64_t shfl_xor64(uint64_t v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m, 64), hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Sorts one key per lane across the wave, descending (lane 0 largest).
+__device__ inline uint64_t wave_sort_desc(uint64_t x, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t y = shfl_xor64(x, j);
+      x = (((lane & k) == 0) == ((lane & j) == 0)) ? umax64(x, y) : umin64(x, y);
+    }
+  }
+  return x;
+}
+// Top 64 of two descending wave lists, descending.
+__device__ inline uint64_t wave_merge_desc(uint64_t a, uint64_t b_sorted, int lane) {
+  uint64_t t = umax64(a, shfl64(b_sorted, 63 - lane));
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const uint64_t y = shfl_xor64(t, j);
+    t = (lane & j) == 0 ? umax64(t, y) : umin64(t, y);
+  }
+  return t;
+}
+
+// ---- LDS layout ------------------------------------------------------------
 struct SelLds {
   int lcap;           // list capacity = max(beam, pages per query)
-  int wave_bytes;     // per wave: list[2][lcap] u64, chunk[64] u64, cand[64] i32, 4 ints
-  int off_query;      // per query: list[lcap] u64
-  int off_wn;         // per wave: list count and current buffer (2 ints)
-  int off_qn;         // per query: list count
-  int off_sel;        // [G][kpg] i32
-  int off_flag;       // [G][kpg] i32
+  int wave_bytes;     // per wave: [LDS lists: list[2][lcap] u64] chunk[64] u64, cand/cval[64] i32, 4 ints
+  int off_comb;       // register lists: [2 parities][kWaves][64] u64
+  int off_query;      // LDS lists: query list[lcap] u64
+  int off_wn;         // LDS lists: per wave count and buffer (2 ints)
+  int off_misc;       // 4 ints
   int total;
 };
 
-__host__ __device__ inline SelLds sel_lds(int G, int lcap, int kpg) {
+__host__ __device__ inline SelLds sel_lds(int lcap, bool big) {
   SelLds s;
   s.lcap = lcap;
-  s.wave_bytes = 2 * lcap * 8 + 64 * 8 + kChainBatch * 4 + 16;
-  s.off_query = kWaves * s.wave_bytes;
-  s.off_wn = s.off_query + G * lcap * 8;
-  s.off_qn = s.off_wn + kWaves * 8;
-  s.off_sel = s.off_qn + ICE_MAX_GROUP * 4;
-  s.off_flag = s.off_sel + G * kpg * 4;
-  s.total = s.off_flag + G * kpg * 4;
+  s.wave_bytes = (big ? 2 * lcap * 8 : 0) + 64 * 8 + 2 * kChainBatch * 4 + 16;
+  s.off_comb = kWaves * s.wave_bytes;
+  s.off_query = s.off_comb + (big ? 0 : 2 * kWaves * 64 * 8);
+  s.off_wn = s.off_query + (big ? lcap * 8 : 0);
+  s.off_misc = s.off_wn + kWaves * 8;
+  s.total = s.off_misc + 16;
   return s;
 }
 
 struct WaveArea {
-  uint64_t* lists;     // two buffers of lcap keys each
+  uint64_t* lists;     // two buffers of lcap keys each (LDS lists only)
   int lcap;
   uint64_t* chunk;
-  int32_t* cand;
+  int32_t* cand;       // gathered page / block ids
+  int32_t* cval;       // their valid slots
   int32_t* ncand;
 };
 
-__device__ inline WaveArea wave_area(char* smem, const SelLds& S, int wv) {
+__device__ inline WaveArea wave_area(char* smem, const SelLds& S, int wv, bool big) {
   char* b = smem + wv * S.wave_bytes;
   WaveArea a;
   a.lists = reinterpret_cast<uint64_t*>(b);
   a.lcap = S.lcap;
-  a.chunk = a.lists + 2 * S.lcap;
+  a.chunk = a.lists + (big ? 2 * S.lcap : 0);
   a.cand = reinterpret_cast<int32_t*>(a.chunk + 64);
-  a.ncand = a.cand + kChainBatch;
+  a.cval = a.cand + kChainBatch;
+  a.ncand = a.cval + kChainBatch;
   return a;
 }
 
-// Wave-local sorted (descending) top list of at most `cap` keys.
-struct TopList {
-  int cur, n, cap;
+// ---- wave top lists --------------------------------------------------------
+// Register list (cap <= 64): lane i holds entry i, 0 = empty.
+struct RegTop {
+  uint64_t L;
+  int cap;
+  __device__ inline void init(int c) {
+    L = 0ull;
+    cap = c;
+  }
+  __device__ inline void push(const WaveArea&, uint64_t x, int lane) {
+    const uint64_t thr = shfl64(L, cap - 1);   // 0 until the list is full
+    if (__ballot(x > thr) == 0) return;
+    const uint64_t t = wave_merge_desc(L, wave_sort_desc(x, lane), lane);
+    L = lane < cap ? t : 0ull;
+  }
 };
 
-// Merges the 64 keys in `a.chunk` (0 = empty) into the list.
-__device__ void merge_chunk(const WaveArea& a, TopList& tl, int lane) {
-  wave_sync();
-  const uint64_t* Lc = a.lists + tl.cur * a.lcap;
-  uint64_t* Nx = a.lists + (tl.cur ^ 1) * a.lcap;
-  const uint64_t x = a.chunk[lane];
-  const uint64_t thr = tl.n == tl.cap ? Lc[tl.cap - 1] : 0ull;
-  const bool live = x > thr;
-  const uint64_t live_mask = __ballot(live);
-  if (live_mask == 0) {
+// LDS list (any cap up to ICE_MAX_BEAM), sorted descending, double-buffered.
+struct LdsTop {
+  int cur, n, cap;
+  __device__ inline void init(int c) {
+    cur = 0;
+    n = 0;
+    cap = c;
+  }
+  __device__ void push(const WaveArea& a, uint64_t x, int lane) {
+    a.chunk[lane] = x;
     wave_sync();
-    return;
+    const uint64_t* Lc = a.lists + cur * a.lcap;
+    uint64_t* Nx = a.lists + (cur ^ 1) * a.lcap;
+    const uint64_t thr = n == cap ? Lc[cap - 1] : 0ull;
+    const bool live = x > thr;
+    const uint64_t live_mask = __ballot(live);
+    if (live_mask == 0) {
+      wave_sync();
+      return;
+    }
+    int rc = 0;
+    for (int j = 0; j < 64; ++j) rc += a.chunk[j] > x;
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (Lc[mid] > x) lo = mid + 1;
+      else hi = mid;
+    }
+    for (int i = lane; i < n; i += 64) {
+      const uint64_t y = Lc[i];
+      int c = 0;
+      for (int j = 0; j < 64; ++j) c += a.chunk[j] > y;
+      if (i + c < cap) Nx[i + c] = y;
+    }
+    if (live && lo + rc < cap) Nx[lo + rc] = x;
+    n = min(cap, n + __popcll(live_mask));
+    cur ^= 1;
+    wave_sync();
   }
-  int rc = 0;
-  for (int j = 0; j < 64; ++j) rc += a.chunk[j] > x;
-  int lo = 0, hi = tl.n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (Lc[mid] > x) lo = mid + 1;
-    else hi = mid;
-  }
-  for (int i = lane; i < tl.n; i += 64) {
-    const uint64_t y = Lc[i];
-    int c = 0;
-    for (int j = 0; j < 64; ++j) c += a.chunk[j] > y;
-    if (i + c < tl.cap) Nx[i + c] = y;
-  }
-  if (live && lo + rc < tl.cap) Nx[lo + rc] = x;
-  tl.n = min(tl.cap, tl.n + __popcll(live_mask));
-  tl.cur ^= 1;
-  wave_sync();
-}
+};
 
 // number of keys greater than x in a descending list of n keys
 __device__ inline int count_greater(const uint64_t* l, int n, uint64_t x) {
@@ -180,20 +240,37 @@ __device__ inline int count_greater(const uint64_t* l, int n, uint64_t x) {
   return lo;
 }
 
-// Gathers up to kChainBatch page ids from the chains in `cur` (lane-owned
-// entries); each lane resumes its walk where the batch filled up.
-__device__ inline int gather_chains(const WaveArea& a, int32_t (&cur)[ICE_MAX_BEAM / 64], const int32_t* next,
-                                    int lane) {
+// Walks the pages of one owner per lane. An owner's pages are all full except
+// its last; the pages of the build form one contiguous run starting at
+// first[], so they need no pointer chasing; only pages split off later by
+// inserts are reached through next[].
+struct OwnerWalk {
+  int page, idx, first, run, cnt;
+  __device__ inline void start(int owner_slot, const int32_t* firsts, const int32_t* runs, const int32_t* cnts) {
+    page = -1;
+    if (owner_slot < 0) return;
+    first = firsts[owner_slot];
+    run = runs[owner_slot];
+    cnt = cnts[owner_slot];
+    idx = 0;
+    page = cnt > 0 ? first : -1;
+  }
+};
+
+// Gathers up to kChainBatch (page, valid slots) pairs from this wave's lanes'
+// owners; a lane resumes where the batch filled up. Returns the count.
+__device__ inline int gather_pages(const WaveArea& a, OwnerWalk& w, const int32_t* next, int lane) {
   if (lane == 0) *a.ncand = 0;
   wave_sync();
-#pragma unroll
-  for (int e = 0; e < ICE_MAX_BEAM / 64; ++e) {
-    while (cur[e] >= 0) {
-      const int slot = atomicAdd(a.ncand, 1);
-      if (slot >= kChainBatch) break;
-      a.cand[slot] = cur[e];
-      cur[e] = next[cur[e]];
-    }
+  while (w.page >= 0) {
+    const int slot = atomicAdd(a.ncand, 1);
+    if (slot >= kChainBatch) break;
+    a.cand[slot] = w.page;
+    a.cval[slot] = min(ICE_PAGE_CAP, w.cnt - ICE_PAGE_CAP * w.idx);
+    ++w.idx;
+    if (w.idx * ICE_PAGE_CAP >= w.cnt) w.page = -1;
+    else if (w.idx < w.run) w.page = w.first + w.idx;
+    else w.page = next[w.page];
   }
   wave_sync();
   const int n = min(*a.ncand, kChainBatch);
@@ -201,23 +278,50 @@ __device__ inline int gather_chains(const WaveArea& a, int32_t (&cur)[ICE_MAX_BE
   return n;
 }
 
+// Keys of 4 row groups, one candidate per lane: group g, row r -> lane 16g + r.
+// `ok[g]` is per lane (its row of group g), `row[g]` that row, `tok[g]` its id.
 template <int D, class T>
-__global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, const T* Q, int budget, int beam,
-                                                 int W, int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace) {
+__device__ inline uint64_t chunk_keys(const Quarter<D, T>& qs, const bool (&ok)[4], const T* const (&row)[4],
+                                      const int (&tok)[4], int lane) {
   using QG = Quarter<D, T>;
+  uint64_t key[4];
+#pragma unroll
+  for (int g0 = 0; g0 < 4; g0 += QG::GB) {
+    V4 buf[QG::GB][QG::NL];
+#pragma unroll
+    for (int b = 0; b < QG::GB; ++b) qs.fetch(ok[g0 + b], row[g0 + b], buf[b]);
+#pragma unroll
+    for (int b = 0; b < QG::GB; ++b) {
+      const float s = quad_sum(qs.dot(buf[b]));
+      key[g0 + b] = ok[g0 + b] ? make_key(s, tok[g0 + b]) : 0ull;
+    }
+  }
+  const int src = (lane & 15) * 4, grp = lane >> 4;
+  const uint64_t x0 = shfl64(key[0], src), x1 = shfl64(key[1], src);
+  const uint64_t x2 = shfl64(key[2], src), x3 = shfl64(key[3], src);
+  return grp == 0 ? x0 : grp == 1 ? x1 : grp == 2 ? x2 : x3;
+}
+
+template <int D, class T, bool BIG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_select(
+    DevLayout L, const void* blob, const T* Q, int budget, int beam, int32_t* sel, int32_t* trace) {
+  using QG = Quarter<D, T>;
+  using Top = std::conditional_t<BIG, LdsTop, RegTop>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = L.G;
-  const int g = wv / W, j = wv % W;      // query head, wave within the query
+  // block -> (head, query head): the G blocks of a head share an XCD
+  const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
+  const int h = (rest / G) * 8 + xcd, g = rest % G;
+  if (h >= L.H) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int W = kWaves, j = wv;
   const int kpg = budget / ICE_PAGE_CAP;
-  const SelLds S = sel_lds(G, max(beam, kpg), kpg);
-  const WaveArea A = wave_area(smem, S, wv);
-  uint64_t* qlist = reinterpret_cast<uint64_t*>(smem + S.off_query) + g * S.lcap;
+  const SelLds S = sel_lds(max(beam, kpg), BIG);
+  const WaveArea A = wave_area(smem, S, wv, BIG);
+  uint64_t* comb = reinterpret_cast<uint64_t*>(smem + S.off_comb);
+  uint64_t* qlist = reinterpret_cast<uint64_t*>(smem + S.off_query);
   int32_t* wn = reinterpret_cast<int32_t*>(smem + S.off_wn);
-  int32_t* qn = reinterpret_cast<int32_t*>(smem + S.off_qn);
-  int32_t* sel_all = reinterpret_cast<int32_t*>(smem + S.off_sel);
-  int32_t* first_flag = reinterpret_cast<int32_t*>(smem + S.off_flag);
+  int32_t* misc = reinterpret_cast<int32_t*>(smem + S.off_misc);
 
   const void* hb = head_base(blob, L, h);
   const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
@@ -231,150 +335,155 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
   if (tr && j == 0)
     for (int i = lane; i < L.L * beam; i += 64) tr[i] = -1;
 
-  // Merges the W wave lists of every query into its query list (all waves).
-  auto combine = [&](TopList& tl, int cap) {
-    if (lane == 0) {
-      wn[2 * wv] = tl.n;
-      wn[2 * wv + 1] = tl.cur;
-    }
-    __syncthreads();
-    const uint64_t* mine = A.lists + tl.cur * A.lcap;
-    int tot = 0;
-    for (int jj = 0; jj < W; ++jj) tot += wn[2 * (g * W + jj)];
-    for (int i = lane; i < tl.n; i += 64) {
-      const uint64_t x = mine[i];
-      int rank = i;
-      for (int jj = 0; jj < W; ++jj) {
-        if (jj == j) continue;
-        const int ow = g * W + jj;
-        const uint64_t* other = reinterpret_cast<const uint64_t*>(smem + ow * S.wave_bytes) + wn[2 * ow + 1] * S.lcap;
-        rank += count_greater(other, wn[2 * ow], x);
+  // the query head's kept list after each cut: a register list (lane i holds
+  // entry i) or, for long lists, qlist in LDS
+  uint64_t ql = 0ull;
+  int qcount = 0, parity = 0;
+  auto combine = [&](Top& t, int cap) {
+    if constexpr (!BIG) {
+      uint64_t* area = comb + parity * kWaves * 64;
+      area[wv * 64 + lane] = t.L;
+      __syncthreads();
+      uint64_t r = t.L;
+      for (int jj = 0; jj < W; ++jj)
+        if (jj != j) r = wave_merge_desc(r, area[jj * 64 + lane], lane);
+      ql = lane < cap ? r : 0ull;
+      qcount = __popcll(__ballot(ql != 0ull));
+      parity ^= 1;
+    } else {
+      if (lane == 0) {
+        wn[2 * wv] = t.n;
+        wn[2 * wv + 1] = t.cur;
       }
-      if (rank < cap) qlist[rank] = x;
+      __syncthreads();
+      const uint64_t* mine = A.lists + t.cur * A.lcap;
+      int tot = 0;
+      for (int jj = 0; jj < W; ++jj) tot += wn[2 * jj];
+      for (int i = lane; i < t.n; i += 64) {
+        const uint64_t x = mine[i];
+        int rank = i;
+        for (int jj = 0; jj < W; ++jj) {
+          if (jj == j) continue;
+          const uint64_t* other = reinterpret_cast<const uint64_t*>(smem + jj * S.wave_bytes) + wn[2 * jj + 1] * S.lcap;
+          rank += count_greater(other, wn[2 * jj], x);
+        }
+        if (rank < cap) qlist[rank] = x;
+      }
+      if (j == 0 && lane == 0) misc[0] = min(cap, tot);
+      __syncthreads();
+      qcount = misc[0];
     }
-    if (j == 0 && lane == 0) qn[g] = min(cap, tot);
-    __syncthreads();
   };
-  auto emit_trace = [&](int cut) {
-    if (tr && j == 0)
-      for (int i = lane; i < qn[g]; i += 64) tr[cut * beam + i] = key_id(qlist[i]);
+  // owner (token id) of kept entry oi, -1 past the list; every lane calls it
+  auto kept = [&](int oi) -> int {
+    if constexpr (!BIG) {
+      const uint64_t k = shfl64(ql, oi & 63);
+      return oi < qcount ? key_id(k) : -1;
+    } else {
+      return oi < qcount ? key_id(qlist[oi]) : -1;
+    }
+  };
+  auto emit = [&](int32_t* dst, int n_out) {   // kept ids (rank order), -1 padded
+    if constexpr (!BIG) {
+      if (lane < n_out) dst[lane] = lane < qcount ? key_id(ql) : -1;
+    } else {
+      for (int i = lane; i < n_out; i += 64) dst[i] = i < qcount ? key_id(qlist[i]) : -1;
+    }
   };
 
   int cut = 0;
-  int32_t cur[ICE_MAX_BEAM / 64];
   if (n_tok > 0 && Ltop >= 1) {
-    // ---- top level: every point of the top list, 16-row groups split over the query's waves
+    // ---- top level: every point of the top list, 16-row groups split over the waves
     {
       const int n_top = hdr->n_top;
       const int32_t* top_tok = at<int32_t>(hb, L.off_top_tok);
       const T* top_K = at<T>(hb, L.off_top_K);
       const int ngroups = (n_top + 15) / 16;
-      TopList tl{0, 0, beam};
-      int fill = 0;
-      for (int m0 = j; m0 < ngroups; m0 += W * QG::GB) {
-        V4 buf[QG::GB][QG::NL];
+      Top tl;
+      tl.init(beam);
+      for (int m0 = j; m0 < ngroups; m0 += 4 * W) {
+        bool ok[4];
+        const T* rp[4];
+        int tk[4];
 #pragma unroll
-        for (int b = 0; b < QG::GB; ++b) {
+        for (int b = 0; b < 4; ++b) {
           const int r = (m0 + b * W) * 16 + row;
-          qs.fetch(r < n_top, top_K + (int64_t)(r < n_top ? r : 0) * D, buf[b]);
+          ok[b] = r < n_top;
+          rp[b] = top_K + (int64_t)(ok[b] ? r : 0) * D;
+          tk[b] = ok[b] ? top_tok[r] : 0;
         }
-#pragma unroll
-        for (int b = 0; b < QG::GB; ++b) {
-          const int r = (m0 + b * W) * 16 + row;
-          const float s = quad_sum(qs.dot(buf[b]));
-          if ((lane & 3) == 0) A.chunk[fill + row] = r < n_top ? make_key(s, top_tok[r]) : 0ull;
-          fill += 16;
-          if (fill == 64) {
-            merge_chunk(A, tl, lane);
-            fill = 0;
-          }
-        }
-      }
-      if (fill) {
-        if (lane >= fill) A.chunk[lane] = 0ull;
-        merge_chunk(A, tl, lane);
+        tl.push(A, chunk_keys<D, T>(qs, ok, rp, tk, lane), lane);
       }
       combine(tl, beam);
-      emit_trace(cut++);
+      if (tr && j == 0) emit(tr + cut * beam, beam);
+      ++cut;
     }
     // ---- levels Ltop-1 .. 1: the children of the kept points
     for (int l = Ltop - 1; l >= 1; --l) {
-      const int32_t* first = at<int32_t>(hb, L.off_first[l]);
       const int32_t* next = at<int32_t>(hb, L.off_pg_next[l]);
       const int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[l]);
-      const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[l]);
       const T* pgK = at<T>(hb, L.off_pgK[l]);
-      const int nq = qn[g];
+      OwnerWalk ow;
+      ow.start(kept(j + W * lane), at<int32_t>(hb, L.off_first[l]), at<int32_t>(hb, L.off_orun[l]),
+               at<int32_t>(hb, L.off_ocnt[l]));
+      Top tl;
+      tl.init(beam);
+      for (int nb; (nb = gather_pages(A, ow, next, lane)) > 0;) {
+        for (int b0 = 0; b0 < nb; b0 += 4) {
+          bool ok[4];
+          const T* rp[4];
+          int tk[4];
 #pragma unroll
-      for (int e = 0; e < ICE_MAX_BEAM / 64; ++e) {
-        const int oi = j + W * (lane + 64 * e);
-        cur[e] = oi < nq ? first[key_id(qlist[oi])] : -1;
-      }
-      __syncthreads();   // every wave has read the old query list
-      TopList tl{0, 0, beam};
-      int fill = 0;
-      for (int nb; (nb = gather_chains(A, cur, next, lane)) > 0;) {
-        for (int b0 = 0; b0 < nb; b0 += QG::GB) {
-          V4 buf[QG::GB][QG::NL];
-          int blk[QG::GB];
-#pragma unroll
-          for (int b = 0; b < QG::GB; ++b) {
-            blk[b] = b0 + b < nb ? A.cand[b0 + b] : -1;
-            const bool ok = blk[b] >= 0 && row < pg_cnt[blk[b]];
-            qs.fetch(ok, pgK + ((int64_t)(ok ? blk[b] : 0) * 16 + row) * D, buf[b]);
+          for (int b = 0; b < 4; ++b) {
+            const int blk = b0 + b < nb ? A.cand[b0 + b] : -1;
+            ok[b] = blk >= 0 && row < A.cval[b0 + b];
+            const int64_t r = (int64_t)(ok[b] ? blk : 0) * ICE_PAGE_CAP + row;
+            rp[b] = pgK + r * D;
+            tk[b] = ok[b] ? pg_tok[r] : 0;
           }
-#pragma unroll
-          for (int b = 0; b < QG::GB; ++b) {
-            const bool ok = blk[b] >= 0 && row < pg_cnt[blk[b]];
-            const float s = quad_sum(qs.dot(buf[b]));
-            if ((lane & 3) == 0)
-              A.chunk[fill + row] = ok ? make_key(s, pg_tok[(int64_t)blk[b] * 16 + row]) : 0ull;
-            fill += 16;
-            if (fill == 64) {
-              merge_chunk(A, tl, lane);
-              fill = 0;
-            }
-          }
+          tl.push(A, chunk_keys<D, T>(qs, ok, rp, tk, lane), lane);
         }
       }
-      if (fill) {
-        if (lane >= fill) A.chunk[lane] = 0ull;
-        merge_chunk(A, tl, lane);
-      }
       combine(tl, beam);
-      emit_trace(cut++);
+      if (tr && j == 0) emit(tr + cut * beam, beam);
+      ++cut;
     }
   }
 
   // ---- level 0: the pages of the kept level-1 points (every page at the root)
   {
-    TopList tl{0, 0, kpg};
+    Top tl;
+    tl.init(kpg);
     if (n_tok > 0) {
       const int32_t* next = at<int32_t>(hb, L.off_pg_next[0]);
-      const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
       const T* pgK = at<T>(hb, L.off_pgK[0]);
-      const int32_t* first = at<int32_t>(hb, L.off_first[0]);
-      const int n_pages = hdr->n_pages[0];
+      const int32_t* firsts = at<int32_t>(hb, L.off_first[0]);
+      const int32_t* runs = at<int32_t>(hb, L.off_orun[0]);
+      const int32_t* cnts = at<int32_t>(hb, L.off_ocnt[0]);
+      OwnerWalk ow;
+      int root_next = j, root_cnt = 0, n_pages = 0;
       if (Ltop >= 1) {
-        const int nq = qn[g];
-#pragma unroll
-        for (int e = 0; e < ICE_MAX_BEAM / 64; ++e) {
-          const int oi = j + W * (lane + 64 * e);
-          cur[e] = oi < nq ? first[key_id(qlist[oi])] : -1;
-        }
+        ow.start(kept(j + W * lane), firsts, runs, cnts);
+      } else {
+        // root: chain order is page id order; the pages are split over the waves by id
+        ow.page = -1;
+        root_cnt = cnts[L.cap];
+        n_pages = hdr->n_pages[0];
       }
-      __syncthreads();
+      uint64_t pk = 0ull;
       int fill = 0;
-      // root: the pages are split over the waves by id, no chain walk
-      int root_next = j;
       for (;;) {
         int nb;
         if (Ltop >= 1) {
-          nb = gather_chains(A, cur, next, lane);
+          nb = gather_pages(A, ow, next, lane);
         } else {
           nb = min(kChainBatch, (n_pages - root_next + W - 1) / W);
           if (nb > 0) {
-            for (int i = lane; i < nb; i += 64) A.cand[i] = root_next + i * W;
+            for (int i = lane; i < nb; i += 64) {
+              const int pg = root_next + i * W;
+              A.cand[i] = pg;
+              A.cval[i] = min(ICE_PAGE_CAP, root_cnt - ICE_PAGE_CAP * pg);
+            }
             root_next += nb * W;
           }
           wave_sync();
@@ -382,95 +491,121 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
         if (nb <= 0) break;
         for (int b0 = 0; b0 < nb; b0 += QG::GB) {
           V4 buf[QG::GB][QG::NL];
-          int pg[QG::GB];
+          int pg[QG::GB], cv[QG::GB];
 #pragma unroll
           for (int b = 0; b < QG::GB; ++b) {
             pg[b] = b0 + b < nb ? A.cand[b0 + b] : -1;
-            const bool ok = pg[b] >= 0 && row < pg_cnt[pg[b]];
-            qs.fetch(ok, pgK + ((int64_t)(ok ? pg[b] : 0) * 16 + row) * D, buf[b]);
+            cv[b] = b0 + b < nb ? A.cval[b0 + b] : 0;
+            const bool ok = pg[b] >= 0 && row < cv[b];
+            qs.fetch(ok, pgK + ((int64_t)(ok ? pg[b] : 0) * ICE_PAGE_CAP + row) * D, buf[b]);
           }
 #pragma unroll
           for (int b = 0; b < QG::GB; ++b) {
             if (pg[b] < 0) continue;
             float s = quad_sum(qs.dot(buf[b]));
-            if (row >= pg_cnt[pg[b]]) s = -INFINITY;
+            if (row >= cv[b]) s = -INFINITY;
             s = rows_max(s);
-            if (lane == 0) A.chunk[fill] = make_key(s, pg[b]);
+            if (lane == fill) pk = make_key(s, pg[b]);
             if (++fill == 64) {
-              merge_chunk(A, tl, lane);
+              tl.push(A, pk, lane);
+              pk = 0ull;
               fill = 0;
             }
           }
         }
       }
-      if (fill) {
-        if (lane >= fill) A.chunk[lane] = 0ull;
-        merge_chunk(A, tl, lane);
-      }
-    } else {
-      __syncthreads();
+      if (fill) tl.push(A, pk, lane);
     }
     combine(tl, kpg);
   }
-
   // ---- outputs of this query head
-  if (j == 0) {
-    int32_t* srow = sel + ((int64_t)h * G + g) * kpg;
-    for (int i = lane; i < kpg; i += 64) {
-      const int v = i < qn[g] ? key_id(qlist[i]) : -1;
-      srow[i] = v;
-      sel_all[g * kpg + i] = v;
+  if (j == 0) emit(sel + ((int64_t)h * G + g) * kpg, kpg);
+}
+
+// Union of the G selection rows of a head, ascending, -1 padded. Rows of up to
+// 64 entries in total are sorted in one wave; longer ones by rank in LDS.
+__global__ __launch_bounds__(256) void k_union(const int32_t* sel, int tot, int32_t* uni, int32_t* n_uni) {
+  extern __shared__ int32_t u_lds[];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int32_t* s = sel + (int64_t)h * tot;
+  int32_t* u = uni + (int64_t)h * tot;
+  if (tot <= 64) {
+    if (tid >= 64) return;
+    int v = lane < tot ? s[lane] : INT_MAX;
+    if (v < 0) v = INT_MAX;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        const int y = __shfl_xor(v, jj, 64);
+        v = (((lane & k) == 0) == ((lane & jj) == 0)) ? min(v, y) : max(v, y);
+      }
     }
+    const int prev = __shfl_up(v, 1, 64);
+    const bool keep = v != INT_MAX && (lane == 0 || v != prev);
+    const uint64_t m = __ballot(keep);
+    const int n = __popcll(m);
+    if (keep) u[__popcll(m & ((1ull << lane) - 1ull))] = v;
+    if (lane >= n && lane < tot) u[lane] = -1;
+    if (lane == 0) n_uni[h] = n;
+    return;
   }
+  int32_t* vals = u_lds;
+  int32_t* first = u_lds + tot;
+  for (int i = tid; i < tot; i += blockDim.x) vals[i] = s[i];
   __syncthreads();
-  // ---- union over the group, ascending page id
-  const int tot = G * kpg;
   for (int i = tid; i < tot; i += blockDim.x) {
-    const int v = sel_all[i];
+    const int v = vals[i];
     bool f = v >= 0;
-    for (int k = 0; k < i && f; ++k) f = sel_all[k] != v;
-    first_flag[i] = f;
+    for (int k = 0; k < i && f; ++k) f = vals[k] != v;
+    first[i] = f;
   }
   __syncthreads();
-  int32_t* urow = uni + (int64_t)h * tot;
   int nf = 0;
-  for (int k = 0; k < tot; ++k) nf += first_flag[k];
+  for (int k = 0; k < tot; ++k) nf += first[k];
   for (int i = tid; i < tot; i += blockDim.x) {
-    if (first_flag[i]) {
-      const int v = sel_all[i];
+    if (first[i]) {
+      const int v = vals[i];
       int pos = 0;
-      for (int k = 0; k < tot; ++k) pos += first_flag[k] && sel_all[k] < v;
-      urow[pos] = v;
+      for (int k = 0; k < tot; ++k) pos += first[k] && vals[k] < v;
+      u[pos] = v;
     }
-    if (i >= nf) urow[i] = -1;
+    if (i >= nf) u[i] = -1;
   }
   if (tid == 0) n_uni[h] = nf;
+}
+
+template <int D, class T>
+void launch_typed(const DevLayout& L, const void* blob, const void* Qv, int budget, int beam, int32_t* sel,
+                  int32_t* trace, hipStream_t s) {
+  const int kpg = budget / ICE_PAGE_CAP;
+  const int lcap = beam > kpg ? beam : kpg;
+  const bool big = lcap > 64;
+  const SelLds S = sel_lds(lcap, big);
+  const dim3 grid((unsigned)(((L.H + 7) / 8) * 8 * L.G)), block(64 * kWaves);
+  const T* Q = static_cast<const T*>(Qv);
+  if (big) k_select<D, T, true><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, trace);
+  else k_select<D, T, false><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, trace);
 }
 
 }  // namespace
 
 hipError_t launch_select(const DevLayout& L, const void* blob, const void* Q, int budget, int beam,
                          int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace, hipStream_t s) {
-  const int kpg = budget / ICE_PAGE_CAP;
-  const int W = kWaves / L.G;
-  const SelLds S = sel_lds(L.G, beam > kpg ? beam : kpg, kpg);
-  const dim3 grid((unsigned)L.H), block((unsigned)(64 * W * L.G));
-  const size_t lds = (size_t)S.total;
   if (L.dtype == ICE_BF16) {
-    const uint16_t* q = static_cast<const uint16_t*>(Q);
-    if (L.d == 128) k_select<128, uint16_t><<<grid, block, lds, s>>>(L, blob, q, budget, beam, W, sel, uni, n_uni, trace);
-    else k_select<64, uint16_t><<<grid, block, lds, s>>>(L, blob, q, budget, beam, W, sel, uni, n_uni, trace);
+    if (L.d == 128) launch_typed<128, uint16_t>(L, blob, Q, budget, beam, sel, trace, s);
+    else launch_typed<64, uint16_t>(L, blob, Q, budget, beam, sel, trace, s);
   } else {
-    const float* q = static_cast<const float*>(Q);
-    if (L.d == 128) k_select<128, float><<<grid, block, lds, s>>>(L, blob, q, budget, beam, W, sel, uni, n_uni, trace);
-    else k_select<64, float><<<grid, block, lds, s>>>(L, blob, q, budget, beam, W, sel, uni, n_uni, trace);
+    if (L.d == 128) launch_typed<128, float>(L, blob, Q, budget, beam, sel, trace, s);
+    else launch_typed<64, float>(L, blob, Q, budget, beam, sel, trace, s);
   }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int tot = L.G * (budget / ICE_PAGE_CAP);
+  const size_t lds = tot > 64 ? (size_t)tot * 8 : 0;
+  k_union<<<(unsigned)L.H, tot > 64 ? 256 : 64, lds, s>>>(sel, tot, uni, n_uni);
   return hipGetLastError();
-}
-
-size_t select_lds_bytes(int G, int budget, int beam) {
-  const int kpg = budget / ICE_PAGE_CAP;
-  return (size_t)sel_lds(G, beam > kpg ? beam : kpg, kpg).total;
 }
 
 }  // namespace ice

@@ -23,7 +23,8 @@
  * returns; results are ready when the stream reaches them. All argument and
  * capacity checks run on the host before anything is enqueued, so a call that
  * returns an error has changed nothing. Nothing throws across the ABI.
- * Calls on one index object must be issued from one host thread at a time.
+ * Calls on one index object must be issued from one host thread at a time
+ * and must not overlap on the device (enqueue them on one stream).
  */
 #ifndef ICE_H_
 #define ICE_H_
@@ -151,6 +152,8 @@ int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const in
 #define ICE_EXP_PAGE_K     10  /* dtype [pages][16][d] page-pool keys (level 0) / copies   */
 #define ICE_EXP_PAGE_V     11  /* dtype [pages][16][d] page-pool values (level 0 only)     */
 #define ICE_EXP_HEADER     12  /* ice_head_stats                                           */
+#define ICE_EXP_OWNER_RUN  13  /* int32 [capacity+1] pages of the owner's contiguous run   */
+#define ICE_EXP_OWNER_COUNT 14 /* int32 [capacity+1] members of the owner                  */
 
 typedef struct ice_head_stats {
   int32_t n_tokens;        /* tokens in the head                                  */
@@ -161,7 +164,9 @@ typedef struct ice_head_stats {
   int32_t splits;          /* KV pages split off by inserts (level-0 page table)   */
   int32_t near_ties;       /* parent choices whose two best lifted distances were
                               within 1e-4 relative, build and insert              */
-  int32_t pad;
+  int32_t overflow;        /* 1 if a page table was full (ruled out by the sizes) */
+  int32_t reserved0;
+  int32_t reserved1;
   double  M2;              /* largest squared key norm at build                   */
 } ice_head_stats;
 

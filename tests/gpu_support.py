@@ -64,7 +64,8 @@ def read_head(ix, h: int) -> GpuHead:
         tables.append(dict(
             tok=tok, cnt=cnt, pages=[[int(x) for x in tok[p, :cnt[p]]] for p in range(P)],
             next=ix.export(h, L.ICE_EXP_PAGE_NEXT, l)[:P], owner=ix.export(h, L.ICE_EXP_PAGE_OWNER, l)[:P],
-            first=ix.export(h, L.ICE_EXP_OWNER_FIRST, l), tail=ix.export(h, L.ICE_EXP_OWNER_TAIL, l)))
+            first=ix.export(h, L.ICE_EXP_OWNER_FIRST, l), tail=ix.export(h, L.ICE_EXP_OWNER_TAIL, l),
+            run=ix.export(h, L.ICE_EXP_OWNER_RUN, l), count=ix.export(h, L.ICE_EXP_OWNER_COUNT, l)))
     top = [int(x) for x in ix.export(h, L.ICE_EXP_TOP)[:st["n_top"]]] if st["n_top"] > 0 else []
     return GpuHead(n=n, L_top=Lt, n_top=st["n_top"], lev=lev, e=e, parent=parent, tables=tables, top=top,
                    stats=st)
@@ -89,6 +90,10 @@ def check_table_structure(g: GpuHead, cap: int):
             chain = owner_chain(tab, slot)
             assert chain, f"table {l}: owner {o} has no chain"
             assert int(tab["tail"][slot]) == chain[-1]
+            # the owner's member count, and its contiguous run of pages from first[]
+            assert int(tab["count"][slot]) == int(sum(tab["cnt"][p] for p in chain))
+            run = int(tab["run"][slot])
+            assert 1 <= run <= len(chain) and chain[:run] == list(range(chain[0], chain[0] + run))
             for i, p in enumerate(chain):
                 seen[p] += 1
                 assert int(tab["owner"][p]) == o
