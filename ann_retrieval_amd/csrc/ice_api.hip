@@ -286,7 +286,7 @@ int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const in
   if (uni_stride < 1 || uni_stride > ICE_MAX_GROUP * ICE_MAX_BEAM)
     return fail(ICE_ERR_ARG, "uni_stride must be in [1, %d]", ICE_MAX_GROUP * ICE_MAX_BEAM);
   const int64_t need = attend_ws_bytes(idx->L, uni_stride);
-  if (!ws || ws_bytes < (size_t)need)
+  if (need > 0 && (!ws || ws_bytes < (size_t)need))
     return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, attend needs %lld", ws_bytes, (long long)need);
   hipError_t e = launch_attend(idx->L, idx->blob, Q, uni, n_uni, uni_stride, scale, O, lse, ws,
                                static_cast<hipStream_t>(stream));

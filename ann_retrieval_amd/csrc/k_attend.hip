@@ -6,39 +6,137 @@
 // only. Every query head of a GQA group attends the group's page union (key
 // design 3).
 //
-// k_attend_part: one block per (split of the union, head). The block stages
-// 4 pages (64 rows of K and V) at a time in LDS with 16-byte coalesced loads
-// and keeps an online softmax per query head (one wave per query head). Logits
-// are kept in base-2 units (q pre-scaled by scale * log2 e) so the exponent is
-// one exp2. k_attend_combine merges the per-split (m, l, o) partials.
+// One block of 8 waves per head; wave w takes union pages w, w+8, ... and
+// keeps an online softmax (running max m, sum l, output o) for up to 4 query
+// heads at a time. Per page (16 rows) the wave reads K with 4 lanes per row
+// (a quarter row each, bf16 dot2 for q.k) and V with 16 lanes per row (each
+// lane 4 rows x D/16 dims), so both are plain coalesced 16-byte loads; the
+// next page's loads are issued before the current page is used. Logits are
+// kept in base 2 (scaled by scale * log2 e). The 8 wave partials of a head
+// are merged in LDS. Every row of a created page holds finite values (empty
+// slots are zero), so rows are loaded unconditionally and masked by the
+// page's count.
 #include "ice_launch.h"
 
 namespace ice {
 namespace {
 
-constexpr int kPagesPerSplit = 8;
-constexpr int kBatchPages = 4;
-constexpr int kRows = kBatchPages * ICE_PAGE_CAP;   // 64 rows per LDS batch
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kAttWaves = 8;
+constexpr int kQPerPass = 4;        // query heads per pass over the pages
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kMaxQPerWave = ICE_MAX_GROUP / 4;
 
 template <int D, class T>
-__global__ __launch_bounds__(256) void k_attend_part(DevLayout L, const void* blob, const T* Q,
-                                                     const int32_t* uni, const int32_t* n_uni, int uni_stride,
-                                                     float scale, float* part) {
-  constexpr int ROWB = D * (int)sizeof(T);
-  constexpr int LDSB = ROWB + 16;     // padded row stride: rows start on different banks
-  constexpr int DPL = D / 64;         // output dims per lane
-  __shared__ __attribute__((aligned(16))) char Kt[kRows * LDSB];
-  __shared__ __attribute__((aligned(16))) char Vt[kRows * LDSB];
-  __shared__ __attribute__((aligned(16))) float qs[ICE_MAX_GROUP * D];
-  __shared__ float ps[4][kRows];
-  __shared__ int32_t rowcnt[kBatchPages];
-  __shared__ int32_t rowpg[kBatchPages];
+struct AttGeo {
+  static constexpr int ROWB = D * (int)sizeof(T);
+  static constexpr int NLK = ROWB / 64;        // 16-byte K loads per lane (quarter row)
+  static constexpr int VB = ROWB / 16;         // V bytes per lane per row (16 lanes per row)
+  static constexpr int DV = D / 16;            // output dims per lane
+  static constexpr int EPK = 16 / (int)sizeof(T);
+};
 
-  const int h = blockIdx.y, split = blockIdx.x, nsplit = gridDim.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// V bytes -> floats
+template <class T, int DV>
+__device__ inline void unpack_v(const char* src, float* out) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(src);
+#pragma unroll
+    for (int i = 0; i < DV / 2; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float* f = reinterpret_cast<const float*>(src);
+#pragma unroll
+    for (int i = 0; i < DV; ++i) out[i] = f[i];
+  }
+}
+
+template <int D, class T>
+struct PageRegs {
+  using A = AttGeo<D, T>;
+  V4 k[A::NLK];
+  uint32_t v[4][A::VB / 4];
+  int cnt;
+};
+
+template <int D, class T>
+__device__ inline void load_page(const T* pgK, const T* pgV, int pg, int lane, PageRegs<D, T>& r) {
+  using A = AttGeo<D, T>;
+  const int64_t base = (int64_t)pg * ICE_PAGE_CAP;
+  const char* krow = reinterpret_cast<const char*>(pgK + (base + (lane >> 2)) * D) + (lane & 3) * (A::ROWB / 4);
+#pragma unroll
+  for (int i = 0; i < A::NLK; ++i) r.k[i] = *reinterpret_cast<const V4*>(krow + 16 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const char* vrow = reinterpret_cast<const char*>(pgV + (base + (lane >> 4) + 4 * i) * D) + (lane & 15) * A::VB;
+    if constexpr (A::VB >= 16) {
+#pragma unroll
+      for (int c = 0; c < A::VB / 16; ++c) {
+        const V4 x = *reinterpret_cast<const V4*>(vrow + 16 * c);
+        r.v[i][4 * c] = x.x;
+        r.v[i][4 * c + 1] = x.y;
+        r.v[i][4 * c + 2] = x.z;
+        r.v[i][4 * c + 3] = x.w;
+      }
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(vrow);
+      r.v[i][0] = x.x;
+      r.v[i][1] = x.y;
+    }
+  }
+}
+
+template <int D, class T>
+__device__ inline float qk_dot(const V4* q, const V4* k) {
+  using A = AttGeo<D, T>;
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < A::NLK; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k[i].x), __builtin_bit_cast(bf16x2, q[i].x), s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k[i].y), __builtin_bit_cast(bf16x2, q[i].y), s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k[i].z), __builtin_bit_cast(bf16x2, q[i].z), s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k[i].w), __builtin_bit_cast(bf16x2, q[i].w), s, false);
+    } else {
+      s = fmaf(__uint_as_float(k[i].x), __uint_as_float(q[i].x), s);
+      s = fmaf(__uint_as_float(k[i].y), __uint_as_float(q[i].y), s);
+      s = fmaf(__uint_as_float(k[i].z), __uint_as_float(q[i].z), s);
+      s = fmaf(__uint_as_float(k[i].w), __uint_as_float(q[i].w), s);
+    }
+  }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  return s;
+}
+
+// sum / max over the 16 rows of a page (lanes 4r + part)
+__device__ inline float rows_sum(float s) {
+  s += __shfl_xor(s, 4, 64);
+  s += __shfl_xor(s, 8, 64);
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  return s;
+}
+__device__ inline float rows_max(float s) {
+  s = fmaxf(s, __shfl_xor(s, 4, 64));
+  s = fmaxf(s, __shfl_xor(s, 8, 64));
+  s = fmaxf(s, __shfl_xor(s, 16, 64));
+  s = fmaxf(s, __shfl_xor(s, 32, 64));
+  return s;
+}
+
+template <int D, class T>
+__global__ __launch_bounds__(kAttWaves * 64) void k_attend(DevLayout L, const void* blob, const T* Q,
+                                                           const int32_t* uni, const int32_t* n_uni,
+                                                           int uni_stride, float scale, float* O, float* lse) {
+  using A = AttGeo<D, T>;
+  __shared__ float part_m[kAttWaves][kQPerPass], part_l[kAttWaves][kQPerPass];
+  __shared__ float part_o[kAttWaves][kQPerPass][D];
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int G = L.G;
   const void* hb = head_base(blob, L, h);
   const T* pgK = at<T>(hb, L.off_pgK[0]);
@@ -46,158 +144,134 @@ __global__ __launch_bounds__(256) void k_attend_part(DevLayout L, const void* bl
   const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
   const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
   const int nu = min(n_uni[h], uni_stride);
-  const int pbeg = split * kPagesPerSplit;
-  const int pend = min(nu, pbeg + kPagesPerSplit);
+  const int32_t* u = uni + (int64_t)h * uni_stride;
+  const float c2 = scale * kLog2e;
+  const int krow = lane >> 2;
 
-  for (int i = threadIdx.x; i < G * D; i += 256)
-    qs[i] = Elt<T>::load(Q, (int64_t)h * G * D + i) * (scale * kLog2e);
-
-  float m[kMaxQPerWave], l[kMaxQPerWave], o[kMaxQPerWave][DPL];
+  for (int g0 = 0; g0 < G; g0 += kQPerPass) {
+    const int ng = min(kQPerPass, G - g0);
+    V4 q[kQPerPass][A::NLK];
 #pragma unroll
-  for (int j = 0; j < kMaxQPerWave; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.0f;
+    for (int g = 0; g < kQPerPass; ++g) {
+      const char* qrow = reinterpret_cast<const char*>(Q + ((int64_t)h * G + g0 + (g < ng ? g : 0)) * D) +
+                         (lane & 3) * (A::ROWB / 4);
 #pragma unroll
-    for (int c = 0; c < DPL; ++c) o[j][c] = 0.0f;
-  }
-
-  for (int pb = pbeg; pb < pend; pb += kBatchPages) {
-    const int npg = min(kBatchPages, pend - pb);
-    __syncthreads();
-    if (threadIdx.x < kBatchPages) {
-      int pg = threadIdx.x < npg ? uni[(int64_t)h * uni_stride + pb + threadIdx.x] : -1;
-      if (pg >= n_pages) pg = -1;   // ids outside the page table are ignored
-      rowpg[threadIdx.x] = pg;
-      rowcnt[threadIdx.x] = pg >= 0 ? pg_cnt[pg] : 0;
+      for (int i = 0; i < A::NLK; ++i) q[g][i] = *reinterpret_cast<const V4*>(qrow + 16 * i);
     }
-    __syncthreads();
-    constexpr int CPR = ROWB / 16;    // 16-byte chunks per row
-    for (int c = threadIdx.x; c < kRows * CPR; c += 256) {
-      const int r = c / CPR, q = c % CPR;
-      const int pg = rowpg[r / ICE_PAGE_CAP];
-      V4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-      if (pg >= 0 && (r % ICE_PAGE_CAP) < rowcnt[r / ICE_PAGE_CAP]) {
-        const int64_t row = (int64_t)pg * ICE_PAGE_CAP + (r % ICE_PAGE_CAP);
-        kx = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(pgK + row * D) + q * 16);
-        vx = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(pgV + row * D) + q * 16);
+    float m[kQPerPass], l[kQPerPass], o[kQPerPass][A::DV];
+#pragma unroll
+    for (int g = 0; g < kQPerPass; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < A::DV; ++c) o[g][c] = 0.0f;
+    }
+    // pages wv, wv+8, ...: their ids and valid counts are fetched up front, one
+    // per lane (ids outside the page table are skipped)
+    const int npw = nu > wv ? (nu - wv + kAttWaves - 1) / kAttWaves : 0;
+    for (int k0 = 0; k0 < npw; k0 += 64) {
+      int my_pg = -1, my_cnt = 0;
+      if (k0 + lane < npw) {
+        my_pg = u[wv + kAttWaves * (k0 + lane)];
+        if (my_pg < 0 || my_pg >= n_pages) my_pg = -1;
+        else my_cnt = pg_cnt[my_pg];
       }
-      *reinterpret_cast<V4*>(Kt + r * LDSB + q * 16) = kx;
-      *reinterpret_cast<V4*>(Vt + r * LDSB + q * 16) = vx;
-    }
-    __syncthreads();
-    const bool valid = rowpg[lane / ICE_PAGE_CAP] >= 0 && (lane % ICE_PAGE_CAP) < rowcnt[lane / ICE_PAGE_CAP];
+      const int nk = min(64, npw - k0);
+      // loads are unconditional (a skipped id reads page 0 and is masked) so
+      // the next page's loads stay in flight while the current one is used
+      int pg = __shfl(my_pg, 0, 64);
+      PageRegs<D, T> cur, nxt;
+      load_page<D, T>(pgK, pgV, pg >= 0 ? pg : 0, lane, cur);
+      for (int k = 0; k < nk; ++k) {
+        const int pgn = k + 1 < nk ? __shfl(my_pg, k + 1, 64) : -1;
+        load_page<D, T>(pgK, pgV, pgn >= 0 ? pgn : 0, lane, nxt);
+        const int cnt = __shfl(my_cnt, k, 64);
+        if (pg >= 0) {
+          const bool valid = krow < cnt;
+          float p[kQPerPass];
 #pragma unroll
-    for (int j = 0; j < kMaxQPerWave; ++j) {
-      const int g = wave + 4 * j;
-      if (g >= G) break;
-      // logit of row `lane` for query g
-      float s = -INFINITY;
-      if (valid) {
-        float acc = 0.0f;
-        const float* qg = qs + g * D;
-#pragma unroll 4
-        for (int c = 0; c < ROWB / 16; ++c) {
-          const V4 kv = *reinterpret_cast<const V4*>(Kt + lane * LDSB + c * 16);
-          float f[Elt<T>::per16];
-          Elt<T>::unpack(kv, f);
+          for (int g = 0; g < kQPerPass; ++g) {
+            const float s = valid ? qk_dot<D, T>(q[g], cur.k) * c2 : -INFINITY;
+            const float mn = fmaxf(m[g], rows_max(s));
+            const float corr = exp2f(m[g] - mn);
+            p[g] = valid ? exp2f(s - mn) : 0.0f;
+            l[g] = l[g] * corr + rows_sum(p[g]);
+            m[g] = mn;
 #pragma unroll
-          for (int i = 0; i < Elt<T>::per16; ++i) acc = fmaf(qg[c * Elt<T>::per16 + i], f[i], acc);
+            for (int c = 0; c < A::DV; ++c) o[g][c] *= corr;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v[A::DV];
+            unpack_v<T, A::DV>(reinterpret_cast<const char*>(cur.v[r]), v);
+            const int src = 4 * ((lane >> 4) + 4 * r);   // a lane holding row (lane/16 + 4r)'s weight
+#pragma unroll
+            for (int g = 0; g < kQPerPass; ++g) {
+              const float pr = __shfl(p[g], src, 64);
+#pragma unroll
+              for (int c = 0; c < A::DV; ++c) o[g][c] = fmaf(pr, v[c], o[g][c]);
+            }
+          }
         }
-        s = acc;
+        cur = nxt;
+        pg = pgn;
       }
-      const float mt = wave_max(s);
-      if (mt == -INFINITY) continue;
-      const float mn = fmaxf(m[j], mt);
-      const float corr = exp2f(m[j] - mn);
-      const float p = valid ? exp2f(s - mn) : 0.0f;
-      l[j] = l[j] * corr + wave_sum(p);
-      m[j] = mn;
+    }
+    // the four row groups of the wave hold partial outputs of the same dims
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) o[j][c] *= corr;
-      ps[wave][lane] = p;
-      wave_sync();
-      for (int r = 0; r < kRows; ++r) {
-        const float pr = ps[wave][r];
+    for (int g = 0; g < kQPerPass; ++g) {
 #pragma unroll
-        for (int c = 0; c < DPL; ++c) {
-          const int dim = lane * DPL + c;
-          const float vv = sizeof(T) == 4 ? *reinterpret_cast<const float*>(Vt + r * LDSB + dim * 4)
-                                          : bf16_to_f32(*reinterpret_cast<const uint16_t*>(Vt + r * LDSB + dim * 2));
-          o[j][c] = fmaf(pr, vv, o[j][c]);
+      for (int c = 0; c < A::DV; ++c) {
+        o[g][c] += __shfl_xor(o[g][c], 16, 64);
+        o[g][c] += __shfl_xor(o[g][c], 32, 64);
+      }
+      if (lane == 0) {
+        part_m[wv][g] = m[g];
+        part_l[wv][g] = l[g];
+      }
+      if (lane < 16)
+#pragma unroll
+        for (int c = 0; c < A::DV; ++c) part_o[wv][g][lane * A::DV + c] = o[g][c];
+    }
+    __syncthreads();
+    // merge the wave partials: thread -> (query, dim)
+    for (int t = threadIdx.x; t < ng * D; t += blockDim.x) {
+      const int g = t / D, dd = t % D;
+      float M = -INFINITY;
+      for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, part_m[w][g]);
+      float Ls = 0.0f, acc = 0.0f;
+      if (M > -INFINITY) {
+        for (int w = 0; w < kAttWaves; ++w) {
+          if (part_m[w][g] == -INFINITY) continue;
+          const float wt = exp2f(part_m[w][g] - M);
+          Ls = fmaf(part_l[w][g], wt, Ls);
+          acc = fmaf(part_o[w][g][dd], wt, acc);
         }
       }
-      wave_sync();
+      O[((int64_t)h * G + g0 + g) * D + dd] = Ls > 0.0f ? acc / Ls : 0.0f;
+      if (lse && dd == 0) lse[(int64_t)h * G + g0 + g] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
     }
+    __syncthreads();
   }
-  // partials [h][split][g] = (m, l, o[D])
-#pragma unroll
-  for (int j = 0; j < kMaxQPerWave; ++j) {
-    const int g = wave + 4 * j;
-    if (g >= G) break;
-    float* dst = part + (((int64_t)h * nsplit + split) * G + g) * (D + 2);
-    if (lane == 0) {
-      dst[0] = m[j];
-      dst[1] = l[j];
-    }
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) dst[2 + lane * DPL + c] = o[j][c];
-  }
-}
-
-template <int D>
-__global__ void k_attend_combine(int G, int nsplit, const float* part, float* O, float* lse) {
-  constexpr int DPL = D / 64;
-  const int h = blockIdx.x;
-  const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (g >= G) return;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[(((int64_t)h * nsplit + s) * G + g) * (D + 2)]);
-  float Ls = 0.0f, o[DPL];
-#pragma unroll
-  for (int c = 0; c < DPL; ++c) o[c] = 0.0f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float* p = part + (((int64_t)h * nsplit + s) * G + g) * (D + 2);
-      if (p[0] == -INFINITY) continue;
-      const float w = exp2f(p[0] - M);
-      Ls = fmaf(p[1], w, Ls);
-#pragma unroll
-      for (int c = 0; c < DPL; ++c) o[c] = fmaf(p[2 + lane * DPL + c], w, o[c]);
-    }
-  }
-  float* out = O + ((int64_t)h * G + g) * D;
-  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-#pragma unroll
-  for (int c = 0; c < DPL; ++c) out[lane * DPL + c] = o[c] * inv;
-  if (lse && lane == 0) lse[(int64_t)h * G + g] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
 
-int attend_splits(int uni_stride) {
-  const int n = (uni_stride + kPagesPerSplit - 1) / kPagesPerSplit;
-  return n < 1 ? 1 : n;
-}
+int attend_splits(int) { return 0; }
 
 hipError_t launch_attend(const DevLayout& L, const void* blob, const void* Q, const int32_t* uni,
-                         const int32_t* n_uni, int uni_stride, float scale, float* O, float* lse, void* ws,
+                         const int32_t* n_uni, int uni_stride, float scale, float* O, float* lse, void*,
                          hipStream_t s) {
-  const int nsplit = attend_splits(uni_stride);
-  float* part = static_cast<float*>(ws);
-  const dim3 grid((unsigned)nsplit, (unsigned)L.H);
+  const dim3 grid((unsigned)L.H), block(kAttWaves * 64);
   if (L.dtype == ICE_BF16) {
     const uint16_t* q = static_cast<const uint16_t*>(Q);
-    if (L.d == 128) k_attend_part<128, uint16_t><<<grid, 256, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, part);
-    else k_attend_part<64, uint16_t><<<grid, 256, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, part);
+    if (L.d == 128) k_attend<128, uint16_t><<<grid, block, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, O, lse);
+    else k_attend<64, uint16_t><<<grid, block, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, O, lse);
   } else {
     const float* q = static_cast<const float*>(Q);
-    if (L.d == 128) k_attend_part<128, float><<<grid, 256, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, part);
-    else k_attend_part<64, float><<<grid, 256, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, part);
+    if (L.d == 128) k_attend<128, float><<<grid, block, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, O, lse);
+    else k_attend<64, float><<<grid, block, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, O, lse);
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (L.d == 128) k_attend_combine<128><<<(unsigned)L.H, 64 * L.G, 0, s>>>(L.G, nsplit, part, O, lse);
-  else k_attend_combine<64><<<(unsigned)L.H, 64 * L.G, 0, s>>>(L.G, nsplit, part, O, lse);
   return hipGetLastError();
 }
 

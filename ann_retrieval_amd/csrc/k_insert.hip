@@ -228,6 +228,17 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
       e_sh = et;
     }
     __syncthreads();
+    // a page created by this insert gets zero rows besides the new token, so
+    // every row of every page holds finite values
+    for (int l = 0; l < Ltop || l == 0; ++l) {
+      if (plc.page[l] < 0 || plc.slot[l] != 0) continue;
+      const int64_t base = (int64_t)plc.page[l] * ICE_PAGE_CAP;
+      for (int i = tid + D; i < ICE_PAGE_CAP * D; i += 256) {
+        at<T>(hb, L.off_pgK[l])[base * D + i] = T(0);
+        if (l == 0) at<T>(hb, L.off_pgV)[base * D + i] = T(0);
+        else if (i % D == 0) at<float>(hb, L.off_pgE[l])[base + i / D] = 0.0f;
+      }
+    }
     // rows into the pools
     for (int i = tid; i < D; i += 256) {
       const T kv = krow[i];

@@ -409,8 +409,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         for (int b = 0; b < 4; ++b) {
           const int r = (m0 + b * W) * 16 + row;
           ok[b] = r < n_top;
-          rp[b] = top_K + (int64_t)(ok[b] ? r : 0) * D;
-          tk[b] = ok[b] ? top_tok[r] : 0;
+          const int rc = ok[b] ? r : 0;          // loads are unconditional so they batch
+          rp[b] = top_K + (int64_t)rc * D;
+          tk[b] = top_tok[rc];
         }
         tl.push(A, chunk_keys<D, T>(qs, ok, rp, tk, lane), lane);
       }
@@ -437,9 +438,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
           for (int b = 0; b < 4; ++b) {
             const int blk = b0 + b < nb ? A.cand[b0 + b] : -1;
             ok[b] = blk >= 0 && row < A.cval[b0 + b];
-            const int64_t r = (int64_t)(ok[b] ? blk : 0) * ICE_PAGE_CAP + row;
+            const int64_t r = (int64_t)(blk >= 0 ? blk : 0) * ICE_PAGE_CAP + row;   // in the page: 16 slots exist
             rp[b] = pgK + r * D;
-            tk[b] = ok[b] ? pg_tok[r] : 0;
+            tk[b] = pg_tok[r];
           }
           tl.push(A, chunk_keys<D, T>(qs, ok, rp, tk, lane), lane);
         }
