@@ -199,6 +199,43 @@ __device__ inline void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// ---- cross-lane exchange on the VALU (no LDS round trip) -----------------
+// xor_lane<m>(x) returns x from lane ^ m. m = 1, 2: DPP quad permutes; m = 4:
+// DPP row rotations (a row is 16 lanes; row_ror:n reads lane i-n of the row);
+// m = 8: row_ror:8; m = 16, 32: the gfx950 permlane16 / permlane32 swaps.
+// All lanes of the wave must be active.
+template <int m>
+__device__ inline int xor_lane(int x) {
+  const int lane = __lane_id();
+  if constexpr (m == 1) {
+    return __builtin_amdgcn_update_dpp(0, x, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (m == 2) {
+    return __builtin_amdgcn_update_dpp(0, x, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (m == 4) {
+    const int down = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false);   // lane i-4
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x12c, 0xf, 0xf, false);     // lane i+4
+    return (lane & 4) ? down : up;
+  } else if constexpr (m == 8) {
+    return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);   // row_ror:8
+  } else if constexpr (m == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? (int)p[0] : (int)p[1];
+  } else {
+    static_assert(m == 32, "xor distance");
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? (int)p[0] : (int)p[1];
+  }
+}
+template <int m>
+__device__ inline float xor_lane_f(float x) {
+  return __int_as_float(xor_lane<m>(__float_as_int(x)));
+}
+template <int m>
+__device__ inline uint64_t xor_lane_u64(uint64_t x) {
+  const int lo = xor_lane<m>((int)(uint32_t)x), hi = xor_lane<m>((int)(uint32_t)(x >> 32));
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int m = 1; m < ICE_WAVE; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, ICE_WAVE));

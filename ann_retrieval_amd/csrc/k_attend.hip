@@ -107,24 +107,24 @@ __device__ inline float qk_dot(const V4* q, const V4* k) {
       s = fmaf(__uint_as_float(k[i].w), __uint_as_float(q[i].w), s);
     }
   }
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
+  s += xor_lane_f<1>(s);
+  s += xor_lane_f<2>(s);
   return s;
 }
 
 // sum / max over the 16 rows of a page (lanes 4r + part)
 __device__ inline float rows_sum(float s) {
-  s += __shfl_xor(s, 4, 64);
-  s += __shfl_xor(s, 8, 64);
-  s += __shfl_xor(s, 16, 64);
-  s += __shfl_xor(s, 32, 64);
+  s += xor_lane_f<4>(s);
+  s += xor_lane_f<8>(s);
+  s += xor_lane_f<16>(s);
+  s += xor_lane_f<32>(s);
   return s;
 }
 __device__ inline float rows_max(float s) {
-  s = fmaxf(s, __shfl_xor(s, 4, 64));
-  s = fmaxf(s, __shfl_xor(s, 8, 64));
-  s = fmaxf(s, __shfl_xor(s, 16, 64));
-  s = fmaxf(s, __shfl_xor(s, 32, 64));
+  s = fmaxf(s, xor_lane_f<4>(s));
+  s = fmaxf(s, xor_lane_f<8>(s));
+  s = fmaxf(s, xor_lane_f<16>(s));
+  s = fmaxf(s, xor_lane_f<32>(s));
   return s;
 }
 
@@ -222,8 +222,8 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend(DevLayout L, const vo
     for (int g = 0; g < kQPerPass; ++g) {
 #pragma unroll
       for (int c = 0; c < A::DV; ++c) {
-        o[g][c] += __shfl_xor(o[g][c], 16, 64);
-        o[g][c] += __shfl_xor(o[g][c], 32, 64);
+        o[g][c] += xor_lane_f<16>(o[g][c]);
+        o[g][c] += xor_lane_f<32>(o[g][c]);
       }
       if (lane == 0) {
         part_m[wv][g] = m[g];

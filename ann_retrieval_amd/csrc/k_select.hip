@@ -9,19 +9,19 @@
 // lifted as [q, 0], the lifted distance |q|^2 + M^2 - 2 q.k ranks exactly like
 // q.k descending, which is what is scored. A page scores its best token.
 //
-// k_select: one block of 4 waves per (head, query head); the blocks of a head
-// are mapped to one XCD (workgroups go round-robin over the 8 XCDs) so they
-// share its L2. At every level the candidate rows are split over the waves: a
-// wave scores 16 rows per pass with 4 lanes per row (bf16 dot2 on gfx950),
-// issuing the loads of several 16-row groups before any arithmetic. Keys pack
-// (score, ~id) into 64 bits, so "score descending, id ascending" is plain
-// unsigned order. Each wave keeps its top list in registers, one key per lane:
-// a chunk of 64 candidates is bitonic-sorted across the wave and merged by
-// taking max(list[i], chunk[63-i]) (the 64 largest of both, as a bitonic
-// sequence) followed by a 6-step bitonic merge; the lists of the 4 waves are
-// merged the same way. Lists longer than 64 keys (beams or budgets beyond 64
-// entries) use a slower LDS list instead.
-// k_union: the union of a head's selected pages, ascending page id.
+// One block per head; each of its G query heads gets W waves (W = 4 for
+// G <= 4, else 16/G). At every level a query's candidate rows are split over
+// its waves: a wave scores 16 rows per pass with 4 lanes per row (bf16 dot2 on
+// gfx950), issuing the loads of several 16-row groups before any arithmetic.
+// Keys pack (score, ~id) into 64 bits, so "score descending, id ascending" is
+// plain unsigned order. Each wave keeps its top list in registers, one key per
+// lane: a chunk of 64 candidates is bitonic-sorted across the wave and merged
+// by taking max(list[i], chunk[63-i]) (the 64 largest of both, as a bitonic
+// sequence) followed by a 6-step bitonic merge; the W lists of a query merge
+// the same way. All lane exchanges of these networks are DPP / permlane moves
+// on the VALU. Lists longer than 64 keys (beams or budgets beyond 64 entries)
+// use a slower LDS list instead. The block ends with the union of its query
+// heads' pages, ascending.
 #include "ice_launch.h"
 
 #include <type_traits>
@@ -31,8 +31,16 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;           // waves per (head, query head) block
+constexpr int kMaxWaves = 16;
 constexpr int kChainBatch = 64;     // pages gathered per round
+
+__host__ __device__ inline int waves_per_query(int G) { return G <= 4 ? 4 : 16 / G; }
+// LDS slots of the union's sort: the next power of two
+__host__ __device__ inline int union_pad(int n) {
+  int p = 64;
+  while (p < n) p <<= 1;
+  return p;
+}
 
 // ---- scoring geometry: 4 lanes per row, 16 rows per wave pass -------------
 template <int D, class T>
@@ -58,7 +66,7 @@ struct Quarter {
       if (ok) out[i] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(row) + part * PB + i * 16);
     }
   }
-  // partial dot of this lane's quarter; quad_sum completes it
+  // q.row from this lane's quarter, summed over the row's 4 lanes
   __device__ inline float dot(const V4* k) const {
     float s = 0.0f;
 #pragma unroll
@@ -75,21 +83,18 @@ struct Quarter {
         s = fmaf(__uint_as_float(k[i].w), __uint_as_float(q[i].w), s);
       }
     }
+    s += xor_lane_f<1>(s);
+    s += xor_lane_f<2>(s);
     return s;
   }
 };
 
-__device__ inline float quad_sum(float s) {
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  return s;
-}
 // max over the 16 rows of a pass (lanes 4r + part)
 __device__ inline float rows_max(float s) {
-  s = fmaxf(s, __shfl_xor(s, 4, 64));
-  s = fmaxf(s, __shfl_xor(s, 8, 64));
-  s = fmaxf(s, __shfl_xor(s, 16, 64));
-  s = fmaxf(s, __shfl_xor(s, 32, 64));
+  s = fmaxf(s, xor_lane_f<4>(s));
+  s = fmaxf(s, xor_lane_f<8>(s));
+  s = fmaxf(s, xor_lane_f<16>(s));
+  s = fmaxf(s, xor_lane_f<32>(s));
   return s;
 }
 
@@ -97,33 +102,60 @@ __device__ inline uint64_t shfl64(uint64_t v, int src) {
   const int lo = __shfl((int)(uint32_t)v, src, 64), hi = __shfl((int)(uint32_t)(v >> 32), src, 64);
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
-__device__ inline uint64_t shfl_xor64(uint64_t v, int m) {
-  const int lo = __shfl_xor((int)(uint32_t)v, m, 64), hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
 __device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
+template <int k, int j>
+__device__ inline uint64_t bitonic_step(uint64_t x, int lane) {
+  const uint64_t y = xor_lane_u64<j>(x);
+  return (((lane & k) == 0) == ((lane & j) == 0)) ? umax64(x, y) : umin64(x, y);
+}
 // Sorts one key per lane across the wave, descending (lane 0 largest).
 __device__ inline uint64_t wave_sort_desc(uint64_t x, int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t y = shfl_xor64(x, j);
-      x = (((lane & k) == 0) == ((lane & j) == 0)) ? umax64(x, y) : umin64(x, y);
-    }
-  }
+  x = bitonic_step<2, 1>(x, lane);
+  x = bitonic_step<4, 2>(x, lane);
+  x = bitonic_step<4, 1>(x, lane);
+  x = bitonic_step<8, 4>(x, lane);
+  x = bitonic_step<8, 2>(x, lane);
+  x = bitonic_step<8, 1>(x, lane);
+  x = bitonic_step<16, 8>(x, lane);
+  x = bitonic_step<16, 4>(x, lane);
+  x = bitonic_step<16, 2>(x, lane);
+  x = bitonic_step<16, 1>(x, lane);
+  x = bitonic_step<32, 16>(x, lane);
+  x = bitonic_step<32, 8>(x, lane);
+  x = bitonic_step<32, 4>(x, lane);
+  x = bitonic_step<32, 2>(x, lane);
+  x = bitonic_step<32, 1>(x, lane);
+  x = bitonic_step<64, 32>(x, lane);
+  x = bitonic_step<64, 16>(x, lane);
+  x = bitonic_step<64, 8>(x, lane);
+  x = bitonic_step<64, 4>(x, lane);
+  x = bitonic_step<64, 2>(x, lane);
+  x = bitonic_step<64, 1>(x, lane);
   return x;
+}
+template <int j>
+__device__ inline uint64_t merge_step(uint64_t t, int lane) {
+  const uint64_t y = xor_lane_u64<j>(t);
+  return (lane & j) == 0 ? umax64(t, y) : umin64(t, y);
 }
 // Top 64 of two descending wave lists, descending.
 __device__ inline uint64_t wave_merge_desc(uint64_t a, uint64_t b_sorted, int lane) {
-  uint64_t t = umax64(a, shfl64(b_sorted, 63 - lane));
-#pragma unroll
-  for (int j = 32; j > 0; j >>= 1) {
-    const uint64_t y = shfl_xor64(t, j);
-    t = (lane & j) == 0 ? umax64(t, y) : umin64(t, y);
-  }
+  // b reversed: lane ^ 63 == 63 - lane
+  uint64_t r = xor_lane_u64<1>(b_sorted);
+  r = xor_lane_u64<2>(r);
+  r = xor_lane_u64<4>(r);
+  r = xor_lane_u64<8>(r);
+  r = xor_lane_u64<16>(r);
+  r = xor_lane_u64<32>(r);
+  uint64_t t = umax64(a, r);
+  t = merge_step<32>(t, lane);
+  t = merge_step<16>(t, lane);
+  t = merge_step<8>(t, lane);
+  t = merge_step<4>(t, lane);
+  t = merge_step<2>(t, lane);
+  t = merge_step<1>(t, lane);
   return t;
 }
 
@@ -131,22 +163,24 @@ __device__ inline uint64_t wave_merge_desc(uint64_t a, uint64_t b_sorted, int la
 struct SelLds {
   int lcap;           // list capacity = max(beam, pages per query)
   int wave_bytes;     // per wave: [LDS lists: list[2][lcap] u64] chunk[64] u64, cand/cval[64] i32, 4 ints
-  int off_comb;       // register lists: [2 parities][kWaves][64] u64
-  int off_query;      // LDS lists: query list[lcap] u64
+  int off_comb;       // register lists: [2 parities][kMaxWaves][64] u64
+  int off_query;      // LDS lists: [G][lcap] u64 query lists
   int off_wn;         // LDS lists: per wave count and buffer (2 ints)
-  int off_misc;       // 4 ints
+  int off_qn;         // LDS lists: per query count
+  int off_sel;        // [G][kpg] i32 selections (for the union)
   int total;
 };
 
-__host__ __device__ inline SelLds sel_lds(int lcap, bool big) {
+__host__ __device__ inline SelLds sel_lds(int G, int lcap, int kpg, bool big) {
   SelLds s;
   s.lcap = lcap;
   s.wave_bytes = (big ? 2 * lcap * 8 : 0) + 64 * 8 + 2 * kChainBatch * 4 + 16;
-  s.off_comb = kWaves * s.wave_bytes;
-  s.off_query = s.off_comb + (big ? 0 : 2 * kWaves * 64 * 8);
-  s.off_wn = s.off_query + (big ? lcap * 8 : 0);
-  s.off_misc = s.off_wn + kWaves * 8;
-  s.total = s.off_misc + 16;
+  s.off_comb = kMaxWaves * s.wave_bytes;
+  s.off_query = s.off_comb + (big ? 0 : 2 * kMaxWaves * 64 * 8);
+  s.off_wn = s.off_query + (big ? G * lcap * 8 : 0);
+  s.off_qn = s.off_wn + kMaxWaves * 8;
+  s.off_sel = s.off_qn + ICE_MAX_GROUP * 4;
+  s.total = s.off_sel + union_pad(G * kpg) * 4;
   return s;
 }
 
@@ -292,7 +326,7 @@ __device__ inline uint64_t chunk_keys(const Quarter<D, T>& qs, const bool (&ok)[
     for (int b = 0; b < QG::GB; ++b) qs.fetch(ok[g0 + b], row[g0 + b], buf[b]);
 #pragma unroll
     for (int b = 0; b < QG::GB; ++b) {
-      const float s = quad_sum(qs.dot(buf[b]));
+      const float s = qs.dot(buf[b]);
       key[g0 + b] = ok[g0 + b] ? make_key(s, tok[g0 + b]) : 0ull;
     }
   }
@@ -303,25 +337,23 @@ __device__ inline uint64_t chunk_keys(const Quarter<D, T>& qs, const bool (&ok)[
 }
 
 template <int D, class T, bool BIG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_select(
-    DevLayout L, const void* blob, const T* Q, int budget, int beam, int32_t* sel, int32_t* trace) {
+__global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, const T* Q, int budget, int beam,
+                                                 int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace) {
   using QG = Quarter<D, T>;
   using Top = std::conditional_t<BIG, LdsTop, RegTop>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int G = L.G;
-  // block -> (head, query head): the G blocks of a head share an XCD
-  const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
-  const int h = (rest / G) * 8 + xcd, g = rest % G;
-  if (h >= L.H) return;
+  const int G = L.G, W = waves_per_query(G);
+  const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int W = kWaves, j = wv;
+  const int g = wv / W, j = wv % W;      // query head, wave within the query
   const int kpg = budget / ICE_PAGE_CAP;
-  const SelLds S = sel_lds(max(beam, kpg), BIG);
+  const SelLds S = sel_lds(G, max(beam, kpg), kpg, BIG);
   const WaveArea A = wave_area(smem, S, wv, BIG);
   uint64_t* comb = reinterpret_cast<uint64_t*>(smem + S.off_comb);
-  uint64_t* qlist = reinterpret_cast<uint64_t*>(smem + S.off_query);
+  uint64_t* qlist = reinterpret_cast<uint64_t*>(smem + S.off_query) + g * S.lcap;
   int32_t* wn = reinterpret_cast<int32_t*>(smem + S.off_wn);
-  int32_t* misc = reinterpret_cast<int32_t*>(smem + S.off_misc);
+  int32_t* qn = reinterpret_cast<int32_t*>(smem + S.off_qn);
+  int32_t* sel_all = reinterpret_cast<int32_t*>(smem + S.off_sel);
 
   const void* hb = head_base(blob, L, h);
   const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
@@ -341,12 +373,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   int qcount = 0, parity = 0;
   auto combine = [&](Top& t, int cap) {
     if constexpr (!BIG) {
-      uint64_t* area = comb + parity * kWaves * 64;
+      uint64_t* area = comb + parity * kMaxWaves * 64;
       area[wv * 64 + lane] = t.L;
       __syncthreads();
       uint64_t r = t.L;
       for (int jj = 0; jj < W; ++jj)
-        if (jj != j) r = wave_merge_desc(r, area[jj * 64 + lane], lane);
+        if (jj != j) r = wave_merge_desc(r, area[(g * W + jj) * 64 + lane], lane);
       ql = lane < cap ? r : 0ull;
       qcount = __popcll(__ballot(ql != 0ull));
       parity ^= 1;
@@ -358,20 +390,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       __syncthreads();
       const uint64_t* mine = A.lists + t.cur * A.lcap;
       int tot = 0;
-      for (int jj = 0; jj < W; ++jj) tot += wn[2 * jj];
+      for (int jj = 0; jj < W; ++jj) tot += wn[2 * (g * W + jj)];
       for (int i = lane; i < t.n; i += 64) {
         const uint64_t x = mine[i];
         int rank = i;
         for (int jj = 0; jj < W; ++jj) {
           if (jj == j) continue;
-          const uint64_t* other = reinterpret_cast<const uint64_t*>(smem + jj * S.wave_bytes) + wn[2 * jj + 1] * S.lcap;
-          rank += count_greater(other, wn[2 * jj], x);
+          const int ow = g * W + jj;
+          const uint64_t* other = reinterpret_cast<const uint64_t*>(smem + ow * S.wave_bytes) + wn[2 * ow + 1] * S.lcap;
+          rank += count_greater(other, wn[2 * ow], x);
         }
         if (rank < cap) qlist[rank] = x;
       }
-      if (j == 0 && lane == 0) misc[0] = min(cap, tot);
+      if (j == 0 && lane == 0) qn[g] = min(cap, tot);
       __syncthreads();
-      qcount = misc[0];
+      qcount = qn[g];
     }
   };
   // owner (token id) of kept entry oi, -1 past the list; every lane calls it
@@ -503,7 +536,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
           for (int b = 0; b < QG::GB; ++b) {
             if (pg[b] < 0) continue;
-            float s = quad_sum(qs.dot(buf[b]));
+            float s = qs.dot(buf[b]);
             if (row >= cv[b]) s = -INFINITY;
             s = rows_max(s);
             if (lane == fill) pk = make_key(s, pg[b]);
@@ -520,20 +553,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     combine(tl, kpg);
   }
   // ---- outputs of this query head
-  if (j == 0) emit(sel + ((int64_t)h * G + g) * kpg, kpg);
-}
-
-// Union of the G selection rows of a head, ascending, -1 padded. Rows of up to
-// 64 entries in total are sorted in one wave; longer ones by rank in LDS.
-__global__ __launch_bounds__(256) void k_union(const int32_t* sel, int tot, int32_t* uni, int32_t* n_uni) {
-  extern __shared__ int32_t u_lds[];
-  const int h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int32_t* s = sel + (int64_t)h * tot;
-  int32_t* u = uni + (int64_t)h * tot;
+  if (j == 0) {
+    emit(sel + ((int64_t)h * G + g) * kpg, kpg);
+    emit(sel_all + g * kpg, kpg);
+  }
+  __syncthreads();
+  // ---- union over the group, ascending page id, -1 padded
+  const int tot = G * kpg;
+  int32_t* urow = uni + (int64_t)h * tot;
   if (tot <= 64) {
-    if (tid >= 64) return;
-    int v = lane < tot ? s[lane] : INT_MAX;
+    if (wv != 0) return;
+    int v = lane < tot ? sel_all[lane] : INT_MAX;
     if (v < 0) v = INT_MAX;
 #pragma unroll
     for (int k = 2; k <= 64; k <<= 1) {
@@ -547,47 +577,67 @@ __global__ __launch_bounds__(256) void k_union(const int32_t* sel, int tot, int3
     const bool keep = v != INT_MAX && (lane == 0 || v != prev);
     const uint64_t m = __ballot(keep);
     const int n = __popcll(m);
-    if (keep) u[__popcll(m & ((1ull << lane) - 1ull))] = v;
-    if (lane >= n && lane < tot) u[lane] = -1;
+    if (keep) urow[__popcll(m & ((1ull << lane) - 1ull))] = v;
+    if (lane >= n && lane < tot) urow[lane] = -1;
     if (lane == 0) n_uni[h] = n;
     return;
   }
-  int32_t* vals = u_lds;
-  int32_t* first = u_lds + tot;
-  for (int i = tid; i < tot; i += blockDim.x) vals[i] = s[i];
-  __syncthreads();
-  for (int i = tid; i < tot; i += blockDim.x) {
-    const int v = vals[i];
-    bool f = v >= 0;
-    for (int k = 0; k < i && f; ++k) f = vals[k] != v;
-    first[i] = f;
+  // long selections: bitonic sort of the padded list in LDS (empty = INT_MAX),
+  // then keep the first of each run of equal ids
+  const int P = union_pad(tot), nthr = blockDim.x, nw = nthr >> 6;
+  for (int i = tid; i < P; i += nthr) {
+    const int v = i < tot ? sel_all[i] : -1;
+    sel_all[i] = v < 0 ? INT_MAX : v;
   }
   __syncthreads();
-  int nf = 0;
-  for (int k = 0; k < tot; ++k) nf += first[k];
-  for (int i = tid; i < tot; i += blockDim.x) {
-    if (first[i]) {
-      const int v = vals[i];
-      int pos = 0;
-      for (int k = 0; k < tot; ++k) pos += first[k] && vals[k] < v;
-      u[pos] = v;
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < P; i += nthr) {
+        const int l = i ^ jj;
+        if (l > i) {
+          const int a = sel_all[i], b = sel_all[l];
+          if (((i & k) == 0) == (a > b)) {
+            sel_all[i] = b;
+            sel_all[l] = a;
+          }
+        }
+      }
+      __syncthreads();
     }
-    if (i >= nf) u[i] = -1;
   }
-  if (tid == 0) n_uni[h] = nf;
+  int32_t* wcount = wn;   // per-wave counts of a round
+  int base = 0;
+  for (int r0 = 0; r0 < P; r0 += nthr) {
+    const int i = r0 + tid;
+    const int v = i < P ? sel_all[i] : INT_MAX;
+    const bool keep = v != INT_MAX && (i == 0 || sel_all[i - 1] != v);
+    const uint64_t m = __ballot(keep);
+    if (lane == 0) wcount[wv] = __popcll(m);
+    __syncthreads();
+    int before = base, all = base;
+    for (int w2 = 0; w2 < nw; ++w2) {
+      before += w2 < wv ? wcount[w2] : 0;
+      all += wcount[w2];
+    }
+    if (keep) urow[before + __popcll(m & ((1ull << lane) - 1ull))] = v;
+    base = all;
+    __syncthreads();
+  }
+  for (int i = base + tid; i < tot; i += nthr) urow[i] = -1;
+  if (tid == 0) n_uni[h] = base;
 }
 
 template <int D, class T>
 void launch_typed(const DevLayout& L, const void* blob, const void* Qv, int budget, int beam, int32_t* sel,
-                  int32_t* trace, hipStream_t s) {
+                  int32_t* uni, int32_t* n_uni, int32_t* trace, hipStream_t s) {
   const int kpg = budget / ICE_PAGE_CAP;
   const int lcap = beam > kpg ? beam : kpg;
   const bool big = lcap > 64;
-  const SelLds S = sel_lds(lcap, big);
-  const dim3 grid((unsigned)(((L.H + 7) / 8) * 8 * L.G)), block(64 * kWaves);
+  const SelLds S = sel_lds(L.G, lcap, kpg, big);
+  const dim3 grid((unsigned)L.H), block(64 * waves_per_query(L.G) * L.G);
   const T* Q = static_cast<const T*>(Qv);
-  if (big) k_select<D, T, true><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, trace);
-  else k_select<D, T, false><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, trace);
+  if (big) k_select<D, T, true><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, uni, n_uni, trace);
+  else k_select<D, T, false><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, uni, n_uni, trace);
 }
 
 }  // namespace
@@ -595,17 +645,12 @@ void launch_typed(const DevLayout& L, const void* blob, const void* Qv, int budg
 hipError_t launch_select(const DevLayout& L, const void* blob, const void* Q, int budget, int beam,
                          int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace, hipStream_t s) {
   if (L.dtype == ICE_BF16) {
-    if (L.d == 128) launch_typed<128, uint16_t>(L, blob, Q, budget, beam, sel, trace, s);
-    else launch_typed<64, uint16_t>(L, blob, Q, budget, beam, sel, trace, s);
+    if (L.d == 128) launch_typed<128, uint16_t>(L, blob, Q, budget, beam, sel, uni, n_uni, trace, s);
+    else launch_typed<64, uint16_t>(L, blob, Q, budget, beam, sel, uni, n_uni, trace, s);
   } else {
-    if (L.d == 128) launch_typed<128, float>(L, blob, Q, budget, beam, sel, trace, s);
-    else launch_typed<64, float>(L, blob, Q, budget, beam, sel, trace, s);
+    if (L.d == 128) launch_typed<128, float>(L, blob, Q, budget, beam, sel, uni, n_uni, trace, s);
+    else launch_typed<64, float>(L, blob, Q, budget, beam, sel, uni, n_uni, trace, s);
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int tot = L.G * (budget / ICE_PAGE_CAP);
-  const size_t lds = tot > 64 ? (size_t)tot * 8 : 0;
-  k_union<<<(unsigned)L.H, tot > 64 ? 256 : 64, lds, s>>>(sel, tot, uni, n_uni);
   return hipGetLastError();
 }
 
