@@ -9,13 +9,13 @@
 // One block of 8 waves per head; wave w takes union pages w, w+8, ... and
 // keeps an online softmax (running max m, sum l, output o) for up to 4 query
 // heads at a time. Per page (16 rows) the wave reads K with 4 lanes per row
-// (a quarter row each, bf16 dot2 for q.k) and V with 16 lanes per row (each
+// (16-byte pieces p, p+4, ... for lane part p; bf16 dot2 for q.k) and V with 16 lanes per row (each
 // lane 4 rows x D/16 dims), so both are plain coalesced 16-byte loads; the
 // next page's loads are issued before the current page is used. Logits are
 // kept in base 2 (scaled by scale * log2 e). The 8 wave partials of a head
-// are merged in LDS. Every row of a created page holds finite values (empty
-// slots are zero), so rows are loaded unconditionally and masked by the
-// page's count.
+// are merged in LDS. Loads are unconditional (so the next page's loads stay
+// in flight): the lanes of rows past a page's count re-read its last valid
+// row, which costs no extra memory traffic, and those rows are masked.
 #include "ice_launch.h"
 
 namespace ice {
@@ -63,15 +63,20 @@ struct PageRegs {
 };
 
 template <int D, class T>
-__device__ inline void load_page(const T* pgK, const T* pgV, int pg, int lane, PageRegs<D, T>& r) {
+__device__ inline void load_page(const T* pgK, const T* pgV, int pg, int cnt, int lane, PageRegs<D, T>& r) {
   using A = AttGeo<D, T>;
   const int64_t base = (int64_t)pg * ICE_PAGE_CAP;
-  const char* krow = reinterpret_cast<const char*>(pgK + (base + (lane >> 2)) * D) + (lane & 3) * (A::ROWB / 4);
+  // rows past the page's count are masked later; they read the last valid row
+  // (already in cache) instead of the empty slots
+  const int last = cnt > 0 ? cnt - 1 : 0;
+  // lane part p holds the 16-byte pieces p, p + 4, ...: the 4 lanes of a row
+  // read one contiguous 64-byte segment per load
+  const char* krow = reinterpret_cast<const char*>(pgK + (base + min(lane >> 2, last)) * D) + (lane & 3) * 16;
 #pragma unroll
-  for (int i = 0; i < A::NLK; ++i) r.k[i] = *reinterpret_cast<const V4*>(krow + 16 * i);
+  for (int i = 0; i < A::NLK; ++i) r.k[i] = *reinterpret_cast<const V4*>(krow + 64 * i);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const char* vrow = reinterpret_cast<const char*>(pgV + (base + (lane >> 4) + 4 * i) * D) + (lane & 15) * A::VB;
+    const char* vrow = reinterpret_cast<const char*>(pgV + (base + min((lane >> 4) + 4 * i, last)) * D) + (lane & 15) * A::VB;
     if constexpr (A::VB >= 16) {
 #pragma unroll
       for (int c = 0; c < A::VB / 16; ++c) {
@@ -154,9 +159,9 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend(DevLayout L, const vo
 #pragma unroll
     for (int g = 0; g < kQPerPass; ++g) {
       const char* qrow = reinterpret_cast<const char*>(Q + ((int64_t)h * G + g0 + (g < ng ? g : 0)) * D) +
-                         (lane & 3) * (A::ROWB / 4);
+                         (lane & 3) * 16;
 #pragma unroll
-      for (int i = 0; i < A::NLK; ++i) q[g][i] = *reinterpret_cast<const V4*>(qrow + 16 * i);
+      for (int i = 0; i < A::NLK; ++i) q[g][i] = *reinterpret_cast<const V4*>(qrow + 64 * i);
     }
     float m[kQPerPass], l[kQPerPass], o[kQPerPass][A::DV];
 #pragma unroll
@@ -181,10 +186,10 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend(DevLayout L, const vo
       // the next page's loads stay in flight while the current one is used
       int pg = __shfl(my_pg, 0, 64);
       PageRegs<D, T> cur, nxt;
-      load_page<D, T>(pgK, pgV, pg >= 0 ? pg : 0, lane, cur);
+      load_page<D, T>(pgK, pgV, pg >= 0 ? pg : 0, __shfl(my_cnt, 0, 64), lane, cur);
       for (int k = 0; k < nk; ++k) {
         const int pgn = k + 1 < nk ? __shfl(my_pg, k + 1, 64) : -1;
-        load_page<D, T>(pgK, pgV, pgn >= 0 ? pgn : 0, lane, nxt);
+        load_page<D, T>(pgK, pgV, pgn >= 0 ? pgn : 0, k + 1 < nk ? __shfl(my_cnt, k + 1, 64) : 0, lane, nxt);
         const int cnt = __shfl(my_cnt, k, 64);
         if (pg >= 0) {
           const bool valid = krow < cnt;

@@ -32,7 +32,6 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxWaves = 16;
-constexpr int kChainBatch = 64;     // pages gathered per round
 
 __host__ __device__ inline int waves_per_query(int G) { return G <= 4 ? 4 : 16 / G; }
 // LDS slots of the union's sort: the next power of two
@@ -46,9 +45,9 @@ __host__ __device__ inline int union_pad(int n) {
 template <int D, class T>
 struct Quarter {
   static constexpr int ROWB = D * (int)sizeof(T);
-  static constexpr int PB = ROWB / 4;                 // bytes per lane per row
-  static constexpr int NL = PB / 16;                  // 16-byte loads per lane per row
-  static constexpr int GB = NL >= 8 ? 2 : 4;          // row groups per load batch
+  static constexpr int NL = ROWB / 64;                // 16-byte loads per lane per row
+  static constexpr int GB = NL >= 4 ? 2 : 4;          // row groups per load batch (keeps 128 VGPRs)
+  static constexpr int GB0 = NL == 4 ? 3 : GB;        // pages per level-0 batch (keeps 128 VGPRs)
   V4 q[NL];
   int part;
 
@@ -56,14 +55,15 @@ struct Quarter {
     part = lane & 3;
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-      q[i] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(qrow) + part * PB + i * 16);
+      q[i] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(qrow) + part * 16 + i * 64);
   }
-  // this lane's quarter of `row`, or zeros when `ok` is false
+  // this lane's 16-byte pieces part, part + 4, ... of `row` (the row's 4 lanes
+  // read one contiguous 64-byte segment per load), or zeros when `ok` is false
   __device__ inline void fetch(bool ok, const T* row, V4* out) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       out[i] = V4{0, 0, 0, 0};
-      if (ok) out[i] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(row) + part * PB + i * 16);
+      if (ok) out[i] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(row) + part * 16 + i * 64);
     }
   }
   // q.row from this lane's quarter, summed over the row's 4 lanes
@@ -160,81 +160,117 @@ __device__ inline uint64_t wave_merge_desc(uint64_t a, uint64_t b_sorted, int la
 }
 
 // ---- LDS layout ------------------------------------------------------------
+// Per wave: its LDS top list (long lists only), a chunk of 64 keys and the 64
+// (page, valid rows) pairs of the current round. Per query head: the owner
+// table of its kept list (page offsets, first page, run and last-page count)
+// and, for long lists, the merged list. Then small counters and the union's
+// sort area.
 struct SelLds {
   int lcap;           // list capacity = max(beam, pages per query)
-  int wave_bytes;     // per wave: [LDS lists: list[2][lcap] u64] chunk[64] u64, cand/cval[64] i32, 4 ints
-  int off_comb;       // register lists: [2 parities][kMaxWaves][64] u64
-  int off_query;      // LDS lists: [G][lcap] u64 query lists
-  int off_wn;         // LDS lists: per wave count and buffer (2 ints)
-  int off_qn;         // LDS lists: per query count
-  int off_sel;        // [G][kpg] i32 selections (for the union)
+  int wave_bytes;
+  int off_comb;       // register lists: [kMaxWaves][64] u64
+  int off_query;      // LDS lists: [G][lcap] u64 merged lists
+  int off_meta;       // [G][meta_ints] owner tables
+  int meta_ints;
+  int off_misc;       // wn[kMaxWaves], qn[ICE_MAX_GROUP], qp[ICE_MAX_GROUP]
+  int off_sel;        // [G * kpg rounded up to a power of two] i32: selections, then the union's sort
   int total;
 };
 
 __host__ __device__ inline SelLds sel_lds(int G, int lcap, int kpg, bool big) {
   SelLds s;
   s.lcap = lcap;
-  s.wave_bytes = (big ? 2 * lcap * 8 : 0) + 64 * 8 + 2 * kChainBatch * 4 + 16;
+  s.wave_bytes = (big ? lcap * 8 : 0) + 64 * 8 + 2 * 64 * 4;
   s.off_comb = kMaxWaves * s.wave_bytes;
-  s.off_query = s.off_comb + (big ? 0 : 2 * kMaxWaves * 64 * 8);
-  s.off_wn = s.off_query + (big ? G * lcap * 8 : 0);
-  s.off_qn = s.off_wn + kMaxWaves * 8;
-  s.off_sel = s.off_qn + ICE_MAX_GROUP * 4;
+  s.off_query = s.off_comb + (big ? 0 : kMaxWaves * 64 * 8);
+  s.off_meta = s.off_query + (big ? G * lcap * 8 : 0);
+  s.meta_ints = 3 * lcap + 2;
+  s.off_misc = s.off_meta + G * s.meta_ints * 4;
+  s.off_sel = s.off_misc + (kMaxWaves + 2 * ICE_MAX_GROUP) * 4;
   s.total = s.off_sel + union_pad(G * kpg) * 4;
   return s;
 }
 
 struct WaveArea {
-  uint64_t* lists;     // two buffers of lcap keys each (LDS lists only)
-  int lcap;
-  uint64_t* chunk;
-  int32_t* cand;       // gathered page / block ids
-  int32_t* cval;       // their valid slots
-  int32_t* ncand;
+  uint64_t* list;      // LDS top list, lcap keys (long lists only)
+  uint64_t* chunk;     // 64 keys
+  int32_t* cand;       // page ids of the round
+  int32_t* cval;       // their valid rows
 };
 
 __device__ inline WaveArea wave_area(char* smem, const SelLds& S, int wv, bool big) {
   char* b = smem + wv * S.wave_bytes;
   WaveArea a;
-  a.lists = reinterpret_cast<uint64_t*>(b);
-  a.lcap = S.lcap;
-  a.chunk = a.lists + (big ? 2 * S.lcap : 0);
+  a.list = reinterpret_cast<uint64_t*>(b);
+  a.chunk = a.list + (big ? S.lcap : 0);
   a.cand = reinterpret_cast<int32_t*>(a.chunk + 64);
-  a.cval = a.cand + kChainBatch;
-  a.ncand = a.cval + kChainBatch;
+  a.cval = a.cand + 64;
   return a;
+}
+
+// the owner table of a query head's kept list: off[i] = first page index of
+// kept owner i among the query's pages (off[n] = their total), fst[i] = its
+// first page, rl[i] = (pages in its build run) * 32 + (rows of its last page)
+struct OwnerTable {
+  int32_t* off;
+  int32_t* fst;
+  int32_t* rl;
+};
+
+__device__ inline OwnerTable owner_table(char* smem, const SelLds& S, int g) {
+  int32_t* m = reinterpret_cast<int32_t*>(smem + S.off_meta) + g * S.meta_ints;
+  return OwnerTable{m, m + S.lcap + 1, m + 2 * S.lcap + 1};
+}
+
+__device__ inline uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d, 64);
+    if (lane >= d) v += y;
+  }
+  return v;
 }
 
 // ---- wave top lists --------------------------------------------------------
 // Register list (cap <= 64): lane i holds entry i, 0 = empty.
 struct RegTop {
   uint64_t L;
-  int cap;
+  int cap, n;
   __device__ inline void init(int c) {
     L = 0ull;
     cap = c;
+    n = 0;
   }
   __device__ inline void push(const WaveArea&, uint64_t x, int lane) {
-    const uint64_t thr = shfl64(L, cap - 1);   // 0 until the list is full
-    if (__ballot(x > thr) == 0) return;
-    const uint64_t t = wave_merge_desc(L, wave_sort_desc(x, lane), lane);
+    const uint64_t thr = n == cap ? readlane64(L, cap - 1) : 0ull;
+    const uint64_t live = __ballot(x > thr);
+    if (live == 0) return;
+    uint64_t t = wave_sort_desc(x, lane);
+    if (n > 0) t = wave_merge_desc(L, t, lane);
     L = lane < cap ? t : 0ull;
+    n = min(cap, n + __popcll(live));
   }
 };
 
-// LDS list (any cap up to ICE_MAX_BEAM), sorted descending, double-buffered.
+// LDS list (any cap up to ICE_MAX_BEAM), sorted descending. A push ranks
+// every entry of the list and of the chunk within their union and rewrites
+// the list in place (all reads happen before the writes).
 struct LdsTop {
-  int cur, n, cap;
+  int n, cap;
   __device__ inline void init(int c) {
-    cur = 0;
     n = 0;
     cap = c;
   }
   __device__ void push(const WaveArea& a, uint64_t x, int lane) {
     a.chunk[lane] = x;
     wave_sync();
-    const uint64_t* Lc = a.lists + cur * a.lcap;
-    uint64_t* Nx = a.lists + (cur ^ 1) * a.lcap;
+    uint64_t* Lc = a.list;
     const uint64_t thr = n == cap ? Lc[cap - 1] : 0ull;
     const bool live = x > thr;
     const uint64_t live_mask = __ballot(live);
@@ -250,15 +286,24 @@ struct LdsTop {
       if (Lc[mid] > x) lo = mid + 1;
       else hi = mid;
     }
-    for (int i = lane; i < n; i += 64) {
-      const uint64_t y = Lc[i];
-      int c = 0;
-      for (int j = 0; j < 64; ++j) c += a.chunk[j] > y;
-      if (i + c < cap) Nx[i + c] = y;
+    uint64_t y[ICE_MAX_BEAM / 64];
+    int c[ICE_MAX_BEAM / 64];
+#pragma unroll
+    for (int k = 0; k < ICE_MAX_BEAM / 64; ++k) {
+      const int i = lane + 64 * k;
+      y[k] = i < n ? Lc[i] : 0ull;
+      c[k] = 0;
+      if (i < n)
+        for (int j = 0; j < 64; ++j) c[k] += a.chunk[j] > y[k];
     }
-    if (live && lo + rc < cap) Nx[lo + rc] = x;
+    wave_sync();
+#pragma unroll
+    for (int k = 0; k < ICE_MAX_BEAM / 64; ++k) {
+      const int i = lane + 64 * k;
+      if (i < n && i + c[k] < cap) Lc[i + c[k]] = y[k];
+    }
+    if (live && lo + rc < cap) Lc[lo + rc] = x;
     n = min(cap, n + __popcll(live_mask));
-    cur ^= 1;
     wave_sync();
   }
 };
@@ -274,42 +319,35 @@ __device__ inline int count_greater(const uint64_t* l, int n, uint64_t x) {
   return lo;
 }
 
-// Walks the pages of one owner per lane. An owner's pages are all full except
-// its last; the pages of the build form one contiguous run starting at
-// first[], so they need no pointer chasing; only pages split off later by
-// inserts are reached through next[].
-struct OwnerWalk {
-  int page, idx, first, run, cnt;
-  __device__ inline void start(int owner_slot, const int32_t* firsts, const int32_t* runs, const int32_t* cnts) {
-    page = -1;
-    if (owner_slot < 0) return;
-    first = firsts[owner_slot];
-    run = runs[owner_slot];
-    cnt = cnts[owner_slot];
-    idx = 0;
-    page = cnt > 0 ? first : -1;
-  }
-};
-
-// Gathers up to kChainBatch (page, valid slots) pairs from this wave's lanes'
-// owners; a lane resumes where the batch filled up. Returns the count.
-__device__ inline int gather_pages(const WaveArea& a, OwnerWalk& w, const int32_t* next, int lane) {
-  if (lane == 0) *a.ncand = 0;
-  wave_sync();
-  while (w.page >= 0) {
-    const int slot = atomicAdd(a.ncand, 1);
-    if (slot >= kChainBatch) break;
-    a.cand[slot] = w.page;
-    a.cval[slot] = min(ICE_PAGE_CAP, w.cnt - ICE_PAGE_CAP * w.idx);
-    ++w.idx;
-    if (w.idx * ICE_PAGE_CAP >= w.cnt) w.page = -1;
-    else if (w.idx < w.run) w.page = w.first + w.idx;
-    else w.page = next[w.page];
+// Fills the wave's cand/cval with its pages of round t0: the query head's
+// pages (all pages of its kept owners, owner by owner) are dealt to its W
+// waves round-robin, wave j taking pages j, j + W, ...; lane l takes the
+// wave's page t0 + l. An owner's pages are all full except its last; the
+// pages of the build form one contiguous run from its first page, so only
+// pages split off later by inserts are reached through next[]. Returns the
+// number of pages of the round.
+__device__ inline int deal_pages(const WaveArea& a, const OwnerTable& T, int n_own, int P, int j, int W, int t0,
+                                 const int32_t* next, int lane) {
+  const int mine = P > j ? (P - j + W - 1) / W : 0;
+  const int nb = min(64, mine - t0);
+  if (nb <= 0) return 0;
+  if (lane < nb) {
+    const int p = j + W * (t0 + lane);
+    int lo = 0, hi = n_own - 1;      // last owner whose first page index is <= p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (T.off[mid] <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    const int k = p - T.off[lo], np = T.off[lo + 1] - T.off[lo];
+    const int run = max(1, T.rl[lo] >> 5), last = T.rl[lo] & 31;
+    int pg = T.fst[lo] + min(k, run - 1);
+    for (int s = run; s <= k; ++s) pg = next[pg];
+    a.cand[lane] = pg;
+    a.cval[lane] = k < np - 1 ? ICE_PAGE_CAP : last;
   }
   wave_sync();
-  const int n = min(*a.ncand, kChainBatch);
-  wave_sync();
-  return n;
+  return nb;
 }
 
 // Keys of 4 row groups, one candidate per lane: group g, row r -> lane 16g + r.
@@ -346,13 +384,16 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = wv / W, j = wv % W;      // query head, wave within the query
+  const bool lead = j == g % W;          // merges the query's lists (leads sit on different SIMDs)
   const int kpg = budget / ICE_PAGE_CAP;
   const SelLds S = sel_lds(G, max(beam, kpg), kpg, BIG);
   const WaveArea A = wave_area(smem, S, wv, BIG);
+  const OwnerTable OT = owner_table(smem, S, g);
   uint64_t* comb = reinterpret_cast<uint64_t*>(smem + S.off_comb);
   uint64_t* qlist = reinterpret_cast<uint64_t*>(smem + S.off_query) + g * S.lcap;
-  int32_t* wn = reinterpret_cast<int32_t*>(smem + S.off_wn);
-  int32_t* qn = reinterpret_cast<int32_t*>(smem + S.off_qn);
+  int32_t* wn = reinterpret_cast<int32_t*>(smem + S.off_misc);
+  int32_t* qn = wn + kMaxWaves;
+  int32_t* qp = qn + ICE_MAX_GROUP;
   int32_t* sel_all = reinterpret_cast<int32_t*>(smem + S.off_sel);
 
   const void* hb = head_base(blob, L, h);
@@ -364,64 +405,96 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
   const int row = lane >> 2;             // row of this lane inside a 16-row pass
 
   int32_t* tr = trace ? trace + ((int64_t)h * G + g) * L.L * beam : nullptr;
-  if (tr && j == 0)
+  if (tr && lead)
     for (int i = lane; i < L.L * beam; i += 64) tr[i] = -1;
 
-  // the query head's kept list after each cut: a register list (lane i holds
-  // entry i) or, for long lists, qlist in LDS
-  uint64_t ql = 0ull;
-  int qcount = 0, parity = 0;
-  auto combine = [&](Top& t, int cap) {
-    if constexpr (!BIG) {
-      uint64_t* area = comb + parity * kMaxWaves * 64;
-      area[wv * 64 + lane] = t.L;
-      __syncthreads();
-      uint64_t r = t.L;
-      for (int jj = 0; jj < W; ++jj)
-        if (jj != j) r = wave_merge_desc(r, area[(g * W + jj) * 64 + lane], lane);
-      ql = lane < cap ? r : 0ull;
-      qcount = __popcll(__ballot(ql != 0ull));
-      parity ^= 1;
-    } else {
-      if (lane == 0) {
-        wn[2 * wv] = t.n;
-        wn[2 * wv + 1] = t.cur;
+  // Owner table of `nk` kept owners (lead wave): their pages in table `lvl`.
+  // id_of(i) gives the token id (owner slot) of kept entry i.
+  auto build_table = [&](int lvl, int nk, auto id_of) {
+    const int32_t* firsts = at<int32_t>(hb, L.off_first[lvl]);
+    const int32_t* runs = at<int32_t>(hb, L.off_orun[lvl]);
+    const int32_t* cnts = at<int32_t>(hb, L.off_ocnt[lvl]);
+    int base = 0;
+    for (int c0 = 0; c0 < nk; c0 += 64) {
+      const int i = c0 + lane;
+      const int o = i < nk ? id_of(i) : -1;
+      int cnt = 0, first = 0, run = 0;
+      if (o >= 0) {
+        cnt = cnts[o];
+        first = firsts[o];
+        run = runs[o];
       }
+      const int np = (cnt + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP;
+      const int incl = wave_incl_scan(np, lane);
+      if (i < nk) {
+        OT.off[i] = base + incl - np;
+        OT.fst[i] = first;
+        OT.rl[i] = run * 32 + (np > 0 ? cnt - ICE_PAGE_CAP * (np - 1) : 0);
+      }
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) {
+      OT.off[nk] = base;
+      qn[g] = nk;
+      qp[g] = base;
+    }
+  };
+
+  // Merges the W wave lists of each query head into its kept list of at most
+  // `cap` entries; the lead wave writes the trace row `cut` (cut >= 0) or the
+  // selection (cut < 0), and the owner table of the kept points in table
+  // `lvl` (lvl >= 0).
+  auto combine = [&](Top& t, int cap, int cut, int lvl) {
+    if constexpr (!BIG) {
+      comb[wv * 64 + lane] = t.L;
       __syncthreads();
-      const uint64_t* mine = A.lists + t.cur * A.lcap;
+      if (lead) {
+        uint64_t r = comb[(g * W) * 64 + lane];
+        for (int jj = 1; jj < W; ++jj) r = wave_merge_desc(r, comb[(g * W + jj) * 64 + lane], lane);
+        const uint64_t ql = lane < cap ? r : 0ull;
+        const int qc = __popcll(__ballot(ql != 0ull));
+        const int id = lane < qc ? key_id(ql) : -1;
+        if (cut >= 0) {
+          if (tr && lane < beam) tr[cut * beam + lane] = id;
+        } else if (lane < kpg) {
+          sel[((int64_t)h * G + g) * kpg + lane] = id;
+          sel_all[g * kpg + lane] = id;
+        }
+        if (lvl >= 0) build_table(lvl, qc, [&](int) { return id; });
+      }
+    } else {
+      if (lane == 0) wn[wv] = t.n;
+      __syncthreads();
       int tot = 0;
-      for (int jj = 0; jj < W; ++jj) tot += wn[2 * (g * W + jj)];
+      for (int jj = 0; jj < W; ++jj) tot += wn[g * W + jj];
       for (int i = lane; i < t.n; i += 64) {
-        const uint64_t x = mine[i];
+        const uint64_t x = A.list[i];
         int rank = i;
         for (int jj = 0; jj < W; ++jj) {
           if (jj == j) continue;
           const int ow = g * W + jj;
-          const uint64_t* other = reinterpret_cast<const uint64_t*>(smem + ow * S.wave_bytes) + wn[2 * ow + 1] * S.lcap;
-          rank += count_greater(other, wn[2 * ow], x);
+          rank += count_greater(reinterpret_cast<const uint64_t*>(smem + ow * S.wave_bytes), wn[ow], x);
         }
         if (rank < cap) qlist[rank] = x;
       }
-      if (j == 0 && lane == 0) qn[g] = min(cap, tot);
       __syncthreads();
-      qcount = qn[g];
+      if (lead) {
+        const int qc = min(cap, tot);
+        auto id_of = [&](int i) { return i < qc ? key_id(qlist[i]) : -1; };
+        if (cut >= 0) {
+          if (tr)
+            for (int i = lane; i < beam; i += 64) tr[cut * beam + i] = id_of(i);
+        } else {
+          for (int i = lane; i < kpg; i += 64) {
+            const int id = id_of(i);
+            sel[((int64_t)h * G + g) * kpg + i] = id;
+            sel_all[g * kpg + i] = id;
+          }
+        }
+        if (lvl >= 0) build_table(lvl, qc, id_of);
+      }
     }
-  };
-  // owner (token id) of kept entry oi, -1 past the list; every lane calls it
-  auto kept = [&](int oi) -> int {
-    if constexpr (!BIG) {
-      const uint64_t k = shfl64(ql, oi & 63);
-      return oi < qcount ? key_id(k) : -1;
-    } else {
-      return oi < qcount ? key_id(qlist[oi]) : -1;
-    }
-  };
-  auto emit = [&](int32_t* dst, int n_out) {   // kept ids (rank order), -1 padded
-    if constexpr (!BIG) {
-      if (lane < n_out) dst[lane] = lane < qcount ? key_id(ql) : -1;
-    } else {
-      for (int i = lane; i < n_out; i += 64) dst[i] = i < qcount ? key_id(qlist[i]) : -1;
-    }
+    __syncthreads();
   };
 
   int cut = 0;
@@ -448,21 +521,17 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
         }
         tl.push(A, chunk_keys<D, T>(qs, ok, rp, tk, lane), lane);
       }
-      combine(tl, beam);
-      if (tr && j == 0) emit(tr + cut * beam, beam);
-      ++cut;
+      combine(tl, beam, cut++, Ltop - 1);
     }
-    // ---- levels Ltop-1 .. 1: the children of the kept points
+    // ---- levels Ltop-1 .. 1: the children of the kept points, every row scored
     for (int l = Ltop - 1; l >= 1; --l) {
       const int32_t* next = at<int32_t>(hb, L.off_pg_next[l]);
       const int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[l]);
       const T* pgK = at<T>(hb, L.off_pgK[l]);
-      OwnerWalk ow;
-      ow.start(kept(j + W * lane), at<int32_t>(hb, L.off_first[l]), at<int32_t>(hb, L.off_orun[l]),
-               at<int32_t>(hb, L.off_ocnt[l]));
+      const int n_own = qn[g], P = qp[g];
       Top tl;
       tl.init(beam);
-      for (int nb; (nb = gather_pages(A, ow, next, lane)) > 0;) {
+      for (int t0 = 0, nb; (nb = deal_pages(A, OT, n_own, P, j, W, t0, next, lane)) > 0; t0 += 64) {
         for (int b0 = 0; b0 < nb; b0 += 4) {
           bool ok[4];
           const T* rp[4];
@@ -477,64 +546,39 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
           }
           tl.push(A, chunk_keys<D, T>(qs, ok, rp, tk, lane), lane);
         }
+        wave_sync();
       }
-      combine(tl, beam);
-      if (tr && j == 0) emit(tr + cut * beam, beam);
-      ++cut;
+      combine(tl, beam, cut++, l - 1);
     }
+  } else if (n_tok > 0) {
+    // ---- root: the virtual root owns every token
+    if (lead) build_table(0, 1, [&](int) { return L.cap; });
+    __syncthreads();
   }
 
-  // ---- level 0: the pages of the kept level-1 points (every page at the root)
+  // ---- level 0: the pages of the kept level-1 points, one key per page
   {
     Top tl;
     tl.init(kpg);
     if (n_tok > 0) {
       const int32_t* next = at<int32_t>(hb, L.off_pg_next[0]);
       const T* pgK = at<T>(hb, L.off_pgK[0]);
-      const int32_t* firsts = at<int32_t>(hb, L.off_first[0]);
-      const int32_t* runs = at<int32_t>(hb, L.off_orun[0]);
-      const int32_t* cnts = at<int32_t>(hb, L.off_ocnt[0]);
-      OwnerWalk ow;
-      int root_next = j, root_cnt = 0, n_pages = 0;
-      if (Ltop >= 1) {
-        ow.start(kept(j + W * lane), firsts, runs, cnts);
-      } else {
-        // root: chain order is page id order; the pages are split over the waves by id
-        ow.page = -1;
-        root_cnt = cnts[L.cap];
-        n_pages = hdr->n_pages[0];
-      }
+      const int n_own = qn[g], P = qp[g];
       uint64_t pk = 0ull;
       int fill = 0;
-      for (;;) {
-        int nb;
-        if (Ltop >= 1) {
-          nb = gather_pages(A, ow, next, lane);
-        } else {
-          nb = min(kChainBatch, (n_pages - root_next + W - 1) / W);
-          if (nb > 0) {
-            for (int i = lane; i < nb; i += 64) {
-              const int pg = root_next + i * W;
-              A.cand[i] = pg;
-              A.cval[i] = min(ICE_PAGE_CAP, root_cnt - ICE_PAGE_CAP * pg);
-            }
-            root_next += nb * W;
-          }
-          wave_sync();
-        }
-        if (nb <= 0) break;
-        for (int b0 = 0; b0 < nb; b0 += QG::GB) {
-          V4 buf[QG::GB][QG::NL];
-          int pg[QG::GB], cv[QG::GB];
+      for (int t0 = 0, nb; (nb = deal_pages(A, OT, n_own, P, j, W, t0, next, lane)) > 0; t0 += 64) {
+        for (int b0 = 0; b0 < nb; b0 += QG::GB0) {
+          V4 buf[QG::GB0][QG::NL];
+          int pg[QG::GB0], cv[QG::GB0];
 #pragma unroll
-          for (int b = 0; b < QG::GB; ++b) {
+          for (int b = 0; b < QG::GB0; ++b) {
             pg[b] = b0 + b < nb ? A.cand[b0 + b] : -1;
             cv[b] = b0 + b < nb ? A.cval[b0 + b] : 0;
             const bool ok = pg[b] >= 0 && row < cv[b];
             qs.fetch(ok, pgK + ((int64_t)(ok ? pg[b] : 0) * ICE_PAGE_CAP + row) * D, buf[b]);
           }
 #pragma unroll
-          for (int b = 0; b < QG::GB; ++b) {
+          for (int b = 0; b < QG::GB0; ++b) {
             if (pg[b] < 0) continue;
             float s = qs.dot(buf[b]);
             if (row >= cv[b]) s = -INFINITY;
@@ -547,17 +591,12 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
             }
           }
         }
+        wave_sync();
       }
       if (fill) tl.push(A, pk, lane);
     }
-    combine(tl, kpg);
+    combine(tl, kpg, -1, -1);
   }
-  // ---- outputs of this query head
-  if (j == 0) {
-    emit(sel + ((int64_t)h * G + g) * kpg, kpg);
-    emit(sel_all + g * kpg, kpg);
-  }
-  __syncthreads();
   // ---- union over the group, ascending page id, -1 padded
   const int tot = G * kpg;
   int32_t* urow = uni + (int64_t)h * tot;

@@ -48,11 +48,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ctx36k", choices=sorted(WORKLOADS))
     ap.add_argument("--budget", type=int, default=256)
-    ap.add_argument("--budgets", default="64,128,256")
+    ap.add_argument("--budgets", default="", help="extra budgets to time beside --budget, e.g. 64,128")
     ap.add_argument("--builds", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size kernel that "
+                         "calibrates hardware byte counters)")
     return ap.parse_args()
 
 
@@ -151,7 +154,7 @@ def main():
     from ann_retrieval_amd.api import IceIndex
 
     H, G, N, d, dtype, C, rotate, desc = WORKLOADS[a.workload]
-    budgets = [int(b) for b in a.budgets.split(",")]
+    budgets = [int(b) for b in a.budgets.split(",") if b]
     if a.budget not in budgets:
         budgets.append(a.budget)
     dev = torch.device("cuda", 0)
@@ -177,34 +180,59 @@ def main():
     print(f"[bench] build {build_ms:.2f} ms", file=sys.stderr, flush=True)
     head_meta(ix, H, N + n_ins)
 
+    if a.copy_mib:
+        # two plain copies of a known size: the runtime's device-to-device copy
+        # and an elementwise x + 0 (16-byte loads and stores per lane)
+        src = torch.empty(a.copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---- decode steps
     Qs = [synth.decode_queries(w, G, gen, device=dev) for _ in range(a.warmup + a.steps)]
     results = {}
     for budget in budgets:
         k = budget // 16
         beam = k
-        sel = torch.empty(H, G, k, dtype=torch.int32, device=dev)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
         for s in range(a.warmup):
             _, uni, nuni = ix.ice_select(Qs[s], budget, beam)
             ix.ice_attend(Qs[s], uni, nuni)
         torch.cuda.synchronize()
+        # whole steps: select + attend back to back, no events in between; a
+        # short spin on the stream first lets the host queue the timed steps
+        # ahead of the GPU, so the events bracket GPU work, not launch gaps
         t0 = time.perf_counter()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(5e7))
         g0.record()
+        unis = []
         for s in range(a.steps):
             q = Qs[a.warmup + s]
-            ev[s][0].record()
             _, uni, nuni = ix.ice_select(q, budget, beam)
-            ev[s][1].record()
             ix.ice_attend(q, uni, nuni)
-            ev[s][2].record()
+            unis.append((uni, nuni))
         g1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms_step = g0.elapsed_time(g1) / a.steps
-        sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-        att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        # each kernel on its own: the same launches back to back between two events
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda._sleep(int(5e7))
+        e[0].record()
+        for s in range(a.steps):
+            ix.ice_select(Qs[a.warmup + s], budget, beam)
+        e[1].record()
+        torch.cuda._sleep(int(5e7))
+        e[2].record()
+        for s in range(a.steps):
+            ix.ice_attend(Qs[a.warmup + s], *unis[s])
+        e[3].record()
+        torch.cuda.synchronize()
+        sel_ms = e[0].elapsed_time(e[1]) / a.steps
+        att_ms = e[2].elapsed_time(e[3]) / a.steps
         # algorithmic bytes from the same selections (replayed with a trace)
         nb = min(a.steps, 4)
         sb = ab = 0
