@@ -14,10 +14,14 @@ the library runs on one GPU and no multi-GPU figure is produced.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -53,10 +57,96 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--summarize", nargs="+", metavar="CSV",
+                    help="print a markdown summary of rocprofv3 output instead of benchmarking: one "
+                         "*_kernel_stats.csv, or a FETCH_SIZE and a WRITE_SIZE *_counter_collection.csv")
+    ap.add_argument("--command", default="", help="the command that produced the CSVs (for --summarize)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel that "
                          "calibrates hardware byte counters)")
     return ap.parse_args()
+
+
+# ---- hardware byte counters ----------------------------------------------
+# Sources each kernel is built from: a recorded counter reading is valid only
+# while these are unchanged.
+KERNEL_SOURCES = {
+    "k_select": ["k_select.hip", "ice_common.h", "ice_launch.h"],
+    "k_attend": ["k_attend.hip", "ice_common.h", "ice_launch.h"],
+}
+CSRC = os.path.join(ROOT, "ann_retrieval_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch recorded under profiles/ for this kernel and
+    workload, or None if none was recorded for the current sources."""
+    want = source_hash(kernel)
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as f:
+            for line in f:
+                m = re.match(r"traffic (\S+) workload=(\S+) bytes_per_launch=(\d+) source=(\w+)", line.strip())
+                if m and m.group(1) == kernel and m.group(2) == workload and m.group(4) == want:
+                    return int(m.group(3))
+    return None
+
+
+def short_name(name):
+    name = name.replace("(anonymous namespace)::", "")
+    m = re.search(r"(k_\w+)(<[^()]*>)?\(", name)
+    if m and "ice::" in name:
+        return m.group(1) + (m.group(2) or "")
+    return name.split("(")[0][-70:]
+
+
+def summarize(paths, command, copy_mib, workload):
+    """Markdown summary of rocprofv3 CSV output (kernel stats, or counters)."""
+    out = [f"Command: `{command}`", ""]
+    if len(paths) == 1:
+        rows = list(csv.DictReader(open(paths[0])))
+        out += ["| Kernel | Calls | Average (us) | Min (us) | Max (us) | Time share (%) |", "|---|---|---|---|---|---|"]
+        for r in rows[:25]:
+            out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                       f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.2f} |")
+        print("\n".join(out))
+        return
+    per = {}
+    factor = {}
+    known = copy_mib * 1024.0           # KiB moved by each calibration copy
+    for path in paths:
+        cal = []
+        for r in csv.DictReader(open(path)):
+            c, v, k = r["Counter_Name"], float(r["Counter_Value"]), r["Kernel_Name"]
+            if "copyBuffer" in k or "OnSelf_add" in k:    # the runtime copy and x + 0 of --copy-mib
+                cal.append((v, k))
+            per.setdefault((short_name(k), c), []).append(v)
+        big = [v for v, _ in cal if v > 0.25 * known]
+        factor[c] = known / (sum(big) / len(big))
+        out.append(f"- {c}: calibration copies of {copy_mib} MiB read {', '.join(f'{v:.0f}' for v in big)} KiB "
+                   f"-> factor {factor[c]:.3f}")
+    out += ["", "| Kernel | Dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes / dispatch (scaled) |",
+            "|---|---|---|---|---|"]
+    names = sorted({k for k, _ in per if k.startswith("k_")})
+    lines = []
+    for k in names:
+        f = per.get((k, "FETCH_SIZE"), [0.0])
+        w = per.get((k, "WRITE_SIZE"), [0.0])
+        fa, wa = sum(f) / len(f), sum(w) / len(w)
+        tot = (fa * factor.get("FETCH_SIZE", 1.0) + wa * factor.get("WRITE_SIZE", 1.0)) * 1024.0
+        out.append(f"| `{k}` | {len(f)} | {fa:.1f} | {wa:.1f} | {tot:.0f} |")
+        base = k.split("<")[0]
+        if base in KERNEL_SOURCES:
+            lines.append(f"traffic {base} workload={workload} bytes_per_launch={tot:.0f} source={source_hash(base)}")
+    out += ["", "Recorded for bench.py (the kernel's sources must still hash the same):", "", "```"] + lines + ["```"]
+    print("\n".join(out))
 
 
 def algorithmic_bytes(ix, trace, uni_n, n_uni, d, elt, G):
@@ -145,6 +235,9 @@ def cpu_baseline(w, Qs, budget, beam, heads, seed):
 
 def main():
     a = parse()
+    if a.summarize:
+        summarize(a.summarize, a.command, a.copy_mib or 1024, a.workload)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; no multi-GPU figure is produced",
                           "n_gpus": a.gpus}))
@@ -283,7 +376,8 @@ def main():
         "config": {"workload": desc, "heads": H, "group": G, "context": N, "d": d, "budget_tokens": a.budget,
                    "beam": a.budget // 16, "levels": 3, "promote": "1/16", "page": 16},
         "roofline": {"bound": "hbm", "kernel": f"k_{dom}", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic(f"k_{dom}", a.workload) if a.budget == 256 else None,
                      "bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
         "index_keys_per_s": H * N / (build_ms / 1000.0),
         "build_ms": build_ms,
