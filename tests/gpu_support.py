@@ -27,6 +27,7 @@ import torch
 
 from oracle import icecache as ic
 from ann_retrieval_amd import _lib as L
+from ann_retrieval_amd import synth
 
 BAND = ic.NEAR_TIE_REL
 ATOL = {"bf16": 2e-3, "f32": 1e-5}
@@ -199,3 +200,132 @@ def compare_selection(ref: ic.HeadIndex, q64, budget, beam, sel_g, trace_g):
 def attn_error(o_gpu: np.ndarray, o_ref: np.ndarray) -> float:
     den = np.abs(o_ref).max()
     return float(np.abs(o_gpu - o_ref).max() / den) if den > 0 else float(np.abs(o_gpu).max())
+
+
+# ---- whole-case helpers ----------------------------------------------------
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def build_case(H, N, d, dtype, C, seed, G=4, levels=3, plog2=4, capacity=None, budget=256, rotate=False):
+    from ann_retrieval_amd.api import IceIndex
+    say(f"build H={H} N={N} d={d} {dtype} C={C} seed={seed} G={G} L={levels} p=2^-{plog2}")
+    w, gen = synth.clustered_kv(H, N, d, C, dtype, seed, device="cpu", rotate=rotate)
+    ix = IceIndex(H, G, d, dtype, capacity or max(N, 1), levels, plog2, seed, max_budget=budget)
+    ix.ice_build(w.K.cuda(), w.V.cuda())
+    torch.cuda.synchronize()
+    return w, gen, ix
+
+
+def raw_rows(x: torch.Tensor) -> np.ndarray:
+    """Raw bits of rows, for bit-exact copies."""
+    return (x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)).cpu().numpy()
+
+
+def check_build(w, ix, heads, seed, levels, plog2, check_pool=True):
+    """Levels exact, lift close, parents within the band, layout exact (near-tie
+    slot swaps counted), page pool rows bit-exact. Returns oracle indexes."""
+    refs, ties, swaps = {}, 0, 0
+    for h in heads:
+        g = read_head(ix, h)
+        K64, V64 = to64(w.K[h]), to64(w.V[h])
+        ref = ic.build_head(K64, V64, h, seed, levels, plog2)
+        assert g.n == ref.n
+        assert np.array_equal(g.lev, ref.lev), "promotion levels differ"
+        assert g.L_top == ref.L_top and g.n_top == len(ref.top)
+        assert abs(g.stats["M2"] - ref.M2) <= 1e-12 * max(ref.M2, 1e-300)
+        if ref.n:
+            assert np.allclose(g.e, ref.e, rtol=2e-6, atol=2e-6 * math.sqrt(ref.M2) + 1e-30)
+        assert g.stats["overflow"] == 0
+        check_table_structure(g, ix.capacity)
+        replay, t = validate_parents(ref, g)
+        if t:
+            ref = oracle_replay(K64, V64, h, seed, levels, plog2, replay)
+        ties += t
+        s = compare_layout(ref, g, ix.capacity)
+        if s:
+            adopt_gpu_slots(ref, g)
+        swaps += s
+        if check_pool and ref.n:
+            P = len(g.tables[0]["pages"])
+            kp = ix.export(h, L.ICE_EXP_PAGE_K, 0, np_dtype=np.int16 if ix.dtype == "bf16" else np.int32)
+            vp = ix.export(h, L.ICE_EXP_PAGE_V, 0, np_dtype=np.int16 if ix.dtype == "bf16" else np.int32)
+            kp = kp.reshape(-1, 16, ix.d)[:P]
+            vp = vp.reshape(-1, 16, ix.d)[:P]
+            Kr, Vr = raw_rows(w.K[h]), raw_rows(w.V[h])
+            tok = g.tables[0]["tok"]
+            valid = tok >= 0
+            assert np.array_equal(kp[valid], Kr[tok[valid]]) and np.array_equal(vp[valid], Vr[tok[valid]])
+            assert not kp[~valid].any() and not vp[~valid].any()
+        refs[h] = ref
+    say(f"build parity ok: heads={len(heads)} parent near-ties={ties} slot swaps={swaps}")
+    return refs
+
+
+def run_decode(ix, Q, budget, beam, scale=None):
+    """One select + attend through the library; host copies of every output."""
+    say(f"decode budget={budget} beam={beam} Q={tuple(Q.shape)}")
+    Qd = Q if Q.is_cuda else Q.cuda()
+    sel, uni, nuni, tr = ix.ice_select(Qd, budget, beam, trace=True)
+    O, lse = ix.ice_attend(Qd, uni, nuni, scale)
+    torch.cuda.synchronize()
+    return dict(Q=Q.cpu(), budget=budget, beam=beam, scale=scale, sel=sel.cpu().numpy(), uni=uni.cpu().numpy(),
+                nuni=nuni.cpu().numpy(), tr=tr.cpu().numpy(), O=O.cpu().double().numpy(),
+                lse=lse.cpu().double().numpy())
+
+
+def check_decode(w, ix, refs, Q, budget, beam, scale=None):
+    out = run_decode(ix, Q, budget, beam, scale)
+    compare_decode(ix, refs, out)
+    return out["sel"], out["uni"], out["nuni"]
+
+
+def compare_decode(ix, refs, out):
+    """Selections of the heads in `refs` exact after tie-tolerant replay, the
+    union exact, attention within the dtype's tolerance."""
+    Q, budget, beam, scale = out["Q"], out["budget"], out["beam"], out["scale"]
+    sel, uni, nuni, tr, O, lse = out["sel"], out["uni"], out["nuni"], out["tr"], out["O"], out["lse"]
+    scale = 1.0 / math.sqrt(ix.d) if scale is None else scale
+    ties, worst = 0, 0.0
+    for h, ref in refs.items():
+        for g in range(ix.G):
+            q64 = to64(Q[h, g])
+            ties += compare_selection(ref, q64, budget, beam, sel[h, g], tr[h, g])
+        # union: ascending unique pages of the group, -1 padded
+        want = sorted(set(int(x) for x in sel[h].ravel() if x >= 0))
+        assert int(nuni[h]) == len(want)
+        assert list(uni[h, :len(want)]) == want and np.all(uni[h, len(want):] == -1)
+        for g in range(ix.G):
+            o_ref, lse_ref = ic.attend(ref, to64(Q[h, g]), want, scale)
+            if want:
+                err = attn_error(O[h, g], o_ref)
+                worst = max(worst, err)
+                assert err <= ATOL[ix.dtype], f"head {h} q {g}: attention error {err:.3g}"
+                assert abs(lse[h, g] - lse_ref) <= 1e-4 * max(1.0, abs(lse_ref))
+            else:
+                assert np.all(O[h, g] == 0) and lse[h, g] == -np.inf
+    say(f"decode parity ok: heads={len(refs)} selection near-ties={ties} worst attention error={worst:.3g}")
+    return ties, worst
+
+
+def replay_inserts(ref, g, k, v, h, seed, levels, plog2):
+    """Applies inserted tokens (rows of k, v) to the oracle index `ref`,
+    accepting the GPU's parent choice (from the GPU head `g`) only inside the
+    near-tie band of the oracle's nearest point at that moment."""
+    for j in range(k.shape[0]):
+        t = ref.n
+        lam = min(ref.L_top, int(ic.draw_levels(seed, h, t, 1, levels, plog2)[0]))
+        override = None
+        if lam < ref.L_top:
+            cand = np.nonzero(ref.lev >= lam + 1)[0]
+            x = np.concatenate([to64(k[j]), [ic.lift_one(to64(k[j]), ref.M2)[0]]])
+            jj, D1, D2 = ic.nearest(x[None, :], ic.lifted(ref.K[cand], ref.e[cand]))
+            gp = int(g.parent[lam][t])
+            if gp != int(cand[jj[0]]):
+                dg = float(((ic.lifted(ref.K[gp:gp + 1], ref.e[gp:gp + 1])[0] - x) ** 2).sum())
+                assert dg - D1[0] <= BAND * dg, f"insert parent of {t} outside the band"
+                override = gp
+        ic.insert(ref, to64(k[j]), to64(v[j]), parent_override=override)
+
+

@@ -22,93 +22,7 @@ if not torch.cuda.is_available():
 from ann_retrieval_amd.api import IceIndex  # noqa: E402
 
 
-def say(*a):
-    print("[case]", *a, flush=True)
-
-
-def build_case(H, N, d, dtype, C, seed, G=4, levels=3, plog2=4, capacity=None, budget=256, rotate=False):
-    say(f"build H={H} N={N} d={d} {dtype} C={C} seed={seed} G={G} L={levels} p=2^-{plog2}")
-    w, gen = synth.clustered_kv(H, N, d, C, dtype, seed, device="cpu", rotate=rotate)
-    ix = IceIndex(H, G, d, dtype, capacity or max(N, 1), levels, plog2, seed, max_budget=budget)
-    ix.ice_build(w.K.cuda(), w.V.cuda())
-    torch.cuda.synchronize()
-    return w, gen, ix
-
-
-def raw_rows(x: torch.Tensor) -> np.ndarray:
-    """Raw bits of rows, for bit-exact copies."""
-    return (x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)).cpu().numpy()
-
-
-def check_build(w, ix, heads, seed, levels, plog2, check_pool=True):
-    """Levels exact, lift close, parents within the band, layout exact (near-tie
-    slot swaps counted), page pool rows bit-exact. Returns oracle indexes."""
-    refs, ties, swaps = {}, 0, 0
-    for h in heads:
-        g = gs.read_head(ix, h)
-        K64, V64 = gs.to64(w.K[h]), gs.to64(w.V[h])
-        ref = ic.build_head(K64, V64, h, seed, levels, plog2)
-        assert g.n == ref.n
-        assert np.array_equal(g.lev, ref.lev), "promotion levels differ"
-        assert g.L_top == ref.L_top and g.n_top == len(ref.top)
-        assert abs(g.stats["M2"] - ref.M2) <= 1e-12 * max(ref.M2, 1e-300)
-        if ref.n:
-            assert np.allclose(g.e, ref.e, rtol=2e-6, atol=2e-6 * math.sqrt(ref.M2) + 1e-30)
-        assert g.stats["overflow"] == 0
-        gs.check_table_structure(g, ix.capacity)
-        replay, t = gs.validate_parents(ref, g)
-        if t:
-            ref = gs.oracle_replay(K64, V64, h, seed, levels, plog2, replay)
-        ties += t
-        s = gs.compare_layout(ref, g, ix.capacity)
-        if s:
-            gs.adopt_gpu_slots(ref, g)
-        swaps += s
-        if check_pool and ref.n:
-            P = len(g.tables[0]["pages"])
-            kp = ix.export(h, L.ICE_EXP_PAGE_K, 0, np_dtype=np.int16 if ix.dtype == "bf16" else np.int32)
-            vp = ix.export(h, L.ICE_EXP_PAGE_V, 0, np_dtype=np.int16 if ix.dtype == "bf16" else np.int32)
-            kp = kp.reshape(-1, 16, ix.d)[:P]
-            vp = vp.reshape(-1, 16, ix.d)[:P]
-            Kr, Vr = raw_rows(w.K[h]), raw_rows(w.V[h])
-            tok = g.tables[0]["tok"]
-            valid = tok >= 0
-            assert np.array_equal(kp[valid], Kr[tok[valid]]) and np.array_equal(vp[valid], Vr[tok[valid]])
-            assert not kp[~valid].any() and not vp[~valid].any()
-        refs[h] = ref
-    say(f"build parity ok: heads={len(heads)} parent near-ties={ties} slot swaps={swaps}")
-    return refs
-
-
-def check_decode(w, ix, refs, Q, budget, beam, scale=None):
-    say(f"decode budget={budget} beam={beam} Q={tuple(Q.shape)}")
-    Qd = Q.cuda()
-    sel, uni, nuni, tr = ix.ice_select(Qd, budget, beam, trace=True)
-    O, lse = ix.ice_attend(Qd, uni, nuni, scale)
-    torch.cuda.synchronize()
-    sel, uni, nuni, tr = sel.cpu().numpy(), uni.cpu().numpy(), nuni.cpu().numpy(), tr.cpu().numpy()
-    O, lse = O.cpu().double().numpy(), lse.cpu().double().numpy()
-    scale = 1.0 / math.sqrt(ix.d) if scale is None else scale
-    ties, worst = 0, 0.0
-    for h, ref in refs.items():
-        for g in range(ix.G):
-            q64 = gs.to64(Q[h, g])
-            ties += gs.compare_selection(ref, q64, budget, beam, sel[h, g], tr[h, g])
-        # union: ascending unique pages of the group, -1 padded
-        want = sorted(set(int(x) for x in sel[h].ravel() if x >= 0))
-        assert int(nuni[h]) == len(want)
-        assert list(uni[h, :len(want)]) == want and np.all(uni[h, len(want):] == -1)
-        for g in range(ix.G):
-            o_ref, lse_ref = ic.attend(ref, gs.to64(Q[h, g]), want, scale)
-            if want:
-                err = gs.attn_error(O[h, g], o_ref)
-                worst = max(worst, err)
-                assert err <= gs.ATOL[ix.dtype], f"head {h} q {g}: attention error {err:.3g}"
-                assert abs(lse[h, g] - lse_ref) <= 1e-4 * max(1.0, abs(lse_ref))
-            else:
-                assert np.all(O[h, g] == 0) and lse[h, g] == -np.inf
-    say(f"decode parity ok: selection near-ties={ties} worst attention error={worst:.3g}")
-    return sel, uni, nuni
+from gpu_support import build_case, check_build, check_decode, say  # noqa: E402
 
 
 # ---------------------------------------------------------------------------
@@ -151,6 +65,17 @@ def test_edge_builds(case):
     refs = check_build(w, ix, [0, 1], 3, c["levels"], c["plog2"])
     check_decode(w, ix, refs, synth.decode_queries(w, c["G"], gen), 64, 4)
     check_decode(w, ix, refs, synth.decode_queries(w, c["G"], gen), 32, 1)
+
+
+def test_max_group_beam_budget():
+    """The largest selection the boundary accepts: G = ICE_MAX_GROUP query heads,
+    beam = ICE_MAX_BEAM, budget = ICE_MAX_BEAM pages (lists kept in LDS, the
+    long union path)."""
+    budget = L.ICE_MAX_BEAM * L.ICE_PAGE_CAP
+    w, gen, ix = build_case(2, 12000, 128, "bf16", 64, 8, G=L.ICE_MAX_GROUP, budget=budget)
+    refs = check_build(w, ix, [0, 1], 8, 3, 4)
+    check_decode(w, ix, refs, synth.decode_queries(w, L.ICE_MAX_GROUP, gen), budget, L.ICE_MAX_BEAM)
+    check_decode(w, ix, refs, synth.decode_queries(w, L.ICE_MAX_GROUP, gen), 1024, 100)
 
 
 def test_identical_keys():
