@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "ice_launch.h"
 
@@ -349,8 +350,23 @@ int ice_export(const ice_index* idx, int32_t head, int32_t what, int32_t level, 
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ice_export sync");
   const char* src = static_cast<const char*>(idx->blob) + (int64_t)head * L.head_bytes + off;
-  e = hipMemcpy(dst, src, n, hipMemcpyDeviceToHost);
+  if (what != ICE_EXP_PAGE_V) {
+    e = hipMemcpy(dst, src, n, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "ice_export copy");
+    return ICE_OK;
+  }
+  // V pages are stored [page][slot group][dim][4 slots]; hand them out as
+  // [page][slot][dim] rows
+  std::vector<char> raw(n);
+  e = hipMemcpy(raw.data(), src, n, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "ice_export copy");
+  const int64_t elt = L.elt, D = L.d, pages = (int64_t)n / (ICE_PAGE_CAP * D * elt);
+  char* out = static_cast<char*>(dst);
+  for (int64_t pg = 0; pg < pages; ++pg)
+    for (int sl = 0; sl < ICE_PAGE_CAP; ++sl)
+      for (int64_t dd = 0; dd < D; ++dd)
+        memcpy(out + ((pg * ICE_PAGE_CAP + sl) * D + dd) * elt,
+                    raw.data() + (((pg * 4 + sl / 4) * D + dd) * 4 + sl % 4) * elt, elt);
   return ICE_OK;
 }
 

@@ -363,8 +363,8 @@ __global__ void k_pack_place(DevLayout L, WsLayout W, void* blob, void* ws, int 
 // Rows of the page table into its key (and, at level 0, value) pool; empty
 // slots are zero. Upper tables also keep each point's lift coordinate.
 template <int D, class T>
-__global__ __launch_bounds__(256) void k_copy_pages(DevLayout L, const T* K, const T* V, int64_t hstride,
-                                                    void* blob, int level) {
+__global__ __launch_bounds__(256) void k_copy_pages(DevLayout L, const T* K, int64_t hstride, void* blob,
+                                                    int level) {
   using G = RowGeo<D, T>;
   const int h = blockIdx.y;
   void* hb = head_base(blob, L, h);
@@ -375,25 +375,54 @@ __global__ __launch_bounds__(256) void k_copy_pages(DevLayout L, const T* K, con
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[level]);
   T* pk = at<T>(hb, L.off_pgK[level]);
-  T* pv = level == 0 ? at<T>(hb, L.off_pgV) : nullptr;
   float* pe = level == 0 ? nullptr : at<float>(hb, L.off_pgE[level]);
   const float* e = at<float>(hb, L.off_e);
   const T* Kh = K + (int64_t)h * hstride;
-  const T* Vh = V + (int64_t)h * hstride;
   const int nrows = n_pages * ICE_PAGE_CAP;
   for (int r0 = (blockIdx.x * 4 + wave) * G::RPP; r0 < nrows; r0 += gridDim.x * 4 * G::RPP) {
     const int r = r0 + lane / G::LPR;
     if (r >= nrows) continue;
     const int tok = pg_tok[r];
     const int64_t so = (lane % G::LPR) * 16;
-    V4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-    if (tok >= 0) {
-      kv = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Kh + (int64_t)tok * D) + so);
-      if (pv) vv = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Vh + (int64_t)tok * D) + so);
-    }
+    V4 kv = {0, 0, 0, 0};
+    if (tok >= 0) kv = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Kh + (int64_t)tok * D) + so);
     *reinterpret_cast<V4*>(reinterpret_cast<char*>(pk + (int64_t)r * D) + so) = kv;
-    if (pv) *reinterpret_cast<V4*>(reinterpret_cast<char*>(pv + (int64_t)r * D) + so) = vv;
     if (pe && (lane % G::LPR) == 0) pe[r] = tok >= 0 ? e[tok] : 0.0f;
+  }
+}
+
+// Level-0 V pages in the layout attention reads: [page][slot group g][dim][4
+// slots], g = slot / 4, so each group of 4 slots is one contiguous run (the
+// groups past a page's count are never read) and the 4 values of one
+// dimension sit together. One wave per page; empty slots are zero.
+template <int D, class T>
+__global__ __launch_bounds__(256) void k_copy_vt(DevLayout L, const T* V, int64_t hstride, void* blob) {
+  constexpr int DPL = D / ICE_WAVE;      // dimensions per lane
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
+  const int n_pages = hdr->n_pages[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[0]);
+  T* pv = at<T>(hb, L.off_pgV);
+  const T* Vh = V + (int64_t)h * hstride;
+  for (int pg = blockIdx.x * 4 + wave; pg < n_pages; pg += gridDim.x * 4) {
+    const int my_tok = lane < ICE_PAGE_CAP ? pg_tok[(int64_t)pg * ICE_PAGE_CAP + lane] : -1;
+    T val[ICE_PAGE_CAP][DPL];
+#pragma unroll
+    for (int sl = 0; sl < ICE_PAGE_CAP; ++sl) {
+      const int tok = __shfl(my_tok, sl, 64);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) val[sl][j] = tok >= 0 ? Vh[(int64_t)tok * D + DPL * lane + j] : T(0);
+    }
+#pragma unroll
+    for (int g = 0; g < ICE_PAGE_CAP / 4; ++g) {
+      T* dst = pv + (((int64_t)pg * 4 + g) * D + DPL * lane) * 4;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[4 * j + i] = val[4 * g + i][j];
+    }
   }
 }
 
@@ -473,8 +502,12 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
       ICE_CHECK();
       using G = RowGeo<D, T>;
       k_copy_pages<D, T><<<dim3(blocks_for((int64_t)L.pcap[level] * ICE_PAGE_CAP, 4 * G::RPP * 8), H), 256, 0,
-                           s>>>(L, K, V, hstride, blob, level);
+                           s>>>(L, K, hstride, blob, level);
       ICE_CHECK();
+      if (level == 0) {
+        k_copy_vt<D, T><<<dim3(blocks_for(L.pcap[0], 4 * 4), H), 256, 0, s>>>(L, V, hstride, blob);
+        ICE_CHECK();
+      }
     }
   }
   if (L.L >= 2 && n > 0) {

@@ -235,9 +235,12 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
       const int64_t base = (int64_t)plc.page[l] * ICE_PAGE_CAP;
       for (int i = tid + D; i < ICE_PAGE_CAP * D; i += 256) {
         at<T>(hb, L.off_pgK[l])[base * D + i] = T(0);
-        if (l == 0) at<T>(hb, L.off_pgV)[base * D + i] = T(0);
-        else if (i % D == 0) at<float>(hb, L.off_pgE[l])[base + i / D] = 0.0f;
+        if (l != 0 && i % D == 0) at<float>(hb, L.off_pgE[l])[base + i / D] = 0.0f;
       }
+      // V pages ([slot group][dim][4 slots]): every element but slot 0's
+      if (l == 0)
+        for (int i = tid; i < ICE_PAGE_CAP * D; i += 256)
+          if (i % 4 != 0 || i >= 4 * D) at<T>(hb, L.off_pgV)[base * D + i] = T(0);
     }
     // rows into the pools
     for (int i = tid; i < D; i += 256) {
@@ -245,7 +248,8 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
       if (plc.page[0] >= 0) {
         const int64_t row = (int64_t)plc.page[0] * ICE_PAGE_CAP + plc.slot[0];
         at<T>(hb, L.off_pgK[0])[row * D + i] = kv;
-        at<T>(hb, L.off_pgV)[row * D + i] = vrow[i];
+        const int sl = plc.slot[0];
+        at<T>(hb, L.off_pgV)[(((int64_t)plc.page[0] * 4 + sl / 4) * D + i) * 4 + sl % 4] = vrow[i];
       }
       for (int l = 1; l < Ltop; ++l) {
         if (plc.page[l] < 0) continue;

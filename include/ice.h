@@ -150,7 +150,8 @@ int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const in
 #define ICE_EXP_OWNER_TAIL 8   /* int32 [capacity+1] last page per owner (+ root), -1      */
 #define ICE_EXP_TOP        9   /* int32 [top capacity] top-level points in order           */
 #define ICE_EXP_PAGE_K     10  /* dtype [pages][16][d] page-pool keys (level 0) / copies   */
-#define ICE_EXP_PAGE_V     11  /* dtype [pages][16][d] page-pool values (level 0 only)     */
+#define ICE_EXP_PAGE_V     11  /* dtype [pages][16][d] page-pool values (level 0 only; the
+                                  device stores each 4-slot group dimension-major) */
 #define ICE_EXP_HEADER     12  /* ice_head_stats                                           */
 #define ICE_EXP_OWNER_RUN  13  /* int32 [capacity+1] pages of the owner's contiguous run   */
 #define ICE_EXP_OWNER_COUNT 14 /* int32 [capacity+1] members of the owner                  */
