@@ -46,6 +46,8 @@ _SIGNATURES = {
                                   c_void_p, c_size, c_void_p]),
     "ice_attend": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_f32, c_void_p, c_void_p,
                                   c_void_p, c_size, c_void_p]),
+    "ice_decode": (ctypes.c_int, [c_void_p, c_void_p, c_i32, c_i32, c_void_p, c_void_p, c_void_p, c_f32, c_void_p,
+                                  c_void_p, c_void_p, c_size, c_void_p]),
     "ice_export_bytes": (c_size, [c_void_p, c_i32, c_i32]),
     "ice_export": (ctypes.c_int, [c_void_p, c_i32, c_i32, c_i32, c_void_p, c_size, c_void_p]),
     "ice_n_tokens": (c_i32, [c_void_p]),

@@ -129,6 +129,22 @@ class IceIndex:
                                   _ptr(L), _ptr(self.ws), self.ws_bytes, _stream_ptr(self.device)), "ice_attend")
         return O, L
 
+    def ice_decode(self, Q: torch.Tensor, budget_tokens: int, beam: int | None = None, scale: float | None = None):
+        """One decode step (select + attend): returns (sel, uni, n_uni, O, lse)."""
+        self._check_q(Q)
+        k = budget_tokens // _lib.ICE_PAGE_CAP
+        beam = k if beam is None else beam
+        scale = 1.0 / math.sqrt(self.d) if scale is None else scale
+        sel = torch.empty(self.H, self.G, k, dtype=torch.int32, device=self.device)
+        uni = torch.empty(self.H, self.G * k, dtype=torch.int32, device=self.device)
+        n_uni = torch.empty(self.H, dtype=torch.int32, device=self.device)
+        O = torch.empty(self.H, self.G, self.d, dtype=torch.float32, device=self.device)
+        L = torch.empty(self.H, self.G, dtype=torch.float32, device=self.device)
+        check(self.lib.ice_decode(self.handle, _ptr(Q), budget_tokens, beam, _ptr(sel), _ptr(uni), _ptr(n_uni),
+                                  scale, _ptr(O), _ptr(L), _ptr(self.ws), self.ws_bytes, _stream_ptr(self.device)),
+              "ice_decode")
+        return sel, uni, n_uni, O, L
+
     def _check_q(self, Q: torch.Tensor):
         if Q.device != self.device or Q.dtype != self.tdtype or tuple(Q.shape) != (self.H, self.G, self.d) \
                 or not Q.is_contiguous():

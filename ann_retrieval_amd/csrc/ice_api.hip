@@ -294,6 +294,31 @@ int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const in
   if (e != hipSuccess) return hip_fail(e, "ice_attend launch");
   return ICE_OK;
 }
+int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32_t beam, int32_t* sel, int32_t* uni,
+               int32_t* n_uni, float scale, float* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (!idx->built) return fail(ICE_ERR_STATE, "decode before build");
+  int rc = check_budget(idx, budget_tokens);
+  if (rc) return rc;
+  if (beam < 1 || beam > ICE_MAX_BEAM) return fail(ICE_ERR_ARG, "beam must be in [1, %d]", ICE_MAX_BEAM);
+  if (!Q || !sel || !uni || !n_uni || !O) return fail(ICE_ERR_ARG, "Q, sel, uni, n_uni or O is null");
+  if (!aligned16(Q)) return fail(ICE_ERR_ARG, "Q must be 16-byte aligned");
+  const int uni_stride = idx->p.group * (budget_tokens / ICE_PAGE_CAP);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (decode_fused(idx->L, budget_tokens, beam)) {
+    hipError_t e = launch_decode(idx->L, idx->blob, Q, budget_tokens, beam, sel, uni, n_uni, scale, O, lse, s);
+    if (e != hipSuccess) return hip_fail(e, "ice_decode launch");
+    return ICE_OK;
+  }
+  const int64_t need = attend_ws_bytes(idx->L, uni_stride);
+  if (need > 0 && (!ws || ws_bytes < (size_t)need))
+    return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, attend needs %lld", ws_bytes, (long long)need);
+  hipError_t e = launch_select(idx->L, idx->blob, Q, budget_tokens, beam, sel, uni, n_uni, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "ice_decode select launch");
+  e = launch_attend(idx->L, idx->blob, Q, uni, n_uni, uni_stride, scale, O, lse, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "ice_decode attend launch");
+  return ICE_OK;
+}
 
 size_t ice_export_bytes(const ice_index* idx, int32_t what, int32_t level) {
   if (!idx) return 0;

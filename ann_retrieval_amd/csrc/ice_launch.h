@@ -17,6 +17,10 @@ hipError_t launch_insert(const DevLayout& L, void* blob, const void* k_new, cons
 // k_select.hip
 hipError_t launch_select(const DevLayout& L, const void* blob, const void* Q, int budget, int beam,
                          int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace, hipStream_t s);
+// true if select + attend run as one fused kernel (bf16, lists of at most 64)
+bool decode_fused(const DevLayout& L, int budget, int beam);
+hipError_t launch_decode(const DevLayout& L, const void* blob, const void* Q, int budget, int beam, int32_t* sel,
+                         int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse, hipStream_t s);
 // k_attend.hip
 int attend_splits(int uni_stride);
 hipError_t launch_attend(const DevLayout& L, const void* blob, const void* Q, const int32_t* uni,

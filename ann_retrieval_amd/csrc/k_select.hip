@@ -23,6 +23,7 @@
 // use a slower LDS list instead. The block ends with the union of its query
 // heads' pages, ascending.
 #include "ice_launch.h"
+#include "attend_mfma.h"
 
 #include <type_traits>
 
@@ -374,14 +375,16 @@ __device__ inline uint64_t chunk_keys(const Quarter<D, T>& qs, const bool (&ok)[
   return grp == 0 ? x0 : grp == 1 ? x1 : grp == 2 ? x2 : x3;
 }
 
+// Selection of head h by the whole block; returns the size of the group's
+// union (in every thread). uni_lds (nullable, LDS outside the selection's
+// area) receives a copy of the union. Ends with a block barrier, after which
+// the selection's LDS area is free.
 template <int D, class T, bool BIG>
-__global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, const T* Q, int budget, int beam,
-                                                 int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace) {
+__device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int budget, int beam, int32_t* sel,
+                           int32_t* uni, int32_t* n_uni, int32_t* trace, char* smem, int h, int32_t* uni_lds) {
   using QG = Quarter<D, T>;
   using Top = std::conditional_t<BIG, LdsTop, RegTop>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int G = L.G, W = waves_per_query(G);
-  const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = wv / W, j = wv % W;      // query head, wave within the query
   const bool lead = j == g % W;          // merges the query's lists (leads sit on different SIMDs)
@@ -601,25 +604,34 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
   const int tot = G * kpg;
   int32_t* urow = uni + (int64_t)h * tot;
   if (tot <= 64) {
-    if (wv != 0) return;
-    int v = lane < tot ? sel_all[lane] : INT_MAX;
-    if (v < 0) v = INT_MAX;
+    if (wv == 0) {
+      int v = lane < tot ? sel_all[lane] : INT_MAX;
+      if (v < 0) v = INT_MAX;
 #pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
+      for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        const int y = __shfl_xor(v, jj, 64);
-        v = (((lane & k) == 0) == ((lane & jj) == 0)) ? min(v, y) : max(v, y);
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+          const int y = __shfl_xor(v, jj, 64);
+          v = (((lane & k) == 0) == ((lane & jj) == 0)) ? min(v, y) : max(v, y);
+        }
+      }
+      const int prev = __shfl_up(v, 1, 64);
+      const bool keep = v != INT_MAX && (lane == 0 || v != prev);
+      const uint64_t m = __ballot(keep);
+      const int n = __popcll(m);
+      if (keep) {
+        const int pos = __popcll(m & ((1ull << lane) - 1ull));
+        urow[pos] = v;
+        if (uni_lds) uni_lds[pos] = v;
+      }
+      if (lane >= n && lane < tot) urow[lane] = -1;
+      if (lane == 0) {
+        n_uni[h] = n;
+        wn[0] = n;
       }
     }
-    const int prev = __shfl_up(v, 1, 64);
-    const bool keep = v != INT_MAX && (lane == 0 || v != prev);
-    const uint64_t m = __ballot(keep);
-    const int n = __popcll(m);
-    if (keep) urow[__popcll(m & ((1ull << lane) - 1ull))] = v;
-    if (lane >= n && lane < tot) urow[lane] = -1;
-    if (lane == 0) n_uni[h] = n;
-    return;
+    __syncthreads();
+    return wn[0];
   }
   // long selections: bitonic sort of the padded list in LDS (empty = INT_MAX),
   // then keep the first of each run of equal ids
@@ -658,12 +670,53 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
       before += w2 < wv ? wcount[w2] : 0;
       all += wcount[w2];
     }
-    if (keep) urow[before + __popcll(m & ((1ull << lane) - 1ull))] = v;
+    if (keep) {
+      const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
+      urow[pos] = v;
+      if (uni_lds) uni_lds[pos] = v;
+    }
     base = all;
     __syncthreads();
   }
   for (int i = base + tid; i < tot; i += nthr) urow[i] = -1;
   if (tid == 0) n_uni[h] = base;
+  return base;
+}
+
+template <int D, class T, bool BIG>
+__global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, const T* Q, int budget, int beam,
+                                                 int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  select_head<D, T, BIG>(L, blob, Q, budget, beam, sel, uni, n_uni, trace, smem, blockIdx.x, nullptr);
+}
+
+// ---- the fused decode step: selection, then attention over the union -------
+// LDS: the selection's area, then the union copy; attention's partials reuse
+// the selection's area once the selection is done.
+struct DecLds {
+  int off_uni, total;
+};
+__host__ __device__ inline DecLds dec_lds(int G, int beam, int kpg, int nw, int D) {
+  const SelLds S = sel_lds(G, max(beam, kpg), kpg, false);
+  const int part = mfma_attend::part_floats(nw, G, D) * 4;
+  DecLds d;
+  d.off_uni = ((S.total > part ? S.total : part) + 15) & ~15;
+  d.total = d.off_uni + G * kpg * 4;
+  return d;
+}
+
+template <int D>
+__global__ __launch_bounds__(1024) void k_decode(DevLayout L, const void* blob, const uint16_t* Q, int budget,
+                                                 int beam, int32_t* sel, int32_t* uni, int32_t* n_uni, float scale,
+                                                 float* O, float* lse) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int h = blockIdx.x, G = L.G, nw = blockDim.x >> 6;
+  const DecLds DL = dec_lds(G, beam, budget / ICE_PAGE_CAP, nw, D);
+  int32_t* uni_lds = reinterpret_cast<int32_t*>(smem + DL.off_uni);
+  const int nu = select_head<D, uint16_t, false>(L, blob, Q, budget, beam, sel, uni, n_uni, nullptr, smem, h, uni_lds);
+  mfma_attend::attend_head<D, false>(L, head_base(blob, L, h), Q + (int64_t)h * G * D, G, uni_lds, nu, scale,
+                              O + (int64_t)h * G * D, lse ? lse + (int64_t)h * G : nullptr,
+                              reinterpret_cast<float*>(smem), nw);
 }
 
 template <int D, class T>
@@ -679,7 +732,29 @@ void launch_typed(const DevLayout& L, const void* blob, const void* Qv, int budg
   else k_select<D, T, false><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, uni, n_uni, trace);
 }
 
+template <int D>
+void launch_decode_typed(const DevLayout& L, const void* blob, const void* Qv, int budget, int beam, int32_t* sel,
+                         int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse, hipStream_t s) {
+  const int kpg = budget / ICE_PAGE_CAP;
+  const int nw = waves_per_query(L.G) * L.G;
+  const DecLds DL = dec_lds(L.G, beam, kpg, nw, D);
+  k_decode<D><<<dim3((unsigned)L.H), dim3(64 * nw), (size_t)DL.total, s>>>(
+      L, blob, static_cast<const uint16_t*>(Qv), budget, beam, sel, uni, n_uni, scale, O, lse);
+}
+
 }  // namespace
+
+bool decode_fused(const DevLayout& L, int budget, int beam) {
+  const int kpg = budget / ICE_PAGE_CAP;
+  return L.dtype == ICE_BF16 && (beam > kpg ? beam : kpg) <= 64;
+}
+
+hipError_t launch_decode(const DevLayout& L, const void* blob, const void* Q, int budget, int beam, int32_t* sel,
+                         int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse, hipStream_t s) {
+  if (L.d == 128) launch_decode_typed<128>(L, blob, Q, budget, beam, sel, uni, n_uni, scale, O, lse, s);
+  else launch_decode_typed<64>(L, blob, Q, budget, beam, sel, uni, n_uni, scale, O, lse, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const DevLayout& L, const void* blob, const void* Q, int budget, int beam,
                          int32_t* sel, int32_t* uni, int32_t* n_uni, int32_t* trace, hipStream_t s) {

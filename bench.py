@@ -3,10 +3,11 @@
 Workload (default): a 36,000-token context for 32 layers x 8 KV heads (256
 independent indexes), 4 query heads per KV head, d = 128, bf16 K/V, keys from
 512-component Gaussian mixtures per head with a random rotation per head.
-A timed step is one decode step of every layer: ``ice_select`` (beam descent,
-top-k pages, GQA union) + ``ice_attend`` (page gather + sparse attention)
-for all 256 heads at a 256-token budget. The index build (keys/s) and the
-insert of one token per head are timed separately and reported beside it.
+A timed step is one decode step of every layer: ``ice_decode`` (beam descent,
+top-k pages, GQA union, page gather + sparse attention; one fused kernel) for
+all 256 heads at a 256-token budget. The separate ``ice_select`` and
+``ice_attend`` kernels, the index build (keys/s) and the insert of one token
+per head are timed separately and reported beside it.
 
 Prints ONE JSON line (see the fields below). ``--gpus N`` with N > 1 exits:
 the library runs on one GPU and no multi-GPU figure is produced.
@@ -71,8 +72,9 @@ def parse():
 # Sources each kernel is built from: a recorded counter reading is valid only
 # while these are unchanged.
 KERNEL_SOURCES = {
-    "k_select": ["k_select.hip", "ice_common.h", "ice_launch.h"],
-    "k_attend": ["k_attend.hip", "ice_common.h", "ice_launch.h"],
+    "k_decode": ["k_select.hip", "attend_mfma.h", "ice_common.h", "ice_launch.h"],
+    "k_select": ["k_select.hip", "attend_mfma.h", "ice_common.h", "ice_launch.h"],
+    "k_attend": ["k_attend.hip", "attend_mfma.h", "ice_common.h", "ice_launch.h"],
 }
 CSRC = os.path.join(ROOT, "ann_retrieval_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -151,13 +153,14 @@ def summarize(paths, command, copy_mib, workload):
 
 def algorithmic_bytes(ix, trace, uni_n, n_uni, d, elt, G):
     """Bytes the method itself must move for one decode step, from the run's
-    own selections: per head the top-level keys, the keys of the unique
-    level-1 candidates, the keys of the valid rows of the unique candidate
-    pages (scoring), their list entries, plus Q in; for attend the K and V
-    rows of the union pages, Q in and O out."""
-    from ann_retrieval_amd import _lib as L
+    own selections. Per head: select reads the top-level keys, the keys of
+    the unique level-1 candidates, the keys of the valid rows of the unique
+    candidate pages and their list entries; attend reads the K and V rows of
+    the union pages. The fused step reads every key once (the union pages'
+    keys are among the candidates), then the union's V rows. Q in and O, lse
+    out are counted where they move."""
     H = trace.shape[0]
-    sel_b = att_b = 0
+    sel_b = kv_b = v_b = ent_b = 0
     for h in range(H):
         m = ix.meta[h]
         Lt = m["L_top"]
@@ -179,9 +182,13 @@ def algorithmic_bytes(ix, trace, uni_n, n_uni, d, elt, G):
             pages, page_rows = m["P0"], m["n"]
         sel_b += (rows_top + c1_rows + page_rows) * d * elt + blocks * (16 * 4 + 8) + pages * 8
         u = uni_n[h][: n_uni[h]]
-        att_b += 2 * int(m["cnt0"][u].sum()) * d * elt + len(u) * 8
+        rows = int(m["cnt0"][u].sum())
+        kv_b += 2 * rows * d * elt
+        v_b += rows * d * elt
+        ent_b += len(u) * 8
     q = H * G * d * elt
-    return sel_b + q, att_b + q + H * G * d * 4 + H * G * 4
+    out = H * G * d * 4 + H * G * 4
+    return dict(select=sel_b + q, attend=kv_b + ent_b + q + out, decode=sel_b + v_b + ent_b + q + out)
 
 
 def head_meta(ix, H, cap):
@@ -291,27 +298,29 @@ def main():
         k = budget // 16
         beam = k
         for s in range(a.warmup):
+            ix.ice_decode(Qs[s], budget, beam)
             _, uni, nuni = ix.ice_select(Qs[s], budget, beam)
             ix.ice_attend(Qs[s], uni, nuni)
         torch.cuda.synchronize()
-        # whole steps: select + attend back to back, no events in between; a
+        # whole steps: one ice_decode per step (the fused select + attend); a
         # short spin on the stream first lets the host queue the timed steps
         # ahead of the GPU, so the events bracket GPU work, not launch gaps
         t0 = time.perf_counter()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda._sleep(int(5e7))
         g0.record()
-        unis = []
         for s in range(a.steps):
-            q = Qs[a.warmup + s]
-            _, uni, nuni = ix.ice_select(q, budget, beam)
-            ix.ice_attend(q, uni, nuni)
-            unis.append((uni, nuni))
+            ix.ice_decode(Qs[a.warmup + s], budget, beam)
         g1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms_step = g0.elapsed_time(g1) / a.steps
-        # each kernel on its own: the same launches back to back between two events
+        # the separate calls, each kernel on its own: the same launches back to
+        # back between two events
+        unis = []
+        for s in range(a.steps):
+            _, uni, nuni = ix.ice_select(Qs[a.warmup + s], budget, beam)
+            unis.append((uni, nuni))
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         torch.cuda._sleep(int(5e7))
         e[0].record()
@@ -328,21 +337,21 @@ def main():
         att_ms = e[2].elapsed_time(e[3]) / a.steps
         # algorithmic bytes from the same selections (replayed with a trace)
         nb = min(a.steps, 4)
-        sb = ab = 0
+        byt = dict(select=0.0, attend=0.0, decode=0.0)
         for s in range(nb):
             q = Qs[a.warmup + s]
             _, uni, nuni, tr = ix.ice_select(q, budget, beam, trace=True)
-            b1, b2 = algorithmic_bytes(ix, tr.cpu().numpy(), uni.cpu().numpy(), nuni.cpu().numpy(), d, elt, G)
-            sb += b1
-            ab += b2
-        sb /= nb
-        ab /= nb
+            bb = algorithmic_bytes(ix, tr.cpu().numpy(), uni.cpu().numpy(), nuni.cpu().numpy(), d, elt, G)
+            for k2 in byt:
+                byt[k2] += bb[k2] / nb
+        sb, ab, db = byt["select"], byt["attend"], byt["decode"]
         results[budget] = dict(ms_per_step=ms_step, steps_per_s=1000.0 / ms_step, wall_s=wall,
+                               decode_bytes=db, decode_gbs=db / ms_step / 1e6,
                                select_ms=sel_ms, attend_ms=att_ms, select_bytes=sb, attend_bytes=ab,
                                select_gbs=sb / sel_ms / 1e6, attend_gbs=ab / att_ms / 1e6)
-        print(f"[bench] T={budget}: {ms_step*1000:.1f} us/step select {sel_ms*1000:.1f} us "
-              f"({sb/sel_ms/1e6:.0f} GB/s) attend {att_ms*1000:.1f} us ({ab/att_ms/1e6:.0f} GB/s)",
-              file=sys.stderr, flush=True)
+        print(f"[bench] T={budget}: {ms_step*1000:.1f} us/step fused ({db/ms_step/1e6:.0f} GB/s); separately "
+              f"select {sel_ms*1000:.1f} us ({sb/sel_ms/1e6:.0f} GB/s) attend {att_ms*1000:.1f} us "
+              f"({ab/att_ms/1e6:.0f} GB/s)", file=sys.stderr, flush=True)
 
     # ---- insert: one token per head per step
     knew = [synth.new_tokens(w, gen, device=dev) for _ in range(n_ins)]
@@ -356,9 +365,10 @@ def main():
     insert_ms = e0.elapsed_time(e1) / n_ins
 
     head = results[a.budget]
-    dom = "select" if head["select_ms"] >= head["attend_ms"] else "attend"
-    dom_bytes = head[f"{dom}_bytes"]
-    dom_ms = head[f"{dom}_ms"]
+    # the step is one kernel (the fused decode); its launches run back to back
+    # between the step events, so the step time is its average launch time
+    dom_bytes = head["decode_bytes"]
+    dom_ms = head["ms_per_step"]
     achieved = dom_bytes / dom_ms / 1e6
     out = {
         "metric": METRIC,
@@ -375,9 +385,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "heads": H, "group": G, "context": N, "d": d, "budget_tokens": a.budget,
                    "beam": a.budget // 16, "levels": 3, "promote": "1/16", "page": 16},
-        "roofline": {"bound": "hbm", "kernel": f"k_{dom}", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic(f"k_{dom}", a.workload) if a.budget == 256 else None,
+                     "traffic": recorded_traffic("k_decode", a.workload) if a.budget == 256 else None,
                      "bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
         "index_keys_per_s": H * N / (build_ms / 1000.0),
         "build_ms": build_ms,

@@ -136,6 +136,18 @@ int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const in
                int32_t uni_stride, float scale, float* O, float* lse,
                void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step of the hot path (the framework's steps 2 and 3 together):
+ * ice_select (without trace) followed by ice_attend over its union, with
+ * uni_stride = G * budget_tokens / 16. The outputs and argument rules are
+ * those of the two calls; the results equal theirs up to the order of the
+ * fp32 sums in the attention. For bf16 keys with beam and budget/16 at most
+ * 64 it runs as one kernel per step (each head selects, then attends its own
+ * union, with no pass through memory in between); otherwise it enqueues the
+ * two calls' kernels. */
+int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32_t beam,
+               int32_t* sel, int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse,
+               void* ws, size_t ws_bytes, void* stream);
+
 /* ---- inspection (synchronise the stream; for parity tests and stats) ---- */
 
 /* Arrays of one head that ice_export copies to host memory. */

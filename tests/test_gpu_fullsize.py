@@ -61,6 +61,14 @@ def test_ctx36k_sampled_heads():
         out = run_decode(ix, Q, budget, budget // 16)
         compare_decode(ix, refs, out)
         check_all_heads(ix, out)
+        # the fused decode step, in the benchmark's launch configuration
+        s1, u1, n1, O1, l1 = ix.ice_decode(Q, budget, budget // 16)
+        torch.cuda.synchronize()
+        assert np.array_equal(s1.cpu().numpy(), out["sel"]) and np.array_equal(u1.cpu().numpy(), out["uni"])
+        O1 = O1.cpu().double().numpy()
+        den = np.abs(out["O"]).max(axis=-1, keepdims=True)
+        assert float((np.abs(O1 - out["O"]) / np.maximum(den, 1e-30)).max()) <= 1e-5
+        say(f"ctx36k budget {budget}: fused decode equals select + attend")
 
 
 def test_llama_layer_decode_with_inserts():

@@ -78,6 +78,34 @@ def test_max_group_beam_budget():
     check_decode(w, ix, refs, synth.decode_queries(w, L.ICE_MAX_GROUP, gen), 1024, 100)
 
 
+@pytest.mark.parametrize("case", [
+    dict(dtype="bf16", G=4, budget=256, beam=16, d=128),
+    dict(dtype="bf16", G=4, budget=64, beam=4, d=128),
+    dict(dtype="bf16", G=8, budget=128, beam=8, d=64),
+    dict(dtype="bf16", G=2, budget=256, beam=100, d=128),     # long lists: the two-kernel path
+    dict(dtype="f32", G=4, budget=128, beam=8, d=128),        # fp32: the two-kernel path
+], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_decode_matches_select_then_attend(case):
+    """ice_decode equals ice_select followed by ice_attend: selections and
+    unions exactly, attention up to the order of fp32 sums; and the oracle."""
+    w, gen, ix = build_case(3, 4000, case["d"], case["dtype"], 40, 11, G=case["G"], budget=case["budget"])
+    refs = check_build(w, ix, [0, 2], 11, 3, 4)
+    for _ in range(2):
+        Q = synth.decode_queries(w, case["G"], gen).cuda()
+        say(f"decode vs select+attend {case}")
+        s1, u1, n1, O1, l1 = ix.ice_decode(Q, case["budget"], case["beam"])
+        s2, u2, n2 = ix.ice_select(Q, case["budget"], case["beam"])
+        O2, l2 = ix.ice_attend(Q, u2, n2)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, s2) and torch.equal(u1, u2) and torch.equal(n1, n2)
+        den = O2.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
+        assert float(((O1 - O2).abs() / den).max()) <= 1e-5
+        assert float((l1 - l2).abs().max()) <= 1e-5 * max(1.0, float(l2.abs().max()))
+        out = gs.run_decode(ix, Q, case["budget"], case["beam"])
+        out["O"], out["lse"] = O1.cpu().double().numpy(), l1.cpu().double().numpy()
+        gs.compare_decode(ix, refs, out)
+
+
 def test_identical_keys():
     say("build identical keys H=1 N=200 d=128 bf16")
     K = torch.ones(1, 200, 128).to(torch.bfloat16)
