@@ -32,7 +32,7 @@ class IceParams(ctypes.Structure):
 class IceHeadStats(ctypes.Structure):
     _fields_ = [("n_tokens", c_i32), ("top_level", c_i32), ("n_top", c_i32), ("n_pages", c_i32 * ICE_MAX_LEVELS),
                 ("clamps", c_i32), ("splits", c_i32), ("near_ties", c_i32), ("overflow", c_i32),
-                ("reserved0", c_i32), ("reserved1", c_i32), ("M2", ctypes.c_double)]
+                ("sync_timeouts", c_i32), ("reserved1", c_i32), ("M2", ctypes.c_double)]
 
 
 _SIGNATURES = {

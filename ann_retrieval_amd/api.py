@@ -166,4 +166,5 @@ class IceIndex:
         check(self.lib.ice_export(self.handle, head, _lib.ICE_EXP_HEADER, 0, ctypes.byref(st), ctypes.sizeof(st),
                                   _stream_ptr(self.device)), "ice_export")
         return dict(n_tokens=st.n_tokens, top_level=st.top_level, n_top=st.n_top, n_pages=list(st.n_pages),
-                    clamps=st.clamps, splits=st.splits, near_ties=st.near_ties, overflow=st.overflow, M2=st.M2)
+                    clamps=st.clamps, splits=st.splits, near_ties=st.near_ties, overflow=st.overflow,
+                    sync_timeouts=st.sync_timeouts, M2=st.M2)

@@ -24,7 +24,7 @@ struct Hdr {
   int32_t splits;
   int32_t near_ties;
   int32_t overflow;        // page table full (ruled out within capacity)
-  int32_t reserved0;
+  int32_t sync_timeouts;
   int32_t reserved1;
   double M2;
 };

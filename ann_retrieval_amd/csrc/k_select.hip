@@ -173,7 +173,7 @@ struct SelLds {
   int off_query;      // LDS lists: [G][lcap] u64 merged lists
   int off_meta;       // [G][meta_ints] owner tables
   int meta_ints;
-  int off_misc;       // wn[kMaxWaves], qn[ICE_MAX_GROUP], qp[ICE_MAX_GROUP]
+  int off_misc;       // wn[kMaxWaves], qn[ICE_MAX_GROUP], qp[ICE_MAX_GROUP], qbar[ICE_MAX_GROUP]
   int off_sel;        // [G * kpg rounded up to a power of two] i32: selections, then the union's sort
   int total;
 };
@@ -187,7 +187,7 @@ __host__ __device__ inline SelLds sel_lds(int G, int lcap, int kpg, bool big) {
   s.off_meta = s.off_query + (big ? G * lcap * 8 : 0);
   s.meta_ints = 3 * lcap + 2;
   s.off_misc = s.off_meta + G * s.meta_ints * 4;
-  s.off_sel = s.off_misc + (kMaxWaves + 2 * ICE_MAX_GROUP) * 4;
+  s.off_sel = s.off_misc + (kMaxWaves + 3 * ICE_MAX_GROUP) * 4;
   s.total = s.off_sel + union_pad(G * kpg) * 4;
   return s;
 }
@@ -236,6 +236,31 @@ __device__ inline int wave_incl_scan(int v, int lane) {
     if (lane >= d) v += y;
   }
   return v;
+}
+
+// Barrier of the W waves of one query head: an LDS arrival counter that only
+// grows (each wave waits for its target, W more per barrier). The wait is
+// bounded: past kSpinLimit polls it counts a timeout in the head's header and
+// goes on, so the kernel always ends.
+constexpr int kSpinLimit = 1 << 20;
+
+__device__ inline void query_sync(int* ctr, int& target, int W, int* timeouts) {
+  target += W;
+  if (W == 1) {
+    wave_sync();
+    return;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (__lane_id() == 0) atomicAdd(ctr, 1);
+  int spins = 0;
+  while (__atomic_load_n(ctr, __ATOMIC_RELAXED) < target) {
+    if (++spins > kSpinLimit) {
+      if (__lane_id() == 0) atomicAdd(timeouts, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // ---- wave top lists --------------------------------------------------------
@@ -397,11 +422,18 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
   int32_t* wn = reinterpret_cast<int32_t*>(smem + S.off_misc);
   int32_t* qn = wn + kMaxWaves;
   int32_t* qp = qn + ICE_MAX_GROUP;
+  int32_t* qbar = qp + ICE_MAX_GROUP;
   int32_t* sel_all = reinterpret_cast<int32_t*>(smem + S.off_sel);
 
   const void* hb = head_base(blob, L, h);
   const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
   const int n_tok = hdr->n_tokens, Ltop = hdr->top_level;
+  // the query heads progress independently between their own barriers
+  int* timeouts = const_cast<int*>(&hdr->sync_timeouts);
+  if (tid < ICE_MAX_GROUP) qbar[tid] = 0;
+  __syncthreads();
+  int bar_target = 0;
+  auto qsync = [&]() { query_sync(&qbar[g], bar_target, W, timeouts); };
 
   QG qs;
   qs.load(Q + ((int64_t)h * G + g) * D, lane);
@@ -450,7 +482,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
   auto combine = [&](Top& t, int cap, int cut, int lvl) {
     if constexpr (!BIG) {
       comb[wv * 64 + lane] = t.L;
-      __syncthreads();
+      qsync();
       if (lead) {
         uint64_t r = comb[(g * W) * 64 + lane];
         for (int jj = 1; jj < W; ++jj) r = wave_merge_desc(r, comb[(g * W + jj) * 64 + lane], lane);
@@ -467,7 +499,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
       }
     } else {
       if (lane == 0) wn[wv] = t.n;
-      __syncthreads();
+      qsync();
       int tot = 0;
       for (int jj = 0; jj < W; ++jj) tot += wn[g * W + jj];
       for (int i = lane; i < t.n; i += 64) {
@@ -480,7 +512,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
         }
         if (rank < cap) qlist[rank] = x;
       }
-      __syncthreads();
+      qsync();
       if (lead) {
         const int qc = min(cap, tot);
         auto id_of = [&](int i) { return i < qc ? key_id(qlist[i]) : -1; };
@@ -497,7 +529,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
         if (lvl >= 0) build_table(lvl, qc, id_of);
       }
     }
-    __syncthreads();
+    qsync();
   };
 
   int cut = 0;
@@ -556,7 +588,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
   } else if (n_tok > 0) {
     // ---- root: the virtual root owns every token
     if (lead) build_table(0, 1, [&](int) { return L.cap; });
-    __syncthreads();
+    qsync();
   }
 
   // ---- level 0: the pages of the kept level-1 points, one key per page
@@ -600,6 +632,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
     }
     combine(tl, kpg, -1, -1);
   }
+  __syncthreads();      // every query head's selection is in sel_all
   // ---- union over the group, ascending page id, -1 padded
   const int tot = G * kpg;
   int32_t* urow = uni + (int64_t)h * tot;

@@ -178,7 +178,9 @@ typedef struct ice_head_stats {
   int32_t near_ties;       /* parent choices whose two best lifted distances were
                               within 1e-4 relative, build and insert              */
   int32_t overflow;        /* 1 if a page table was full (ruled out by the sizes) */
-  int32_t reserved0;
+  int32_t sync_timeouts;   /* selection-kernel barrier waits that hit their spin
+                              limit (a bound that keeps kernels finite; 0 in
+                              correct operation)                                 */
   int32_t reserved1;
   double  M2;              /* largest squared key norm at build                   */
 } ice_head_stats;

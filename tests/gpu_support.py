@@ -305,6 +305,8 @@ def compare_decode(ix, refs, out):
                 assert abs(lse[h, g] - lse_ref) <= 1e-4 * max(1.0, abs(lse_ref))
             else:
                 assert np.all(O[h, g] == 0) and lse[h, g] == -np.inf
+    for h in refs:
+        assert ix.stats(h)["sync_timeouts"] == 0, "a selection barrier wait hit its spin limit"
     say(f"decode parity ok: heads={len(refs)} selection near-ties={ties} worst attention error={worst:.3g}")
     return ties, worst
 
