@@ -201,22 +201,23 @@ __device__ inline void wave_sync() {
 
 // ---- cross-lane exchange on the VALU (no LDS round trip) -----------------
 // xor_lane<m>(x) returns x from lane ^ m. m = 1, 2: DPP quad permutes; m = 4:
-// DPP row rotations (a row is 16 lanes; row_ror:n reads lane i-n of the row);
-// m = 8: row_ror:8; m = 16, 32: the gfx950 permlane16 / permlane32 swaps.
-// All lanes of the wave must be active.
+// two DPP row shifts under bank masks (banks 0 and 2 of a row read lane + 4,
+// banks 1 and 3 lane - 4; a bank is 4 lanes of a 16-lane row); m = 8:
+// row_ror:8; m = 16, 32: the gfx950 permlane16 / permlane32 swaps. The DPP
+// moves leave no lane unwritten, so they need no initial value. All lanes of
+// the wave must be active.
 template <int m>
 __device__ inline int xor_lane(int x) {
   const int lane = __lane_id();
   if constexpr (m == 1) {
-    return __builtin_amdgcn_update_dpp(0, x, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+    return __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false);     // quad_perm [1,0,3,2]
   } else if constexpr (m == 2) {
-    return __builtin_amdgcn_update_dpp(0, x, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    return __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false);     // quad_perm [2,3,0,1]
   } else if constexpr (m == 4) {
-    const int down = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false);   // lane i-4
-    const int up = __builtin_amdgcn_update_dpp(0, x, 0x12c, 0xf, 0xf, false);     // lane i+4
-    return (lane & 4) ? down : up;
+    const int y = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xf, 0x5, false);   // row_shl:4, banks 0, 2
+    return __builtin_amdgcn_update_dpp(y, x, 0x114, 0xf, 0xa, false);          // row_shr:4, banks 1, 3
   } else if constexpr (m == 8) {
-    return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);   // row_ror:8
+    return __builtin_amdgcn_mov_dpp(x, 0x128, 0xf, 0xf, false);    // row_ror:8
   } else if constexpr (m == 16) {
     const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
     return (lane & 16) ? (int)p[0] : (int)p[1];

@@ -15,11 +15,13 @@
 // gfx950), issuing the loads of several 16-row groups before any arithmetic.
 // Keys pack (score, ~id) into 64 bits, so "score descending, id ascending" is
 // plain unsigned order. Each wave keeps its top list in registers, one key per
-// lane: a chunk of 64 candidates is bitonic-sorted across the wave and merged
-// by taking max(list[i], chunk[63-i]) (the 64 largest of both, as a bitonic
-// sequence) followed by a 6-step bitonic merge; the W lists of a query merge
-// the same way. All lane exchanges of these networks are DPP / permlane moves
-// on the VALU. Lists longer than 64 keys (beams or budgets beyond 64 entries)
+// lane: a chunk of 64 candidates is bitonic-sorted across the wave (ascending)
+// and merged by taking max(list[i], chunk[i]) (the 64 largest of both, as a
+// bitonic sequence) followed by a 6-step bitonic merge; the W lists of a
+// query (at most 64 keys together) are read into one wave as bitonic runs and
+// merged in 11 steps. A compare-exchange step is one lane exchange (DPP or
+// permlane swap), one 64-bit compare and two selects on the VALU. Lists
+// longer than 64 keys (beams or budgets beyond 64 entries)
 // use a slower LDS list instead. The block ends with the union of its query
 // heads' pages, ascending.
 #include "ice_launch.h"
@@ -104,60 +106,98 @@ __device__ inline uint64_t shfl64(uint64_t v, int src) {
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 __device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-template <int k, int j>
-__device__ inline uint64_t bitonic_step(uint64_t x, int lane) {
-  const uint64_t y = xor_lane_u64<j>(x);
-  return (((lane & k) == 0) == ((lane & j) == 0)) ? umax64(x, y) : umin64(x, y);
+// Compare-exchange of lanes i and i ^ j: a lane with keep_max set keeps the
+// larger of its key and its partner's, the other the smaller. For j = 16, 32
+// the permlane swap leaves the pair's two keys in (a, b) of both lanes, in
+// the same order, which is all a compare-exchange needs.
+template <int j>
+__device__ inline uint64_t cx64(uint64_t x, bool keep_max) {
+  uint64_t a = x, b;
+  if constexpr (j >= 16) {
+    const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+    int pl0, pl1, ph0, ph1;
+    if constexpr (j == 16) {
+      const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+      const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+      pl0 = pl[0]; pl1 = pl[1]; ph0 = ph[0]; ph1 = ph[1];
+    } else {
+      static_assert(j == 32, "exchange distance");
+      const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+      const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+      pl0 = pl[0]; pl1 = pl[1]; ph0 = ph[0]; ph1 = ph[1];
+    }
+    a = ((uint64_t)(uint32_t)ph0 << 32) | (uint32_t)pl0;
+    b = ((uint64_t)(uint32_t)ph1 << 32) | (uint32_t)pl1;
+  } else {
+    b = xor_lane_u64<j>(x);
+  }
+  return (a > b) == keep_max ? a : b;
 }
-// Sorts one key per lane across the wave, descending (lane 0 largest).
-__device__ inline uint64_t wave_sort_desc(uint64_t x, int lane) {
-  x = bitonic_step<2, 1>(x, lane);
-  x = bitonic_step<4, 2>(x, lane);
-  x = bitonic_step<4, 1>(x, lane);
-  x = bitonic_step<8, 4>(x, lane);
-  x = bitonic_step<8, 2>(x, lane);
-  x = bitonic_step<8, 1>(x, lane);
-  x = bitonic_step<16, 8>(x, lane);
-  x = bitonic_step<16, 4>(x, lane);
-  x = bitonic_step<16, 2>(x, lane);
-  x = bitonic_step<16, 1>(x, lane);
-  x = bitonic_step<32, 16>(x, lane);
-  x = bitonic_step<32, 8>(x, lane);
-  x = bitonic_step<32, 4>(x, lane);
-  x = bitonic_step<32, 2>(x, lane);
-  x = bitonic_step<32, 1>(x, lane);
-  x = bitonic_step<64, 32>(x, lane);
-  x = bitonic_step<64, 16>(x, lane);
-  x = bitonic_step<64, 8>(x, lane);
-  x = bitonic_step<64, 4>(x, lane);
-  x = bitonic_step<64, 2>(x, lane);
-  x = bitonic_step<64, 1>(x, lane);
+// step (k, j) of a bitonic sort: blocks of k lanes alternate direction
+template <int k, int j>
+__device__ inline uint64_t sort_step(uint64_t x, int lane, bool desc) {
+  return cx64<j>(x, (((lane & k) == 0) == ((lane & j) == 0)) == desc);
+}
+// Sorts one key per lane across the wave: descending (lane 0 largest) when
+// `desc`, else ascending.
+__device__ inline uint64_t wave_sort(uint64_t x, int lane, bool desc) {
+  x = sort_step<2, 1>(x, lane, desc);
+  x = sort_step<4, 2>(x, lane, desc);
+  x = sort_step<4, 1>(x, lane, desc);
+  x = sort_step<8, 4>(x, lane, desc);
+  x = sort_step<8, 2>(x, lane, desc);
+  x = sort_step<8, 1>(x, lane, desc);
+  x = sort_step<16, 8>(x, lane, desc);
+  x = sort_step<16, 4>(x, lane, desc);
+  x = sort_step<16, 2>(x, lane, desc);
+  x = sort_step<16, 1>(x, lane, desc);
+  x = sort_step<32, 16>(x, lane, desc);
+  x = sort_step<32, 8>(x, lane, desc);
+  x = sort_step<32, 4>(x, lane, desc);
+  x = sort_step<32, 2>(x, lane, desc);
+  x = sort_step<32, 1>(x, lane, desc);
+  x = sort_step<64, 32>(x, lane, desc);
+  x = sort_step<64, 16>(x, lane, desc);
+  x = sort_step<64, 8>(x, lane, desc);
+  x = sort_step<64, 4>(x, lane, desc);
+  x = sort_step<64, 2>(x, lane, desc);
+  x = sort_step<64, 1>(x, lane, desc);
   return x;
 }
-template <int j>
-__device__ inline uint64_t merge_step(uint64_t t, int lane) {
-  const uint64_t y = xor_lane_u64<j>(t);
-  return (lane & j) == 0 ? umax64(t, y) : umin64(t, y);
-}
-// Top 64 of two descending wave lists, descending.
-__device__ inline uint64_t wave_merge_desc(uint64_t a, uint64_t b_sorted, int lane) {
-  // b reversed: lane ^ 63 == 63 - lane
-  uint64_t r = xor_lane_u64<1>(b_sorted);
-  r = xor_lane_u64<2>(r);
-  r = xor_lane_u64<4>(r);
-  r = xor_lane_u64<8>(r);
-  r = xor_lane_u64<16>(r);
-  r = xor_lane_u64<32>(r);
-  uint64_t t = umax64(a, r);
-  t = merge_step<32>(t, lane);
-  t = merge_step<16>(t, lane);
-  t = merge_step<8>(t, lane);
-  t = merge_step<4>(t, lane);
-  t = merge_step<2>(t, lane);
-  t = merge_step<1>(t, lane);
+// Sorts a bitonic sequence across the wave, descending.
+__device__ inline uint64_t bitonic_merge_desc(uint64_t t, int lane) {
+  t = cx64<32>(t, (lane & 32) == 0);
+  t = cx64<16>(t, (lane & 16) == 0);
+  t = cx64<8>(t, (lane & 8) == 0);
+  t = cx64<4>(t, (lane & 4) == 0);
+  t = cx64<2>(t, (lane & 2) == 0);
+  t = cx64<1>(t, (lane & 1) == 0);
   return t;
+}
+// Top 64 of a descending list and an ascending chunk, descending: their
+// lane-wise maximum holds the 64 largest as a bitonic sequence.
+__device__ inline uint64_t wave_merge(uint64_t list_desc, uint64_t chunk_asc, int lane) {
+  return bitonic_merge_desc(umax64(list_desc, chunk_asc), lane);
+}
+// Merges the descending lists of W waves (W = 2 or 4, at most 64 / W keys
+// each; list w at lists + 64 w) into one descending list. The lists sit side
+// by side in segments of 64 / W lanes, every second one read backwards, so
+// each pair of segments is a bitonic sequence.
+__device__ inline uint64_t merge_lists(const uint64_t* lists, int W, int lane) {
+  if (W == 4) {
+    const int sg = lane >> 4, i = lane & 15;
+    uint64_t x = lists[sg * 64 + ((sg & 1) ? 15 - i : i)];
+    // pairs of segments into 32-lane runs, the first descending, the second ascending
+    x = cx64<16>(x, ((lane & 32) == 0) == ((lane & 16) == 0));
+    x = cx64<8>(x, ((lane & 32) == 0) == ((lane & 8) == 0));
+    x = cx64<4>(x, ((lane & 32) == 0) == ((lane & 4) == 0));
+    x = cx64<2>(x, ((lane & 32) == 0) == ((lane & 2) == 0));
+    x = cx64<1>(x, ((lane & 32) == 0) == ((lane & 1) == 0));
+    return bitonic_merge_desc(x, lane);
+  }
+  const int sg = lane >> 5, i = lane & 31;
+  return bitonic_merge_desc(lists[sg * 64 + (sg ? 31 - i : i)], lane);
 }
 
 // ---- LDS layout ------------------------------------------------------------
@@ -277,8 +317,10 @@ struct RegTop {
     const uint64_t thr = n == cap ? readlane64(L, cap - 1) : 0ull;
     const uint64_t live = __ballot(x > thr);
     if (live == 0) return;
-    uint64_t t = wave_sort_desc(x, lane);
-    if (n > 0) t = wave_merge_desc(L, t, lane);
+    // the first chunk is sorted descending into the list, later ones
+    // ascending and merged with it
+    uint64_t t = wave_sort(x, lane, n == 0);
+    if (n > 0) t = wave_merge(L, t, lane);
     L = lane < cap ? t : 0ull;
     n = min(cap, n + __popcll(live));
   }
@@ -484,8 +526,13 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
       comb[wv * 64 + lane] = t.L;
       qsync();
       if (lead) {
-        uint64_t r = comb[(g * W) * 64 + lane];
-        for (int jj = 1; jj < W; ++jj) r = wave_merge_desc(r, comb[(g * W + jj) * 64 + lane], lane);
+        const uint64_t* ql0 = comb + (g * W) * 64;
+        uint64_t r = ql0[lane];
+        if (W > 1 && W * cap <= 64) {
+          r = merge_lists(ql0, W, lane);
+        } else {
+          for (int jj = 1; jj < W; ++jj) r = wave_merge(r, ql0[jj * 64 + 63 - lane], lane);
+        }
         const uint64_t ql = lane < cap ? r : 0ull;
         const int qc = __popcll(__ballot(ql != 0ull));
         const int id = lane < qc ? key_id(ql) : -1;
