@@ -18,6 +18,7 @@ c_size, c_void_p, c_char_p = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
 
 ICE_OK, ICE_ERR_ARG, ICE_ERR_DTYPE, ICE_ERR_STATE, ICE_ERR_CAPACITY, ICE_ERR_HIP = 0, -1, -2, -3, -4, -5
 ICE_F32, ICE_BF16 = 0, 1
+ICE_HOST_POOL = 1
 ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM = 16, 4, 16, 256
 (ICE_EXP_LEVEL, ICE_EXP_LIFT, ICE_EXP_PARENT, ICE_EXP_PAGE_TOK, ICE_EXP_PAGE_CNT, ICE_EXP_PAGE_NEXT,
  ICE_EXP_PAGE_OWNER, ICE_EXP_OWNER_FIRST, ICE_EXP_OWNER_TAIL, ICE_EXP_TOP, ICE_EXP_PAGE_K, ICE_EXP_PAGE_V,
@@ -26,7 +27,8 @@ ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM = 16, 4, 16, 256
 
 class IceParams(ctypes.Structure):
     _fields_ = [("n_heads", c_i32), ("group", c_i32), ("d", c_i32), ("dtype", c_i32), ("page_cap", c_i32),
-                ("levels", c_i32), ("promote_log2", c_i32), ("capacity", c_i32), ("seed", c_u64)]
+                ("levels", c_i32), ("promote_log2", c_i32), ("capacity", c_i32), ("flags", ctypes.c_uint32),
+                ("seed", c_u64)]
 
 
 class IceHeadStats(ctypes.Structure):
@@ -40,6 +42,8 @@ _SIGNATURES = {
     "ice_workspace_bytes": (c_size, [ctypes.POINTER(IceParams), c_i32]),
     "ice_create": (ctypes.c_int, [ctypes.POINTER(IceParams), c_void_p, c_size, ctypes.POINTER(c_void_p)]),
     "ice_destroy": (None, [c_void_p]),
+    "ice_host_pool_bytes": (c_size, [ctypes.POINTER(IceParams)]),
+    "ice_attach_host_pool": (ctypes.c_int, [c_void_p, c_void_p, c_size]),
     "ice_build": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p, c_size, c_void_p]),
     "ice_insert": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_size, c_void_p]),
     "ice_select": (ctypes.c_int, [c_void_p, c_void_p, c_i32, c_i32, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -27,10 +27,41 @@ def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+class PinnedHost:
+    """Pinned host memory of an exact size from hipHostMalloc (mapped into the
+    device address space), freed with hipHostFree. torch's pinned allocator
+    rounds sizes up to powers of two, which doubles a multi-GB pool."""
+
+    _hip = None
+
+    def __init__(self, nbytes: int):
+        if PinnedHost._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+            hip.hipHostMalloc.restype = ctypes.c_int
+            hip.hipHostFree.argtypes = [ctypes.c_void_p]
+            hip.hipHostFree.restype = ctypes.c_int
+            PinnedHost._hip = hip
+        self.ptr = ctypes.c_void_p()
+        self.nbytes = int(nbytes)
+        rc = PinnedHost._hip.hipHostMalloc(ctypes.byref(self.ptr), max(self.nbytes, 1), 0)
+        if rc != 0 or not self.ptr.value:
+            raise MemoryError(f"hipHostMalloc of {self.nbytes} bytes failed with status {rc}")
+
+    def data_ptr(self) -> int:
+        return int(self.ptr.value)
+
+    def __del__(self):
+        if getattr(self, "ptr", None) is not None and self.ptr.value and PinnedHost._hip is not None:
+            PinnedHost._hip.hipHostFree(self.ptr)
+            self.ptr = None
+
+
 def make_params(n_heads: int, group: int, d: int, dtype: str, capacity: int, levels: int = 3,
-                promote_log2: int = 4, seed: int = 0) -> IceParams:
+                promote_log2: int = 4, seed: int = 0, host_pool: bool = False) -> IceParams:
     return IceParams(n_heads=n_heads, group=group, d=d, dtype=_DT[dtype][0], page_cap=_lib.ICE_PAGE_CAP,
-                     levels=levels, promote_log2=promote_log2, capacity=capacity, seed=seed)
+                     levels=levels, promote_log2=promote_log2, capacity=capacity,
+                     flags=_lib.ICE_HOST_POOL if host_pool else 0, seed=seed)
 
 
 def ice_index_bytes(p: IceParams) -> int:
@@ -45,11 +76,14 @@ class IceIndex:
     """One index object: H independent heads, their device blob and workspace.
 
     ``ice_build`` / ``ice_insert`` / ``ice_select`` / ``ice_attend`` map one to
-    one onto the C entry points of the same names.
+    one onto the C entry points of the same names. With ``host_pool=True`` the
+    V pages live in a pinned host tensor (``self.pool``) and every attend
+    gathers the union's pages over the host link first.
     """
 
     def __init__(self, n_heads: int, group: int, d: int, dtype: str, capacity: int, levels: int = 3,
-                 promote_log2: int = 4, seed: int = 0, max_budget: int = 256, device="cuda"):
+                 promote_log2: int = 4, seed: int = 0, max_budget: int = 256, device="cuda",
+                 host_pool: bool = False):
         self.lib = _lib.load()
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
@@ -57,7 +91,7 @@ class IceIndex:
         self.device = dev
         self.dtype = dtype
         self.tdtype = _DT[dtype][1]
-        self.p = make_params(n_heads, group, d, dtype, capacity, levels, promote_log2, seed)
+        self.p = make_params(n_heads, group, d, dtype, capacity, levels, promote_log2, seed, host_pool)
         self.H, self.G, self.d, self.capacity, self.levels = n_heads, group, d, capacity, levels
         self.max_budget = max_budget
         nbytes = ice_index_bytes(self.p)
@@ -71,12 +105,19 @@ class IceIndex:
         h = ctypes.c_void_p()
         check(self.lib.ice_create(ctypes.byref(self.p), _ptr(self.blob), nbytes, ctypes.byref(h)), "ice_create")
         self.handle = h
+        self.pool = None
+        if host_pool:
+            pool_bytes = int(self.lib.ice_host_pool_bytes(ctypes.byref(self.p)))
+            self.pool = PinnedHost(pool_bytes)
+            check(self.lib.ice_attach_host_pool(self.handle, ctypes.c_void_p(self.pool.data_ptr()), pool_bytes),
+                  "ice_attach_host_pool")
 
     def __del__(self):
         h = getattr(self, "handle", None)
         if h is not None and h.value:
             self.lib.ice_destroy(h)
             self.handle = None
+        self.pool = None
 
     # ---- the four calls -------------------------------------------------
     def _check_kv(self, x: torch.Tensor, name: str):

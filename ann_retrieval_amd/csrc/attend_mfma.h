@@ -108,7 +108,11 @@ __device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int qn = lane & 15, qt = lane >> 4;     // query (B column, S^T column) and 4-token group
   const char* pgK = at<char>(hb, L.off_pgK[0]);
-  const char* pgV = at<char>(hb, L.off_pgV);
+  // one block per head; with staged V the page of union entry u is entry u
+  // of the head's staging area, else the page id itself
+  const int h = blockIdx.x;
+  const bool staged = L.vstage != nullptr;
+  const char* pgV = staged ? L.vstage + (int64_t)h * L.vstage_pages * (ICE_PAGE_CAP * M::ROWB) : v_pages(L, hb, h);
   const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
   const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
   const float c2 = scale * kLog2e;
@@ -145,7 +149,7 @@ __device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* 
       const int pg = __shfl(my_pg, kc, 64), cnt = __shfl(my_cnt, kc, 64);
       const bool ok = k < nk && pg >= 0;
       mload_k<D>(pgK, ok ? pg : 0, ok ? cnt : 0, lane, b);
-      if constexpr (PREFETCH_V) mload_v<D>(pgV, ok ? pg : 0, ok ? cnt : 0, lane, b.v);
+      if constexpr (PREFETCH_V) mload_v<D>(pgV, ok ? (staged ? wv + nw * (k0 + kc) : pg) : 0, ok ? cnt : 0, lane, b.v);
     };
     issue(0, bufA);
     auto step = [&](int k, MPage<D>& cur, MPage<D>& nxt) {
@@ -153,7 +157,7 @@ __device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* 
       const int pg_k = __shfl(my_pg, kc, 64), cnt_k = __shfl(my_cnt, kc, 64);
       const int cnt = k < nk && pg_k >= 0 ? cnt_k : 0;      // 0: nothing to attend
       uint2 vcur[M::VC];
-      if constexpr (!PREFETCH_V) mload_v<D>(pgV, cnt > 0 ? pg_k : 0, cnt, lane, vcur);
+      if constexpr (!PREFETCH_V) mload_v<D>(pgV, cnt > 0 ? (staged ? wv + nw * (k0 + kc) : pg_k) : 0, cnt, lane, vcur);
       issue(k + 1, nxt);
       float4v s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll

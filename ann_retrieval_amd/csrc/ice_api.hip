@@ -20,6 +20,7 @@ struct ice_index {
   WsLayout W;
   void* blob;
   size_t blob_bytes;
+  void* host_pool;        // host-pool mode: the caller's pinned V pool (host address)
   int32_t n_tokens;
   bool built;
 };
@@ -52,6 +53,7 @@ int check_params(const ice_params* p) {
   if (p->levels < 1 || p->levels > ICE_MAX_LEVELS) return fail(ICE_ERR_ARG, "levels must be in [1, %d]", ICE_MAX_LEVELS);
   if (p->promote_log2 < 1 || p->promote_log2 > 16) return fail(ICE_ERR_ARG, "promote_log2 must be in [1, 16]");
   if (p->capacity < 1 || p->capacity > (1 << 28)) return fail(ICE_ERR_ARG, "capacity must be in [1, 2^28]");
+  if (p->flags & ~ICE_HOST_POOL) return fail(ICE_ERR_ARG, "unknown flags 0x%x", p->flags);
   return ICE_OK;
 }
 
@@ -117,8 +119,13 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
     L->off_orun[l] = c.take((cap + 1) * 4);
     L->off_ocnt[l] = c.take((cap + 1) * 4);
     L->off_pgK[l] = c.take(P * ICE_PAGE_CAP * d * elt);
-    if (l == 0) L->off_pgV = c.take(P * ICE_PAGE_CAP * d * elt);
-    else L->off_pgE[l] = c.take(P * ICE_PAGE_CAP * 4);
+    if (l == 0) {
+      // host-pool mode keeps V out of the blob: the pool holds it per head
+      if (p->flags & ICE_HOST_POOL) L->vpool_head_bytes = align256(P * ICE_PAGE_CAP * d * elt);
+      else L->off_pgV = c.take(P * ICE_PAGE_CAP * d * elt);
+    } else {
+      L->off_pgE[l] = c.take(P * ICE_PAGE_CAP * 4);
+    }
   }
   L->off_top_tok = c.take((int64_t)L->topcap * 4);
   L->off_top_K = c.take((int64_t)L->topcap * d * elt);
@@ -149,8 +156,25 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
   W->build_bytes = W->head_bytes * p->n_heads;
 }
 
-int64_t attend_ws_bytes(const DevLayout& L, int uni_stride) {
+int64_t attend_part_bytes(const DevLayout& L, int uni_stride) {
   return align256((int64_t)L.H * attend_splits(uni_stride) * L.G * (L.d + 2) * 4);
+}
+bool host_mode(const DevLayout& L) { return L.vpool_head_bytes > 0; }
+int64_t page_bytes(const DevLayout& L) { return (int64_t)ICE_PAGE_CAP * L.d * L.elt; }
+// attention's workspace: split partials, then (host-pool mode) the V staging
+// area of uni_stride pages per head
+int64_t attend_ws_bytes(const DevLayout& L, int uni_stride) {
+  const int64_t stage = host_mode(L) ? (int64_t)L.H * uni_stride * page_bytes(L) : 0;
+  return attend_part_bytes(L, uni_stride) + align256(stage);
+}
+// the layout attention runs with: staged V in host-pool mode
+DevLayout attend_layout(const DevLayout& L, void* ws, int uni_stride) {
+  DevLayout A = L;
+  if (host_mode(L)) {
+    A.vstage = static_cast<const char*>(ws) + attend_part_bytes(L, uni_stride);
+    A.vstage_pages = uni_stride;
+  }
+  return A;
 }
 
 int check_budget(const ice_index* idx, int32_t budget) {
@@ -191,6 +215,14 @@ size_t ice_workspace_bytes(const ice_params* p, int32_t max_budget_tokens) {
   return (size_t)std::max<int64_t>(W.build_bytes, att);
 }
 
+size_t ice_host_pool_bytes(const ice_params* p) {
+  if (check_params(p) != ICE_OK || !(p->flags & ICE_HOST_POOL)) return 0;
+  DevLayout L;
+  WsLayout W;
+  make_layout(p, &L, &W);
+  return (size_t)(L.vpool_head_bytes * p->n_heads);
+}
+
 int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_index** out) {
   if (!out) return fail(ICE_ERR_ARG, "out is null");
   *out = nullptr;
@@ -209,6 +241,7 @@ int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_ind
   }
   idx->blob = index_dev;
   idx->blob_bytes = index_bytes;
+  idx->host_pool = nullptr;
   idx->n_tokens = 0;
   idx->built = false;
   *out = idx;
@@ -216,6 +249,28 @@ int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_ind
 }
 
 void ice_destroy(ice_index* idx) { delete idx; }
+
+int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (!host_mode(idx->L)) return fail(ICE_ERR_STATE, "the index was created without ICE_HOST_POOL");
+  if (!host_pool) return fail(ICE_ERR_ARG, "host pool is null");
+  if (((uintptr_t)host_pool & 255u) != 0) return fail(ICE_ERR_ARG, "host pool must be 256-byte aligned");
+  const size_t need = (size_t)(idx->L.vpool_head_bytes * idx->p.n_heads);
+  if (host_pool_bytes < need)
+    return fail(ICE_ERR_CAPACITY, "host pool has %zu bytes, needs %zu", host_pool_bytes, need);
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, host_pool);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(ICE_ERR_ARG, "host pool is not pinned host memory (allocate it with hipHostMalloc)");
+  }
+  void* dev = nullptr;
+  e = hipHostGetDevicePointer(&dev, host_pool, 0);
+  if (e != hipSuccess || !dev) return hip_fail(e, "hipHostGetDevicePointer of the host pool");
+  idx->host_pool = host_pool;
+  idx->L.vpool = static_cast<char*>(dev);
+  return ICE_OK;
+}
 
 int32_t ice_n_tokens(const ice_index* idx) { return idx ? idx->n_tokens : -1; }
 
@@ -235,6 +290,7 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
     return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, build needs %lld", ws_bytes,
                 (long long)idx->W.build_bytes);
   if (((uintptr_t)ws & 255u) != 0) return fail(ICE_ERR_ARG, "workspace must be 256-byte aligned");
+  if (host_mode(idx->L) && !idx->L.vpool) return fail(ICE_ERR_STATE, "build before ice_attach_host_pool");
   hipError_t e = launch_build(idx->L, idx->W, idx->blob, K, V, n_tokens, head_stride, ws,
                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ice_build launch");
@@ -289,8 +345,12 @@ int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const in
   const int64_t need = attend_ws_bytes(idx->L, uni_stride);
   if (need > 0 && (!ws || ws_bytes < (size_t)need))
     return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, attend needs %lld", ws_bytes, (long long)need);
-  hipError_t e = launch_attend(idx->L, idx->blob, Q, uni, n_uni, uni_stride, scale, O, lse, ws,
-                               static_cast<hipStream_t>(stream));
+  if (need > 0 && ((uintptr_t)ws & 255u) != 0) return fail(ICE_ERR_ARG, "workspace must be 256-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const DevLayout A = attend_layout(idx->L, ws, uni_stride);
+  hipError_t e = hipSuccess;
+  if (host_mode(idx->L)) e = launch_gather_v(A, idx->blob, uni, n_uni, uni_stride, s);
+  if (e == hipSuccess) e = launch_attend(A, idx->blob, Q, uni, n_uni, uni_stride, scale, O, lse, ws, s);
   if (e != hipSuccess) return hip_fail(e, "ice_attend launch");
   return ICE_OK;
 }
@@ -305,7 +365,7 @@ int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32
   if (!aligned16(Q)) return fail(ICE_ERR_ARG, "Q must be 16-byte aligned");
   const int uni_stride = idx->p.group * (budget_tokens / ICE_PAGE_CAP);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (decode_fused(idx->L, budget_tokens, beam)) {
+  if (!host_mode(idx->L) && decode_fused(idx->L, budget_tokens, beam)) {
     hipError_t e = launch_decode(idx->L, idx->blob, Q, budget_tokens, beam, sel, uni, n_uni, scale, O, lse, s);
     if (e != hipSuccess) return hip_fail(e, "ice_decode launch");
     return ICE_OK;
@@ -313,9 +373,15 @@ int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32
   const int64_t need = attend_ws_bytes(idx->L, uni_stride);
   if (need > 0 && (!ws || ws_bytes < (size_t)need))
     return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, attend needs %lld", ws_bytes, (long long)need);
+  if (need > 0 && ((uintptr_t)ws & 255u) != 0) return fail(ICE_ERR_ARG, "workspace must be 256-byte aligned");
   hipError_t e = launch_select(idx->L, idx->blob, Q, budget_tokens, beam, sel, uni, n_uni, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "ice_decode select launch");
-  e = launch_attend(idx->L, idx->blob, Q, uni, n_uni, uni_stride, scale, O, lse, ws, s);
+  const DevLayout A = attend_layout(idx->L, ws, uni_stride);
+  if (host_mode(idx->L)) {
+    e = launch_gather_v(A, idx->blob, uni, n_uni, uni_stride, s);
+    if (e != hipSuccess) return hip_fail(e, "ice_decode gather launch");
+  }
+  e = launch_attend(A, idx->blob, Q, uni, n_uni, uni_stride, scale, O, lse, ws, s);
   if (e != hipSuccess) return hip_fail(e, "ice_decode attend launch");
   return ICE_OK;
 }
@@ -375,6 +441,10 @@ int ice_export(const ice_index* idx, int32_t head, int32_t what, int32_t level, 
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ice_export sync");
   const char* src = static_cast<const char*>(idx->blob) + (int64_t)head * L.head_bytes + off;
+  if (what == ICE_EXP_PAGE_V && host_mode(L)) {
+    if (!idx->host_pool) return fail(ICE_ERR_STATE, "no host pool attached");
+    src = static_cast<const char*>(idx->host_pool) + (int64_t)head * L.vpool_head_bytes;
+  }
   if (what != ICE_EXP_PAGE_V) {
     e = hipMemcpy(dst, src, n, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "ice_export copy");
@@ -383,7 +453,7 @@ int ice_export(const ice_index* idx, int32_t head, int32_t what, int32_t level, 
   // V pages are stored [page][slot group][dim][4 slots]; hand them out as
   // [page][slot][dim] rows
   std::vector<char> raw(n);
-  e = hipMemcpy(raw.data(), src, n, hipMemcpyDeviceToHost);
+  e = hipMemcpy(raw.data(), src, n, host_mode(L) ? hipMemcpyHostToHost : hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "ice_export copy");
   const int64_t elt = L.elt, D = L.d, pages = (int64_t)n / (ICE_PAGE_CAP * D * elt);
   char* out = static_cast<char*>(dst);

@@ -52,7 +52,24 @@ struct DevLayout {
   int64_t off_orun[ICE_MAX_LEVELS], off_ocnt[ICE_MAX_LEVELS];
   int64_t off_pgK[ICE_MAX_LEVELS], off_pgE[ICE_MAX_LEVELS], off_pgV;
   int64_t off_top_tok, off_top_K, off_top_E;
+  // Host-pool mode: level-0 V pages live outside the blob, in pinned host
+  // memory mapped into the device address space (head h at vpool + h *
+  // vpool_head_bytes, same page layout); off_pgV is then unused. Attention
+  // reads V from vstage when it is set: the V page of union entry u of head h
+  // at vstage + (h * vstage_pages + u) * page bytes.
+  char* vpool;
+  int64_t vpool_head_bytes;
+  const char* vstage;
+  int32_t vstage_pages;
 };
+
+// Level-0 V pages of head h (hb = its region of the blob).
+__host__ __device__ inline char* v_pages(const DevLayout& L, void* hb, int h) {
+  return L.vpool ? L.vpool + (int64_t)h * L.vpool_head_bytes : static_cast<char*>(hb) + L.off_pgV;
+}
+__host__ __device__ inline const char* v_pages(const DevLayout& L, const void* hb, int h) {
+  return L.vpool ? L.vpool + (int64_t)h * L.vpool_head_bytes : static_cast<const char*>(hb) + L.off_pgV;
+}
 
 // Build workspace, also laid out per head.
 struct WsLayout {

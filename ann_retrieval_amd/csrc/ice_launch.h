@@ -26,6 +26,9 @@ int attend_splits(int uni_stride);
 hipError_t launch_attend(const DevLayout& L, const void* blob, const void* Q, const int32_t* uni,
                          const int32_t* n_uni, int uni_stride, float scale, float* O, float* lse, void* ws,
                          hipStream_t s);
+// host-pool mode: the V pages of every head's union from the host pool into L.vstage
+hipError_t launch_gather_v(const DevLayout& L, const void* blob, const int32_t* uni, const int32_t* n_uni,
+                           int uni_stride, hipStream_t s);
 // fills `n` int32 words at byte offset `off` of every head region
 hipError_t launch_fill_heads(void* base, int64_t head_bytes, int H, int64_t off, int64_t n, int32_t value,
                              hipStream_t s);

@@ -11,6 +11,8 @@
 #include "ice_launch.h"
 #include "attend_mfma.h"
 
+#include <algorithm>
+
 namespace ice {
 namespace {
 
@@ -137,7 +139,9 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend_f32(DevLayout L, cons
   const int G = L.G;
   const void* hb = head_base(blob, L, h);
   const char* pgK = at<char>(hb, L.off_pgK[0]);
-  const char* pgV = at<char>(hb, L.off_pgV);
+  // with staged V the page of union entry u is entry u of the head's staging area
+  const bool staged = L.vstage != nullptr;
+  const char* pgV = staged ? L.vstage + (int64_t)h * L.vstage_pages * (ICE_PAGE_CAP * D * 4) : v_pages(L, hb, h);
   const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
   const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
   const int nu = min(n_uni[h], uni_stride);
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend_f32(DevLayout L, cons
       {
         const int p0 = __shfl(my_pg, 0, 64), c0 = __shfl(my_cnt, 0, 64);
         fload_k<D>(pgK, p0 >= 0 ? p0 : 0, c0, lane, bufA);
-        fload_v<D>(pgV, p0 >= 0 ? p0 : 0, c0, lane, bufA);
+        fload_v<D>(pgV, p0 >= 0 ? (staged ? wv + kAttWaves * k0 : p0) : 0, c0, lane, bufA);
       }
       // page k from `cur`; page k+1's K loads before the scores, its V after
       auto step = [&](int k, FPage<D>& cur, FPage<D>& nxt) {
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend_f32(DevLayout L, cons
           }
         }
         wave_sync();
-        fload_v<D>(pgV, pgn >= 0 ? pgn : 0, cntn, lane, nxt);
+        fload_v<D>(pgV, pgn >= 0 ? (staged ? wv + kAttWaves * (k0 + k + 1) : pgn) : 0, cntn, lane, nxt);
         if (pg >= 0) {
 #pragma unroll
           for (int g = 0; g < kQPerPass; ++g) {
@@ -268,9 +272,58 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend_f32(DevLayout L, cons
   }
 }
 
+// Host-pool mode, the bulk load of a step: copies the level-0 V pages of head
+// h's union from the pinned host pool into entries 0..n_uni-1 of the head's
+// staging area, in union order (16-byte pieces, kGatherUnroll loads in flight
+// per thread, the link's latency hidden by the blocks of all heads). An id
+// outside the head's page table stages a zero page.
+constexpr int kGatherUnroll = 4;
+
+__global__ __launch_bounds__(256) void k_gather_v(DevLayout L, const void* blob, const int32_t* uni,
+                                                   const int32_t* n_uni, int uni_stride) {
+  const int h = blockIdx.x;
+  const void* hb = head_base(blob, L, h);
+  const int64_t pb = (int64_t)ICE_PAGE_CAP * L.d * L.elt;
+  const char* src = v_pages(L, hb, h);
+  char* dst = const_cast<char*>(L.vstage) + (int64_t)h * L.vstage_pages * pb;
+  const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
+  const int nu = min(n_uni[h], uni_stride);
+  const int32_t* u = uni + (int64_t)h * uni_stride;
+  const int per = (int)(pb / 16);
+  const int total = nu * per;
+  const int step = gridDim.y * blockDim.x * kGatherUnroll;
+  for (int i0 = blockIdx.y * blockDim.x * kGatherUnroll + threadIdx.x; i0 < total; i0 += step) {
+    V4 v[kGatherUnroll];
+#pragma unroll
+    for (int j = 0; j < kGatherUnroll; ++j) {
+      const int i = i0 + j * blockDim.x;
+      v[j] = V4{0, 0, 0, 0};
+      if (i < total) {
+        const int pg = u[i / per];
+        if (pg >= 0 && pg < n_pages) v[j] = *reinterpret_cast<const V4*>(src + (int64_t)pg * pb + (int64_t)(i % per) * 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kGatherUnroll; ++j) {
+      const int i = i0 + j * blockDim.x;
+      if (i < total) *reinterpret_cast<V4*>(dst + (int64_t)i * 16) = v[j];
+    }
+  }
+}
+
 }  // namespace
 
 int attend_splits(int) { return 0; }
+
+hipError_t launch_gather_v(const DevLayout& L, const void* blob, const int32_t* uni, const int32_t* n_uni,
+                           int uni_stride, hipStream_t s) {
+  if (!L.vpool || !L.vstage) return hipErrorInvalidValue;
+  // blocks per head: enough to cover the largest union in one pass
+  const int64_t pieces = (int64_t)uni_stride * ICE_PAGE_CAP * L.d * L.elt / 16;
+  const unsigned per_head = (unsigned)std::max<int64_t>(1, (pieces + 256 * kGatherUnroll - 1) / (256 * kGatherUnroll));
+  k_gather_v<<<dim3((unsigned)L.H, per_head), 256, 0, s>>>(L, blob, uni, n_uni, uni_stride);
+  return hipGetLastError();
+}
 
 hipError_t launch_attend(const DevLayout& L, const void* blob, const void* Q, const int32_t* uni,
                          const int32_t* n_uni, int uni_stride, float scale, float* O, float* lse, void*,

@@ -404,7 +404,7 @@ __global__ __launch_bounds__(256) void k_copy_vt(DevLayout L, const T* V, int64_
   const int n_pages = hdr->n_pages[0];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[0]);
-  T* pv = at<T>(hb, L.off_pgV);
+  T* pv = reinterpret_cast<T*>(v_pages(L, hb, h));
   const T* Vh = V + (int64_t)h * hstride;
   for (int pg = blockIdx.x * 4 + wave; pg < n_pages; pg += gridDim.x * 4) {
     const int my_tok = lane < ICE_PAGE_CAP ? pg_tok[(int64_t)pg * ICE_PAGE_CAP + lane] : -1;

@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
       // V pages ([slot group][dim][4 slots]): every element but slot 0's
       if (l == 0)
         for (int i = tid; i < ICE_PAGE_CAP * D; i += 256)
-          if (i % 4 != 0 || i >= 4 * D) at<T>(hb, L.off_pgV)[base * D + i] = T(0);
+          if (i % 4 != 0 || i >= 4 * D) reinterpret_cast<T*>(v_pages(L, hb, h))[base * D + i] = T(0);
     }
     // rows into the pools
     for (int i = tid; i < D; i += 256) {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
         const int64_t row = (int64_t)plc.page[0] * ICE_PAGE_CAP + plc.slot[0];
         at<T>(hb, L.off_pgK[0])[row * D + i] = kv;
         const int sl = plc.slot[0];
-        at<T>(hb, L.off_pgV)[(((int64_t)plc.page[0] * 4 + sl / 4) * D + i) * 4 + sl % 4] = vrow[i];
+        reinterpret_cast<T*>(v_pages(L, hb, h))[(((int64_t)plc.page[0] * 4 + sl / 4) * D + i) * 4 + sl % 4] = vrow[i];
       }
       for (int l = 1; l < Ltop; ++l) {
         if (plc.page[l] < 0) continue;

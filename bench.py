@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--builds", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-host-pool", action="store_true", help="skip the host-pool mode measurement")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="print a markdown summary of rocprofv3 output instead of benchmarking: one "
@@ -214,6 +215,62 @@ def head_meta(ix, H, cap):
     ix.meta = meta
 
 
+def time_host_pool(w, Qs, a, H, G, N, d, dtype, budget, dev_attend_ms, n_ins):
+    """Host-pool mode on the same workload: V pages in pinned host memory, each
+    step gathers the union's V pages over the host link before attending.
+    Bound by the link, not HBM, so it is reported beside the roofline, not in
+    it. The gather's own time is estimated as the host-pool attend (gather +
+    attention) minus the device-pool attend."""
+    import torch
+    from ann_retrieval_amd.api import IceIndex
+    beam = budget // 16
+    t0 = time.perf_counter()
+    ix = IceIndex(H, G, d, dtype, N + n_ins, seed=a.seed, max_budget=budget, device=w.K.device, host_pool=True)
+    alloc_s = time.perf_counter() - t0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    ix.ice_build(w.K, w.V)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    for s in range(min(a.warmup, 3)):
+        ix.ice_decode(Qs[s], budget, beam)
+    torch.cuda.synchronize()
+    steps = a.steps
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(5e7))
+    g0.record()
+    for s in range(steps):
+        ix.ice_decode(Qs[a.warmup + s], budget, beam)
+    g1.record()
+    torch.cuda.synchronize()
+    ms_step = g0.elapsed_time(g1) / steps
+    unis = [ix.ice_select(Qs[a.warmup + s], budget, beam)[1:] for s in range(steps)]
+    torch.cuda.synchronize()
+    pages = float(np.mean([float(n.sum()) for _, n in unis]))
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(5e7))
+    a0.record()
+    for s in range(steps):
+        ix.ice_attend(Qs[a.warmup + s], *unis[s])
+    a1.record()
+    torch.cuda.synchronize()
+    att_ms = a0.elapsed_time(a1) / steps
+    elt = 2 if dtype == "bf16" else 4
+    gbytes = pages * 16 * d * elt
+    gather_ms = max(att_ms - dev_attend_ms, 1e-6)
+    out = dict(ms_per_step=round(ms_step, 6), steps_per_s=round(1000.0 / ms_step, 3),
+               attend_with_gather_ms=round(att_ms, 6), gather_ms_est=round(gather_ms, 6),
+               gather_bytes=gbytes, link_gbs_est=round(gbytes / gather_ms / 1e6, 3),
+               build_ms=round(build_ms, 3), pool_bytes=ix.pool.nbytes, pool_alloc_s=round(alloc_s, 3))
+    print(f"[bench] host pool T={budget}: {ms_step*1000:.1f} us/step; gather of {gbytes/1e6:.1f} MB about "
+          f"{gather_ms*1000:.1f} us ({out['link_gbs_est']:.1f} GB/s); build {build_ms:.1f} ms",
+          file=sys.stderr, flush=True)
+    del ix
+    return out
+
+
 def cpu_baseline(w, Qs, budget, beam, heads, seed):
     """The fp64 oracle as it stands, on the host cores, on a bounded sample:
     its own index build of `heads` heads, then select + attend of those heads
@@ -353,6 +410,10 @@ def main():
               f"select {sel_ms*1000:.1f} us ({sb/sel_ms/1e6:.0f} GB/s) attend {att_ms*1000:.1f} us "
               f"({ab/att_ms/1e6:.0f} GB/s)", file=sys.stderr, flush=True)
 
+    host_pool = None
+    if not a.no_host_pool:
+        host_pool = time_host_pool(w, Qs, a, H, G, N, d, dtype, a.budget, results[a.budget]["attend_ms"], n_ins)
+
     # ---- insert: one token per head per step
     knew = [synth.new_tokens(w, gen, device=dev) for _ in range(n_ins)]
     torch.cuda.synchronize()
@@ -395,6 +456,8 @@ def main():
         "per_budget": {str(b): {k2: (round(v, 6) if isinstance(v, float) else v) for k2, v in r.items()}
                        for b, r in results.items()},
     }
+    if host_pool is not None:
+        out["host_pool"] = host_pool
     if not a.no_cpu:
         heads = list(range(min(a.cpu_heads, H)))
         t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(3)], a.budget, a.budget // 16,

@@ -63,8 +63,20 @@ typedef struct ice_params {
   int32_t  levels;        /* L in [1, ICE_MAX_LEVELS]: levels 0..L-1, bottom included      */
   int32_t  promote_log2;  /* promotion probability per level = 2^-promote_log2, in [1,16] */
   int32_t  capacity;      /* max tokens per head, build plus inserts, >= 1                */
+  uint32_t flags;         /* 0 or ICE_HOST_POOL                                           */
   uint64_t seed;          /* seed of the promotion draws                                  */
 } ice_params;
+
+/* Host-pool mode (the notes' overall framework, step 3, and the aitangshan.cn
+ * article, sections 4 and 5: the KV cache is offloaded to CPU memory and the
+ * selected pages are moved to the GPU in one bulk load per step). The
+ * level-0 V pages live in a caller-allocated pinned host pool instead of the
+ * device blob; keys, the index and the selection stay in device memory. Each
+ * ice_attend / ice_decode first gathers the V pages of the union from the
+ * pool into a staging area of the workspace (a GPU kernel reads them over the
+ * host link) and attends from there. Results equal the device-pool mode's
+ * bit for bit. */
+#define ICE_HOST_POOL 1u
 
 typedef struct ice_index ice_index;   /* opaque host-side handle */
 
@@ -75,15 +87,29 @@ size_t ice_index_bytes(const ice_params* p);
 
 /* Device bytes of the workspace that ice_build, ice_insert, ice_select and
  * ice_attend need for queries up to `max_budget_tokens` (a multiple of
- * page_cap) per query head. One workspace may be shared by successive calls
- * on one stream; it holds nothing between calls. 0 on invalid arguments. */
+ * page_cap) per query head (in host-pool mode this includes the V staging
+ * area, n_heads * group * max_budget_tokens / 16 pages). One workspace may be
+ * shared by successive calls on one stream; it holds nothing between calls.
+ * 0 on invalid arguments. */
 size_t ice_workspace_bytes(const ice_params* p, int32_t max_budget_tokens);
+
+/* Pinned host bytes of the V page pool in host-pool mode (0 without
+ * ICE_HOST_POOL or on invalid parameters). */
+size_t ice_host_pool_bytes(const ice_params* p);
 
 /* Creates a host handle over a caller-allocated device blob of at least
  * ice_index_bytes(p) bytes (256-byte aligned). The blob stays owned by the
  * caller and must outlive the handle. */
 int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_index** out);
 void ice_destroy(ice_index* idx);
+
+/* Host-pool mode: attaches the V page pool, at least ice_host_pool_bytes(p)
+ * bytes of pinned host memory (hipHostMalloc, or a pinned torch tensor),
+ * 256-byte aligned, that stays owned by the caller and must outlive the
+ * handle. The device reads and writes it directly. Required before
+ * ice_build; ICE_ERR_STATE without ICE_HOST_POOL, ICE_ERR_ARG if the memory
+ * is not pinned host memory the device can reach. */
+int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes);
 
 /* Index build at prefill (the framework's step 1; the article's section 3).
  * K, V: device, [H][n_tokens][d] with `head_stride` elements between heads
@@ -163,7 +189,8 @@ int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32
 #define ICE_EXP_TOP        9   /* int32 [top capacity] top-level points in order           */
 #define ICE_EXP_PAGE_K     10  /* dtype [pages][16][d] page-pool keys (level 0) / copies   */
 #define ICE_EXP_PAGE_V     11  /* dtype [pages][16][d] page-pool values (level 0 only; the
-                                  device stores each 4-slot group dimension-major) */
+                                  device stores each 4-slot group dimension-major; in
+                                  host-pool mode they are read from the host pool) */
 #define ICE_EXP_HEADER     12  /* ice_head_stats                                           */
 #define ICE_EXP_OWNER_RUN  13  /* int32 [capacity+1] pages of the owner's contiguous run   */
 #define ICE_EXP_OWNER_COUNT 14 /* int32 [capacity+1] members of the owner                  */

@@ -99,3 +99,46 @@ def test_create_rejects_small_or_misaligned_blobs(lib):
     assert lib.ice_create(ctypes.byref(p), ctypes.c_void_p(1 << 20), n - 1, ctypes.byref(h)) == L.ICE_ERR_CAPACITY
     assert lib.ice_create(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 64), n, ctypes.byref(h)) == L.ICE_ERR_ARG
     assert lib.ice_create(ctypes.byref(p), None, n, ctypes.byref(h)) == L.ICE_ERR_ARG
+
+
+def test_host_pool_sizes_and_checks(lib):
+    """Host-pool mode moves the level-0 V pages out of the device blob into a
+    pinned host pool of exactly those bytes; the pool must be attached before a
+    build, and only to an index created with the flag."""
+    H, G, d, cap = 3, 4, 128, 5000
+    dev = make_params(H, G, d, "bf16", cap)
+    host = make_params(H, G, d, "bf16", cap, host_pool=True)
+    assert lib.ice_host_pool_bytes(ctypes.byref(dev)) == 0
+    pool = lib.ice_host_pool_bytes(ctypes.byref(host))
+    hd = _fake_handle(lib, dev)
+    try:
+        pages0 = lib.ice_export_bytes(hd, L.ICE_EXP_PAGE_V, 0) // (16 * d * 2)
+    finally:
+        lib.ice_destroy(hd)
+    per_head = -(-pages0 * 16 * d * 2 // 256) * 256
+    assert pool == H * per_head
+    # the blob shrinks by about the V pool; the workspace grows by the staging area
+    shrink = lib.ice_index_bytes(ctypes.byref(dev)) - lib.ice_index_bytes(ctypes.byref(host))
+    assert per_head * H <= shrink <= per_head * H + 256 * H
+    grow = lib.ice_workspace_bytes(ctypes.byref(host), 256) - lib.ice_workspace_bytes(ctypes.byref(dev), 256)
+    assert grow >= 0
+    bad = make_params(H, G, d, "bf16", cap)
+    bad.flags = 6
+    assert lib.ice_index_bytes(ctypes.byref(bad)) == 0
+    # attach: refused without the flag, with a small, misaligned or null pool
+    hd = _fake_handle(lib, dev)
+    try:
+        assert lib.ice_attach_host_pool(hd, ctypes.c_void_p(1 << 20), pool) == L.ICE_ERR_STATE
+    finally:
+        lib.ice_destroy(hd)
+    hh = _fake_handle(lib, host)
+    try:
+        fake = ctypes.c_void_p(1 << 20)
+        ws_bytes = lib.ice_workspace_bytes(ctypes.byref(host), 256)
+        assert lib.ice_attach_host_pool(hh, None, pool) == L.ICE_ERR_ARG
+        assert lib.ice_attach_host_pool(hh, ctypes.c_void_p((1 << 20) + 64), pool) == L.ICE_ERR_ARG
+        assert lib.ice_attach_host_pool(hh, fake, pool - 1) == L.ICE_ERR_CAPACITY
+        # a build before the pool is attached
+        assert lib.ice_build(hh, fake, fake, 10, 10 * d, fake, ws_bytes, None) == L.ICE_ERR_STATE
+    finally:
+        lib.ice_destroy(hh)
