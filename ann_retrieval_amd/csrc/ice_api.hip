@@ -141,7 +141,9 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
   for (int l = 0; l < p->levels; ++l) W->off_exact[l] = w.take((int64_t)L->ncap[l] * 4);
   W->off_cnts = w.take(2 * ICE_MAX_LEVELS * 4);
   const int64_t n1 = p->levels >= 2 ? L->ncap[1] : 0;
-  W->off_opA = w.take(n1 * W->kp * elt);
+  // candidate operand rows, plus kGemmPadRows rows the parent GEMM may read
+  // past the last candidate (its stage loads carry no bounds checks)
+  W->off_opA = w.take((n1 + kGemmPadRows) * W->kp * elt);
   W->off_s1 = w.take(cap * 4);
   W->off_s2 = w.take(cap * 4);
   W->off_oloc = w.take(cap * 4);

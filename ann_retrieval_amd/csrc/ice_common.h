@@ -71,6 +71,10 @@ __host__ __device__ inline const char* v_pages(const DevLayout& L, const void* h
   return L.vpool ? L.vpool + (int64_t)h * L.vpool_head_bytes : static_cast<const char*>(hb) + L.off_pgV;
 }
 
+// Rows of the parent GEMM's candidate operand readable past the last
+// candidate: two 64-row stages.
+constexpr int kGemmPadRows = 128;
+
 // Build workspace, also laid out per head.
 struct WsLayout {
   int32_t kp;                    // padded reduction length of the parent GEMM operand

@@ -9,10 +9,13 @@
 // id (the candidates are in ascending token order).
 //
 // Layout (bf16, gfx950 v_mfma_f32_32x32x16_bf16): candidate parents are the
-// MFMA rows (A operand, streamed through LDS in tiles of 32), children the
-// columns (B operand, kept in registers for the whole sweep). Each lane then
-// owns one child column and 16 parent rows of every tile, so the argmax runs
-// inside the lane's accumulators with one cross-lane step at the end. The
+// MFMA rows (A operand, streamed through double-buffered LDS in stages of 64
+// rows, each stage's global loads issued before the previous stage's MFMAs),
+// children the columns (B operand, kept in registers for the whole sweep: two
+// 32-child fragments per wave, whose MFMA chains interleave). Each lane then
+// owns one child column per fragment and 16 parent rows of every 32-row
+// block, so the argmax runs inside the lane's accumulators (4 VALU operations
+// per score) with one cross-lane step at the end. The
 // e_i e_j term rides in one extra k-step: e is split into three bf16 parts
 // and six of the products are laid out as extra columns (the dropped terms
 // are below 2^-24 relative).
@@ -24,7 +27,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kChildPerBlock = 128;  // 4 waves x 32 children
+constexpr int kChildBf16 = 256;  // children per block: 4 waves x 64 (bf16), 4 waves x 32 (fp32)
+constexpr int kChildF32 = 128;
 
 struct GemmView {
   bool skip;
@@ -94,6 +98,26 @@ __device__ inline void write_parent(const DevLayout& L, const WsLayout& W, const
   if (a.second > -INFINITY && (a.best - a.second) < 1e-4f * (M2 - a.second)) atomicAdd(&v.hdr->near_ties, 1);
 }
 
+// Running best / runner-up of one lane over its rows of one child column,
+// branch-free: the runner-up is the median of (best, runner-up, s), the best
+// and its position move together on a strict comparison (rows arrive in
+// increasing order, so equal scores keep the lowest row). The position is
+// kept as (32-row block, accumulator j): j is a constant per score, and the
+// block is recorded once per block if any of its scores moved the best. The
+// lane's own row offset is added at the end.
+struct LaneMax {
+  float best = -INFINITY, second = -INFINITY;
+  int j = 0, blk = -1;
+  __device__ inline bool push(float s, int jj) {
+    const bool gt = s > best;
+    second = __builtin_amdgcn_fmed3f(best, second, s);
+    best = gt ? s : best;
+    j = gt ? jj : j;
+    return gt;
+  }
+  __device__ inline int row() const { return blk < 0 ? -1 : blk * 32 + 8 * (j >> 2) + (j & 3); }
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, void* blob, const uint16_t* K,
                                                      int64_t hstride, void* ws, int level) {
@@ -101,35 +125,42 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
   constexpr int KS = KP / 16;           // k-steps of 16
   constexpr int ROWB = KP * 2;          // operand row bytes
   constexpr int LDSB = ROWB + 16;       // padded LDS row stride
-  constexpr int TILE = 32;
-  __shared__ __attribute__((aligned(16))) char tile[TILE * LDSB];
+  constexpr int TILE = 64;              // candidate rows per stage (two 32-row MFMA blocks)
+  constexpr int CHUNKS = TILE * ROWB / 16;
+  constexpr int PF = (CHUNKS + 255) / 256;   // 16-byte loads per thread per stage
+  constexpr int NF = 2;                 // 32-child fragments per wave
+  __shared__ __attribute__((aligned(16))) char tile[2][TILE * LDSB];
 
   const GemmView v = gemm_view(L, W, blob, ws, level);
   if (v.skip) return;
-  const int c0 = blockIdx.x * kChildPerBlock;
+  const int c0 = blockIdx.x * kChildBf16;
   if (c0 >= v.n_child) return;
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* e = at<float>(head_base(blob, L, h), L.off_e);
   const uint16_t* Kh = K + (int64_t)h * hstride;
   const char* opA = reinterpret_cast<const char*>(at<uint16_t>(v.wh, W.off_opA));
-
-  // child operand: column lane%32, k elements 8*(lane/32) .. +7 of each step
-  const int ci = c0 + wave * 32 + (lane & 31);
-  const bool cvalid = ci < v.n_child;
-  const int ctok = cvalid ? v.exact[ci] : 0;
   const int half = lane >> 5;
-  bf16x8 bfr[KS];
+
+  // child operands: fragment f holds column lane%32 = child c0 + 64 wave + 32 f
+  // + lane%32, k elements 8*(lane/32) .. +7 of each step
+  int ctok[NF];
+  bool cvalid[NF];
+  bf16x8 bfr[NF][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS - 1; ++ks) {
+  for (int f = 0; f < NF; ++f) {
+    const int ci = c0 + wave * 64 + f * 32 + (lane & 31);
+    cvalid[f] = ci < v.n_child;
+    ctok[f] = cvalid[f] ? v.exact[ci] : 0;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      V4 x = {0, 0, 0, 0};
+      if (cvalid[f]) x = *reinterpret_cast<const V4*>(Kh + (int64_t)ctok[f] * D + ks * 16 + half * 8);
+      bfr[f][ks] = __builtin_bit_cast(bf16x8, x);
+    }
     V4 x = {0, 0, 0, 0};
-    if (cvalid) x = *reinterpret_cast<const V4*>(Kh + (int64_t)ctok * D + ks * 16 + half * 8);
-    bfr[ks] = __builtin_bit_cast(bf16x8, x);
-  }
-  {
-    V4 x = {0, 0, 0, 0};
-    if (cvalid && half == 0) {
-      const float ev = e[ctok];
+    if (cvalid[f] && half == 0) {
+      const float ev = e[ctok[f]];
       const uint16_t a0 = f32_to_bf16(ev);
       const float r1 = ev - bf16_to_f32(a0);
       const uint16_t a1 = f32_to_bf16(r1);
@@ -139,34 +170,100 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
       x.y = (uint32_t)a1 | ((uint32_t)a0 << 16);
       x.z = (uint32_t)a2 | ((uint32_t)a1 << 16);
     }
-    bfr[KS - 1] = __builtin_bit_cast(bf16x8, x);
+    bfr[f][KS - 1] = __builtin_bit_cast(bf16x8, x);
   }
 
-  ArgMax am;
-  constexpr int CHUNKS = TILE * ROWB / 16;
-  for (int p0 = 0; p0 < v.n_cand; p0 += TILE) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < CHUNKS; c += 256) {
-      const int r = c / (ROWB / 16), q = c % (ROWB / 16);
-      V4 x = {0, 0, 0, 0};
-      if (p0 + r < v.n_cand) x = *reinterpret_cast<const V4*>(opA + (int64_t)(p0 + r) * ROWB + q * 16);
-      *reinterpret_cast<V4*>(tile + r * LDSB + q * 16) = x;
-    }
-    __syncthreads();
-    f32x16 acc = {};
+  // Candidate stages: global -> registers (issued a stage ahead) -> LDS.
+  // Thread chunk i of a stage is fixed, so its global and LDS offsets are
+  // computed once; chunk indices past the stage repeat its last chunk (the
+  // same value to the same LDS address). The loads carry no bounds checks:
+  // the operand has kGemmPadRows readable rows past the last candidate, whose
+  // scores are never pushed.
+  static_assert(2 * TILE <= kGemmPadRows, "stage loads past the candidates");
+  uint32_t goff[PF], soff[PF];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const V4 a = *reinterpret_cast<const V4*>(tile + (lane & 31) * LDSB + ks * 32 + half * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bfr[ks], acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int p = p0 + 8 * (j >> 2) + 4 * half + (j & 3);
-      if (p < v.n_cand) am.push(acc[j], p);
-    }
+  for (int i = 0; i < PF; ++i) {
+    const int c = min(threadIdx.x + 256 * i, CHUNKS - 1);
+    const int r = c / (ROWB / 16), q = c % (ROWB / 16);
+    goff[i] = (uint32_t)(r * ROWB + q * 16);
+    soff[i] = (uint32_t)(r * LDSB + q * 16);
   }
-  am.merge_halves();
-  if (lane < 32 && cvalid) write_parent(L, W, v, blob, level, ctok, am);
+  auto fetch = [&](int p0, V4 (&pf)[PF]) {
+    const char* base = opA + (int64_t)p0 * ROWB;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) pf[i] = *reinterpret_cast<const V4*>(base + goff[i]);
+  };
+  auto stash = [&](char* buf, const V4 (&pf)[PF]) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) *reinterpret_cast<V4*>(buf + soff[i]) = pf[i];
+  };
+
+  LaneMax am[NF];
+  // one stage: the MFMAs and argmax of the rows in `cur`, with the next
+  // stage's loads in flight, then the next stage into `nxt`
+  auto stage = [&](int t, const char* cur, char* nxt) {
+    const int p0 = t * TILE;
+    V4 pf[PF];
+    fetch(p0 + TILE, pf);
+    const bool full = p0 + TILE <= v.n_cand;
+#pragma unroll
+    for (int rb = 0; rb < TILE / 32; ++rb) {
+      f32x16 acc[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const V4 a = *reinterpret_cast<const V4*>(cur + (rb * 32 + (lane & 31)) * LDSB + ks * 32 + half * 16);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bfr[f][ks], acc[f], 0, 0, 0);
+      }
+      // accumulator j of a lane is row 8 (j/4) + 4 half + j%4 of the block
+      const int rbase = p0 + rb * 32;
+      bool moved[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) moved[f] = false;
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+#pragma unroll
+          for (int f = 0; f < NF; ++f) moved[f] |= am[f].push(acc[f][j], j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const bool ok = rbase + 8 * (j >> 2) + 4 * half + (j & 3) < v.n_cand;
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            if (ok) moved[f] |= am[f].push(acc[f][j], j);
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) am[f].blk = moved[f] ? rbase / 32 : am[f].blk;
+    }
+    stash(nxt, pf);
+    __syncthreads();
+  };
+  const int n_tiles = (v.n_cand + TILE - 1) / TILE;
+  {
+    V4 pf[PF];
+    fetch(0, pf);
+    stash(tile[0], pf);
+  }
+  __syncthreads();
+  // stages in pairs, so each one's LDS buffers are fixed addresses
+  for (int t = 0; t < n_tiles; t += 2) {
+    stage(t, tile[0], tile[1]);
+    if (t + 1 < n_tiles) stage(t + 1, tile[1], tile[0]);
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    ArgMax a;
+    a.best = am[f].best;
+    a.second = am[f].second;
+    a.idx = am[f].row() >= 0 ? am[f].row() + 4 * half : 0x7fffffff;
+    a.merge_halves();
+    if (lane < 32 && cvalid[f]) write_parent(L, W, v, blob, level, ctok[f], a);
+  }
 }
 
 // fp32 inputs: v_mfma_f32_32x32x2f32, operand rows [key | e | 0 0 0].
@@ -181,7 +278,7 @@ __global__ __launch_bounds__(256) void k_parent_f32(DevLayout L, WsLayout W, voi
 
   const GemmView v = gemm_view(L, W, blob, ws, level);
   if (v.skip) return;
-  const int c0 = blockIdx.x * kChildPerBlock;
+  const int c0 = blockIdx.x * kChildF32;
   if (c0 >= v.n_child) return;
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -230,7 +327,8 @@ __global__ __launch_bounds__(256) void k_parent_f32(DevLayout L, WsLayout W, voi
 hipError_t launch_parent_gemm(const DevLayout& L, const WsLayout& W, void* blob, const void* K,
                               int64_t head_stride, void* ws, int level, hipStream_t s) {
   const int n_child_max = L.ncap[level];
-  const dim3 grid((unsigned)((n_child_max + kChildPerBlock - 1) / kChildPerBlock), (unsigned)L.H);
+  const int per = L.dtype == ICE_BF16 ? kChildBf16 : kChildF32;
+  const dim3 grid((unsigned)((n_child_max + per - 1) / per), (unsigned)L.H);
   if (grid.x == 0) return hipSuccess;
   if (L.dtype == ICE_BF16) {
     const uint16_t* Kb = static_cast<const uint16_t*>(K);
