@@ -113,6 +113,9 @@ def short_name(name):
 def summarize(paths, command, copy_mib, workload):
     """Markdown summary of rocprofv3 CSV output (kernel stats, or counters)."""
     out = [f"Command: `{command}`", ""]
+    if len(paths) == 1 and "counter_collection" in paths[0]:
+        print("\n".join(out + summarize_mfma(paths[0])))
+        return
     if len(paths) == 1:
         rows = list(csv.DictReader(open(paths[0])))
         out += ["| Kernel | Calls | Average (us) | Min (us) | Max (us) | Time share (%) |", "|---|---|---|---|---|---|"]
@@ -150,6 +153,34 @@ def summarize(paths, command, copy_mib, workload):
             lines.append(f"traffic {base} workload={workload} bytes_per_launch={tot:.0f} source={source_hash(base)}")
     out += ["", "Recorded for bench.py (the kernel's sources must still hash the same):", "", "```"] + lines + ["```"]
     print("\n".join(out))
+
+
+def summarize_mfma(path):
+    """Matrix-core use per dispatch of the library's MFMA kernels from one
+    counter run of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_INSTS_VALU and
+    GRBM_GUI_ACTIVE. GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the
+    dispatch's busy window is GRBM_GUI_ACTIVE / 8 GPU cycles; utilisation =
+    MFMA busy cycles / (window x 1024 SIMDs)."""
+    disp = {}
+    for r in csv.DictReader(open(path)):
+        k = short_name(r["Kernel_Name"])
+        if not k.startswith("k_"):
+            continue
+        key = (k, r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+        disp.setdefault(key, {})[r["Counter_Name"]] = disp.setdefault(key, {}).get(r["Counter_Name"], 0.0) + \
+            float(r["Counter_Value"])
+    out = ["| Kernel | Dispatch | GPU cycles (window) | MFMA instructions | VALU instructions | VALU / MFMA | "
+           "MFMA busy (% of 1024 SIMDs) |", "|---|---|---|---|---|---|---|"]
+    for (k, d), c in sorted(disp.items(), key=lambda x: (x[0][0], int(x[0][1]) if str(x[0][1]).isdigit() else 0)):
+        mf = c.get("SQ_INSTS_MFMA", 0.0)
+        if mf <= 0:
+            continue
+        win = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        util = 100.0 * busy / (win * 1024) if win else float("nan")
+        va = c.get("SQ_INSTS_VALU", 0.0)
+        out.append(f"| `{k}` | {d} | {win:.0f} | {mf:.0f} | {va:.0f} | {va / mf:.1f} | {util:.1f} |")
+    return out
 
 
 def algorithmic_bytes(ix, trace, uni_n, n_uni, d, elt, G):
