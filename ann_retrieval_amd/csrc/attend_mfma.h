@@ -93,47 +93,61 @@ __host__ __device__ inline int part_floats(int nw, int G, int D) {
   return 8 * D + 2 * nw * ICE_MAX_GROUP + nw * G * D;
 }
 
-// Attention of head h for its G query heads over the nu page ids u[0..nu)
-// (global or LDS; ids outside the head's page table are skipped). Qh: the
-// head's [G][D] queries; Oh: [G][D] outputs; lseh nullable. part: LDS of
-// part_floats(nw, G, D) floats; nw: waves of the block (all of them call).
-template <int D, bool PREFETCH_V>
-__device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* Qh, int G, const int32_t* u, int nu,
-                            float scale, float* Oh, float* lseh, float* part, int nw) {
+// One wave's running softmax state over the pages it has attended: base m
+// and sum l of its lane's query, and O^T accumulators.
+template <int D>
+struct WaveAcc {
+  float m, l;
+  float4v acc[MGeo<D>::VC];
+  __device__ inline void init() {
+    m = -INFINITY;
+    l = 0.0f;
+#pragma unroll
+    for (int c = 0; c < MGeo<D>::VC; ++c) acc[c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+};
+
+// The Q^T operand in LDS (read once per page), queries past G zero: every
+// thread of the block takes part; the caller synchronises before use.
+template <int D>
+__device__ inline void stage_q(const uint16_t* Qh, int G, float* part) {
   using M = MGeo<D>;
   V4* q_lds = reinterpret_cast<V4*>(part);          // [KC][4 parts][16 queries]: lane l reads entry c*64 + l
-  float* part_m = part + 8 * D;
-  float* part_l = part_m + nw * ICE_MAX_GROUP;
-  float* part_o = part_l + nw * ICE_MAX_GROUP;     // [nw][G][D]
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int qn = lane & 15, qt = lane >> 4;     // query (B column, S^T column) and 4-token group
-  const char* pgK = at<char>(hb, L.off_pgK[0]);
-  // one block per head; with staged V the page of union entry u is entry u
-  // of the head's staging area, else the page id itself
-  const int h = blockIdx.x;
-  const bool staged = L.vstage != nullptr;
-  const char* pgV = staged ? L.vstage + (int64_t)h * L.vstage_pages * (ICE_PAGE_CAP * M::ROWB) : v_pages(L, hb, h);
-  const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
-  const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
-  const float c2 = scale * kLog2e;
-  // Q^T operand in LDS (read once per page): queries past G are zero
   for (int t = threadIdx.x; t < M::KC * 16 * 4; t += blockDim.x) {
     const int c = t / 64, part4 = (t >> 4) & 3, q = t & 15;     // entry c*64 + lane of lane (q, part4)
     const V4 x = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Qh + (int64_t)min(q, G - 1) * D) +
                                                64 * c + 16 * part4);
     q_lds[t] = q < G ? x : V4{0, 0, 0, 0};
   }
-  __syncthreads();
-  float m = -INFINITY, l = 0.0f;
+}
+
+// One wave attends pages u[wi], u[wi + ws], ... of the nu page ids u[0..nu)
+// (global or LDS; ids outside the head's page table are skipped) for the
+// head's G query heads, into `st`. part holds the staged Q^T. With staged V
+// (host-pool mode) the V page of list entry i is staging entry i.
+template <int D, bool PREFETCH_V>
+__device__ void attend_pages(const DevLayout& L, const void* hb, int h, int G, const int32_t* u, int nu, int wi,
+                             int ws, float c2, const float* part, WaveAcc<D>& st) {
+  using M = MGeo<D>;
+  const V4* q_lds = reinterpret_cast<const V4*>(part);
+  const int lane = threadIdx.x & 63;
+  const int qt = lane >> 4;     // 4-token group of the lane (its query is lane % 16)
+  const char* pgK = at<char>(hb, L.off_pgK[0]);
+  const bool staged = L.vstage != nullptr;
+  const char* pgV = staged ? L.vstage + (int64_t)h * L.vstage_pages * (ICE_PAGE_CAP * M::ROWB) : v_pages(L, hb, h);
+  const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
+  const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
+  float m = st.m, l = st.l;
   float4v acc[M::VC];
 #pragma unroll
-  for (int c = 0; c < M::VC; ++c) acc[c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = 0; c < M::VC; ++c) acc[c] = st.acc[c];
+  (void)G;
 
-  const int npw = nu > wv ? (nu - wv + nw - 1) / nw : 0;
+  const int npw = nu > wi ? (nu - wi + ws - 1) / ws : 0;
   for (int k0 = 0; k0 < npw; k0 += 64) {
     int my_pg = -1, my_cnt = 0;
     if (k0 + lane < npw) {
-      my_pg = u[wv + nw * (k0 + lane)];
+      my_pg = u[wi + ws * (k0 + lane)];
       if (my_pg < 0 || my_pg >= n_pages) my_pg = -1;
       else my_cnt = pg_cnt[my_pg];
     }
@@ -149,7 +163,7 @@ __device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* 
       const int pg = __shfl(my_pg, kc, 64), cnt = __shfl(my_cnt, kc, 64);
       const bool ok = k < nk && pg >= 0;
       mload_k<D>(pgK, ok ? pg : 0, ok ? cnt : 0, lane, b);
-      if constexpr (PREFETCH_V) mload_v<D>(pgV, ok ? (staged ? wv + nw * (k0 + kc) : pg) : 0, ok ? cnt : 0, lane, b.v);
+      if constexpr (PREFETCH_V) mload_v<D>(pgV, ok ? (staged ? wi + ws * (k0 + kc) : pg) : 0, ok ? cnt : 0, lane, b.v);
     };
     issue(0, bufA);
     auto step = [&](int k, MPage<D>& cur, MPage<D>& nxt) {
@@ -157,7 +171,7 @@ __device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* 
       const int pg_k = __shfl(my_pg, kc, 64), cnt_k = __shfl(my_cnt, kc, 64);
       const int cnt = k < nk && pg_k >= 0 ? cnt_k : 0;      // 0: nothing to attend
       uint2 vcur[M::VC];
-      if constexpr (!PREFETCH_V) mload_v<D>(pgV, cnt > 0 ? (staged ? wv + nw * (k0 + kc) : pg_k) : 0, cnt, lane, vcur);
+      if constexpr (!PREFETCH_V) mload_v<D>(pgV, cnt > 0 ? (staged ? wi + ws * (k0 + kc) : pg_k) : 0, cnt, lane, vcur);
       issue(k + 1, nxt);
       float4v s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -213,41 +227,74 @@ __device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* 
       step(k + 1, bufB, bufA);
     }
   }
-  // wave partials: m, l and o of query qn (every lane group holds m and l;
-  // lane group qt holds dims 16c + 4qt + j)
+  st.m = m;
+  st.l = l;
+#pragma unroll
+  for (int c = 0; c < M::VC; ++c) st.acc[c] = acc[c];
+}
+
+// A wave's partials (m, l and o of query qn; every lane group holds m and l,
+// lane group qt holds dims 16c + 4qt + j) into slot wv of the LDS partials.
+template <int D>
+__device__ inline void write_partial(const WaveAcc<D>& st, int wv, int G, float* part, int nw) {
+  using M = MGeo<D>;
+  float* part_m = part + 8 * D;
+  float* part_l = part_m + nw * ICE_MAX_GROUP;
+  float* part_o = part_l + nw * ICE_MAX_GROUP;     // [nw][G][D]
+  const int lane = threadIdx.x & 63;
+  const int qn = lane & 15, qt = lane >> 4;
   if (qt == 0 && qn < G) {
-    part_m[wv * ICE_MAX_GROUP + qn] = m;
-    part_l[wv * ICE_MAX_GROUP + qn] = l;
+    part_m[wv * ICE_MAX_GROUP + qn] = st.m;
+    part_l[wv * ICE_MAX_GROUP + qn] = st.l;
   }
   if (qn < G)
 #pragma unroll
     for (int c = 0; c < M::VC; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part_o[(wv * G + qn) * D + 16 * c + 4 * qt + j] = acc[c][j];
-  __syncthreads();
-  // merge: per query the common base, the total weight and each wave's
-  // normalised factor (one thread per query), then every output element
-  for (int q = threadIdx.x; q < G; q += blockDim.x) {
+      for (int j = 0; j < 4; ++j) part_o[(wv * G + qn) * D + 16 * c + 4 * qt + j] = st.acc[c][j];
+}
+
+// Merges the nw waves' partials (after a block barrier that follows every
+// write_partial) in one pass: every output element's thread forms its
+// query's common base, total weight and the waves' normalised factors itself
+// (the reads of one query's m and l are LDS broadcasts across a wave).
+template <int D>
+__device__ inline void merge_partials(int G, const float* part, int nw, float* Oh, float* lseh) {
+  const float* part_m = part + 8 * D;
+  const float* part_l = part_m + nw * ICE_MAX_GROUP;
+  const float* part_o = part_l + nw * ICE_MAX_GROUP;
+  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
+    const int q = t / D, dd = t % D;
     float Mx = -INFINITY;
     for (int w = 0; w < nw; ++w) Mx = fmaxf(Mx, part_m[w * ICE_MAX_GROUP + q]);
-    float Ls = 0.0f;
+    float Ls = 0.0f, a = 0.0f;
     for (int w = 0; w < nw; ++w) {
       const float mw = part_m[w * ICE_MAX_GROUP + q];
       const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - Mx);
-      part_m[w * ICE_MAX_GROUP + q] = f;         // this thread's column only
       Ls = fmaf(part_l[w * ICE_MAX_GROUP + q], f, Ls);
+      a = fmaf(part_o[(w * G + q) * D + dd], f, a);
     }
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    for (int w = 0; w < nw; ++w) part_m[w * ICE_MAX_GROUP + q] *= inv;
-    if (lseh) lseh[q] = Ls > 0.0f ? (Mx + __log2f(Ls)) * kLn2 : -INFINITY;
+    Oh[(int64_t)q * D + dd] = Ls > 0.0f ? a / Ls : 0.0f;
+    if (lseh && dd == 0) lseh[q] = Ls > 0.0f ? (Mx + __log2f(Ls)) * kLn2 : -INFINITY;
   }
+}
+
+// Attention of head h for its G query heads over the nu page ids u[0..nu),
+// by the whole block: wave w takes pages w, w + nw, ... Qh: the head's
+// [G][D] queries; Oh: [G][D] outputs; lseh nullable. part: LDS of
+// part_floats(nw, G, D) floats; nw: waves of the block (all of them call).
+template <int D, bool PREFETCH_V>
+__device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* Qh, int G, const int32_t* u, int nu,
+                            float scale, float* Oh, float* lseh, float* part, int nw) {
+  const int wv = threadIdx.x >> 6;
+  stage_q<D>(Qh, G, part);
   __syncthreads();
-  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
-    const int q = t / D, dd = t % D;
-    float a = 0.0f;
-    for (int w = 0; w < nw; ++w) a = fmaf(part_o[(w * G + q) * D + dd], part_m[w * ICE_MAX_GROUP + q], a);
-    Oh[(int64_t)q * D + dd] = a;
-  }
+  WaveAcc<D> st;
+  st.init();
+  attend_pages<D, PREFETCH_V>(L, hb, blockIdx.x, G, u, nu, wv, nw, scale * kLog2e, part, st);
+  write_partial<D>(st, wv, G, part, nw);
+  __syncthreads();
+  merge_partials<D>(G, part, nw, Oh, lseh);
 }
 
 }  // namespace mfma_attend

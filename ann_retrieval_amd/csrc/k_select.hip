@@ -442,13 +442,126 @@ __device__ inline uint64_t chunk_keys(const Quarter<D, T>& qs, const bool (&ok)[
   return grp == 0 ? x0 : grp == 1 ? x1 : grp == 2 ? x2 : x3;
 }
 
+// The union of tot <= 64 selections (sel_all, LDS) by one wave: a 64-lane
+// bitonic sort, then the first of each run of equal ids; writes urow
+// (ascending, -1 padded to tot) and uni_lds (nullable). Returns its size.
+__device__ inline int wave_union64(int tot, const int32_t* sel_all, int32_t* urow, int32_t* uni_lds, int lane) {
+  int v = lane < tot ? sel_all[lane] : INT_MAX;
+  if (v < 0) v = INT_MAX;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      const int y = __shfl_xor(v, jj, 64);
+      v = (((lane & k) == 0) == ((lane & jj) == 0)) ? min(v, y) : max(v, y);
+    }
+  }
+  const int prev = __shfl_up(v, 1, 64);
+  const bool keep = v != INT_MAX && (lane == 0 || v != prev);
+  const uint64_t m = __ballot(keep);
+  const int n = __popcll(m);
+  if (keep) {
+    const int pos = __popcll(m & ((1ull << lane) - 1ull));
+    urow[pos] = v;
+    if (uni_lds) uni_lds[pos] = v;
+  }
+  if (lane >= n && lane < tot) urow[lane] = -1;
+  return n;
+}
+
+// Union over the group of the G*kpg selections in sel_all (LDS), ascending
+// page id, -1 padded, into uni row h and n_uni[h]; uni_lds (nullable) gets a
+// copy. Called by the whole block after a barrier; sel_all (union_pad(G*kpg)
+// ints) and wn (kMaxWaves ints) are LDS scratch. Returns the union's size in
+// every thread.
+__device__ int write_union(int G, int kpg, int32_t* sel_all, int32_t* wn, int32_t* uni, int32_t* n_uni, int h,
+                           int32_t* uni_lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // ---- union over the group, ascending page id, -1 padded
+  const int tot = G * kpg;
+  int32_t* urow = uni + (int64_t)h * tot;
+  if (tot <= 64) {
+    if (wv == 0) {
+      const int n = wave_union64(tot, sel_all, urow, uni_lds, lane);
+      if (lane == 0) {
+        n_uni[h] = n;
+        wn[0] = n;
+      }
+    }
+    __syncthreads();
+    return wn[0];
+  }
+  // long selections: bitonic sort of the padded list in LDS (empty = INT_MAX),
+  // then keep the first of each run of equal ids
+  const int P = union_pad(tot), nthr = blockDim.x, nw = nthr >> 6;
+  for (int i = tid; i < P; i += nthr) {
+    const int v = i < tot ? sel_all[i] : -1;
+    sel_all[i] = v < 0 ? INT_MAX : v;
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < P; i += nthr) {
+        const int l = i ^ jj;
+        if (l > i) {
+          const int a = sel_all[i], b = sel_all[l];
+          if (((i & k) == 0) == (a > b)) {
+            sel_all[i] = b;
+            sel_all[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t* wcount = wn;   // per-wave counts of a round
+  int base = 0;
+  for (int r0 = 0; r0 < P; r0 += nthr) {
+    const int i = r0 + tid;
+    const int v = i < P ? sel_all[i] : INT_MAX;
+    const bool keep = v != INT_MAX && (i == 0 || sel_all[i - 1] != v);
+    const uint64_t m = __ballot(keep);
+    if (lane == 0) wcount[wv] = __popcll(m);
+    __syncthreads();
+    int before = base, all = base;
+    for (int w2 = 0; w2 < nw; ++w2) {
+      before += w2 < wv ? wcount[w2] : 0;
+      all += wcount[w2];
+    }
+    if (keep) {
+      const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
+      urow[pos] = v;
+      if (uni_lds) uni_lds[pos] = v;
+    }
+    base = all;
+    __syncthreads();
+  }
+  for (int i = base + tid; i < tot; i += nthr) urow[i] = -1;
+  if (tid == 0) n_uni[h] = base;
+  return base;
+}
+
+// Claims of the fused decode step (LDS): a bit per page id of the head, and
+// per query head the pages it claimed first and their count.
+struct ClaimLds {
+  uint32_t* bits;
+  int32_t* pages;     // [G][kpg]
+  int32_t* count;     // [G]
+  int32_t* done;      // query heads whose claims are complete (zero on entry)
+};
+
 // Selection of head h by the whole block; returns the size of the group's
 // union (in every thread). uni_lds (nullable, LDS outside the selection's
 // area) receives a copy of the union. Ends with a block barrier, after which
-// the selection's LDS area is free.
+// the selection's LDS area is free. With `cl` (the fused decode step) it
+// writes no union: each query head's waves leave as soon as its lead has
+// claimed the query head's pages not yet claimed by another (cl->pages,
+// cl->count; the claim bits must be zero on entry), and the caller writes the
+// union with write_union after a block barrier.
 template <int D, class T, bool BIG>
 __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int budget, int beam, int32_t* sel,
-                           int32_t* uni, int32_t* n_uni, int32_t* trace, char* smem, int h, int32_t* uni_lds) {
+                           int32_t* uni, int32_t* n_uni, int32_t* trace, char* smem, int h, int32_t* uni_lds,
+                           const ClaimLds* cl = nullptr) {
   using QG = Quarter<D, T>;
   using Top = std::conditional_t<BIG, LdsTop, RegTop>;
   const int G = L.G, W = waves_per_query(G);
@@ -679,88 +792,36 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
     }
     combine(tl, kpg, -1, -1);
   }
+  if (cl) {
+    // the query head's selected pages that no other query head of the group
+    // has claimed yet, in selection order: these its waves attend
+    if (lead) {
+      const int p = lane < kpg ? sel_all[g * kpg + lane] : -1;
+      bool mine = false;
+      if (p >= 0) {
+        const uint32_t bit = 1u << (p & 31);
+        mine = (atomicOr(&cl->bits[p >> 5], bit) & bit) == 0u;
+      }
+      const uint64_t mk = __ballot(mine);
+      if (mine) cl->pages[g * kpg + __popcll(mk & ((1ull << lane) - 1ull))] = p;
+      if (lane == 0) cl->count[g] = __popcll(mk);
+      // the last query head to finish sees every selection: it writes the
+      // union right away when one wave can sort it
+      int done = 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) done = atomicAdd(cl->done, 1);
+      done = __shfl(done, 0, 64);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (done == G - 1 && G * kpg <= 64) {
+        const int n = wave_union64(G * kpg, sel_all, uni + (int64_t)h * G * kpg, nullptr, lane);
+        if (lane == 0) n_uni[h] = n;
+      }
+    }
+    qsync();
+    return 0;
+  }
   __syncthreads();      // every query head's selection is in sel_all
-  // ---- union over the group, ascending page id, -1 padded
-  const int tot = G * kpg;
-  int32_t* urow = uni + (int64_t)h * tot;
-  if (tot <= 64) {
-    if (wv == 0) {
-      int v = lane < tot ? sel_all[lane] : INT_MAX;
-      if (v < 0) v = INT_MAX;
-#pragma unroll
-      for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-          const int y = __shfl_xor(v, jj, 64);
-          v = (((lane & k) == 0) == ((lane & jj) == 0)) ? min(v, y) : max(v, y);
-        }
-      }
-      const int prev = __shfl_up(v, 1, 64);
-      const bool keep = v != INT_MAX && (lane == 0 || v != prev);
-      const uint64_t m = __ballot(keep);
-      const int n = __popcll(m);
-      if (keep) {
-        const int pos = __popcll(m & ((1ull << lane) - 1ull));
-        urow[pos] = v;
-        if (uni_lds) uni_lds[pos] = v;
-      }
-      if (lane >= n && lane < tot) urow[lane] = -1;
-      if (lane == 0) {
-        n_uni[h] = n;
-        wn[0] = n;
-      }
-    }
-    __syncthreads();
-    return wn[0];
-  }
-  // long selections: bitonic sort of the padded list in LDS (empty = INT_MAX),
-  // then keep the first of each run of equal ids
-  const int P = union_pad(tot), nthr = blockDim.x, nw = nthr >> 6;
-  for (int i = tid; i < P; i += nthr) {
-    const int v = i < tot ? sel_all[i] : -1;
-    sel_all[i] = v < 0 ? INT_MAX : v;
-  }
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < P; i += nthr) {
-        const int l = i ^ jj;
-        if (l > i) {
-          const int a = sel_all[i], b = sel_all[l];
-          if (((i & k) == 0) == (a > b)) {
-            sel_all[i] = b;
-            sel_all[l] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  int32_t* wcount = wn;   // per-wave counts of a round
-  int base = 0;
-  for (int r0 = 0; r0 < P; r0 += nthr) {
-    const int i = r0 + tid;
-    const int v = i < P ? sel_all[i] : INT_MAX;
-    const bool keep = v != INT_MAX && (i == 0 || sel_all[i - 1] != v);
-    const uint64_t m = __ballot(keep);
-    if (lane == 0) wcount[wv] = __popcll(m);
-    __syncthreads();
-    int before = base, all = base;
-    for (int w2 = 0; w2 < nw; ++w2) {
-      before += w2 < wv ? wcount[w2] : 0;
-      all += wcount[w2];
-    }
-    if (keep) {
-      const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
-      urow[pos] = v;
-      if (uni_lds) uni_lds[pos] = v;
-    }
-    base = all;
-    __syncthreads();
-  }
-  for (int i = base + tid; i < tot; i += nthr) urow[i] = -1;
-  if (tid == 0) n_uni[h] = base;
-  return base;
+  return write_union(G, kpg, sel_all, wn, uni, n_uni, h, uni_lds);
 }
 
 template <int D, class T, bool BIG>
@@ -771,32 +832,60 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
 }
 
 // ---- the fused decode step: selection, then attention over the union -------
-// LDS: the selection's area, then the union copy; attention's partials reuse
-// the selection's area once the selection is done.
+// Each query head's waves attend the pages it claimed as soon as its own
+// selection ends, while the block's other query heads are still selecting;
+// the union is then exactly the claimed pages, each attended once, for all G
+// query heads. The waves' partials are merged after one block barrier.
+// LDS: the selection's area, attention's Q^T and partials, the claim bits
+// (one per page id of the head), the claimed pages and their counts.
 struct DecLds {
-  int off_uni, total;
+  int off_part, off_bits, off_pages, off_count, words, total;
 };
-__host__ __device__ inline DecLds dec_lds(int G, int beam, int kpg, int nw, int D) {
+__host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+__host__ __device__ inline DecLds dec_lds(int G, int beam, int kpg, int nw, int D, int pcap0) {
   const SelLds S = sel_lds(G, max(beam, kpg), kpg, false);
-  const int part = mfma_attend::part_floats(nw, G, D) * 4;
   DecLds d;
-  d.off_uni = ((S.total > part ? S.total : part) + 15) & ~15;
-  d.total = d.off_uni + G * kpg * 4;
+  d.off_part = align16(S.total);
+  d.off_bits = align16(d.off_part + mfma_attend::part_floats(nw, G, D) * 4);
+  d.words = (pcap0 + 31) / 32;
+  d.off_pages = align16(d.off_bits + d.words * 4);
+  d.off_count = d.off_pages + G * kpg * 4;
+  d.total = align16(d.off_count + (G + 1) * 4);
   return d;
 }
+constexpr int kDecodeMaxLds = 160 * 1024;
 
 template <int D>
 __global__ __launch_bounds__(1024) void k_decode(DevLayout L, const void* blob, const uint16_t* Q, int budget,
                                                  int beam, int32_t* sel, int32_t* uni, int32_t* n_uni, float scale,
                                                  float* O, float* lse) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int h = blockIdx.x, G = L.G, nw = blockDim.x >> 6;
-  const DecLds DL = dec_lds(G, beam, budget / ICE_PAGE_CAP, nw, D);
-  int32_t* uni_lds = reinterpret_cast<int32_t*>(smem + DL.off_uni);
-  const int nu = select_head<D, uint16_t, false>(L, blob, Q, budget, beam, sel, uni, n_uni, nullptr, smem, h, uni_lds);
-  mfma_attend::attend_head<D, false>(L, head_base(blob, L, h), Q + (int64_t)h * G * D, G, uni_lds, nu, scale,
-                              O + (int64_t)h * G * D, lse ? lse + (int64_t)h * G : nullptr,
-                              reinterpret_cast<float*>(smem), nw);
+  const int h = blockIdx.x, G = L.G, nw = blockDim.x >> 6, kpg = budget / ICE_PAGE_CAP;
+  const DecLds DL = dec_lds(G, beam, kpg, nw, D, L.pcap[0]);
+  float* part = reinterpret_cast<float*>(smem + DL.off_part);
+  ClaimLds cl{reinterpret_cast<uint32_t*>(smem + DL.off_bits), reinterpret_cast<int32_t*>(smem + DL.off_pages),
+              reinterpret_cast<int32_t*>(smem + DL.off_count), reinterpret_cast<int32_t*>(smem + DL.off_count) + G};
+  const uint16_t* Qh = Q + (int64_t)h * G * D;
+  // ordered before any use by the selection's first block barrier
+  mfma_attend::stage_q<D>(Qh, G, part);
+  for (int i = threadIdx.x; i < DL.words; i += blockDim.x) cl.bits[i] = 0u;
+  if (threadIdx.x == 0) *cl.done = 0;
+  select_head<D, uint16_t, false>(L, blob, Q, budget, beam, sel, uni, n_uni, nullptr, smem, h, nullptr, &cl);
+  const int W = waves_per_query(G), wv = threadIdx.x >> 6, g = wv / W, j = wv % W;
+  mfma_attend::WaveAcc<D> st;
+  st.init();
+  mfma_attend::attend_pages<D, false>(L, head_base(blob, L, h), h, G, cl.pages + g * kpg, cl.count[g], j, W,
+                                      scale * mfma_attend::kLog2e, part, st);
+  mfma_attend::write_partial<D>(st, wv, G, part, nw);
+  __syncthreads();
+  mfma_attend::merge_partials<D>(G, part, nw, O + (int64_t)h * G * D, lse ? lse + (int64_t)h * G : nullptr);
+  // a union too long for one wave: written by the block from the selections
+  // (the selection's LDS is untouched by the attention)
+  if (G * kpg > 64) {
+    const SelLds S = sel_lds(G, max(beam, kpg), kpg, false);
+    write_union(G, kpg, reinterpret_cast<int32_t*>(smem + S.off_sel), reinterpret_cast<int32_t*>(smem + S.off_misc),
+                uni, n_uni, h, nullptr);
+  }
 }
 
 template <int D, class T>
@@ -817,7 +906,7 @@ void launch_decode_typed(const DevLayout& L, const void* blob, const void* Qv, i
                          int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse, hipStream_t s) {
   const int kpg = budget / ICE_PAGE_CAP;
   const int nw = waves_per_query(L.G) * L.G;
-  const DecLds DL = dec_lds(L.G, beam, kpg, nw, D);
+  const DecLds DL = dec_lds(L.G, beam, kpg, nw, D, L.pcap[0]);
   k_decode<D><<<dim3((unsigned)L.H), dim3(64 * nw), (size_t)DL.total, s>>>(
       L, blob, static_cast<const uint16_t*>(Qv), budget, beam, sel, uni, n_uni, scale, O, lse);
 }
@@ -826,7 +915,9 @@ void launch_decode_typed(const DevLayout& L, const void* blob, const void* Qv, i
 
 bool decode_fused(const DevLayout& L, int budget, int beam) {
   const int kpg = budget / ICE_PAGE_CAP;
-  return L.dtype == ICE_BF16 && (beam > kpg ? beam : kpg) <= 64;
+  if (L.dtype != ICE_BF16 || (beam > kpg ? beam : kpg) > 64) return false;
+  const int nw = waves_per_query(L.G) * L.G;
+  return dec_lds(L.G, beam, kpg, nw, L.d, L.pcap[0]).total <= kDecodeMaxLds;
 }
 
 hipError_t launch_decode(const DevLayout& L, const void* blob, const void* Q, int budget, int beam, int32_t* sel,
