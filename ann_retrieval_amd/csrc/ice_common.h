@@ -229,7 +229,6 @@ __device__ inline void wave_sync() {
 // the wave must be active.
 template <int m>
 __device__ inline int xor_lane(int x) {
-  const int lane = __lane_id();
   if constexpr (m == 1) {
     return __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false);     // quad_perm [1,0,3,2]
   } else if constexpr (m == 2) {
@@ -240,12 +239,13 @@ __device__ inline int xor_lane(int x) {
   } else if constexpr (m == 8) {
     return __builtin_amdgcn_mov_dpp(x, 0x128, 0xf, 0xf, false);    // row_ror:8
   } else if constexpr (m == 16) {
+    // lanes with bit 4 set take the swapped-in lower row (a constant lane mask)
     const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? (int)p[0] : (int)p[1];
+    return __builtin_amdgcn_inverse_ballot_w64(0xffff0000ffff0000ull) ? (int)p[0] : (int)p[1];
   } else {
     static_assert(m == 32, "xor distance");
     const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? (int)p[0] : (int)p[1];
+    return __builtin_amdgcn_inverse_ballot_w64(0xffffffff00000000ull) ? (int)p[0] : (int)p[1];
   }
 }
 template <int m>

@@ -107,12 +107,28 @@ __device__ inline uint64_t shfl64(uint64_t v, int src) {
 }
 __device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// Compare-exchange of lanes i and i ^ j: a lane with keep_max set keeps the
-// larger of its key and its partner's, the other the smaller. For j = 16, 32
-// the permlane swap leaves the pair's two keys in (a, b) of both lanes, in
-// the same order, which is all a compare-exchange needs.
+// Lane masks of the networks, as compile-time constants: bit i is lane i's
+// flag. The compare-exchanges take them through inverse ballots, so a
+// direction costs one scalar operation and no vector work.
+__host__ __device__ constexpr uint64_t lanes_where_zero(int m) {      // (lane & m) == 0
+  uint64_t r = 0;
+  for (int i = 0; i < 64; ++i)
+    if ((i & m) == 0) r |= 1ull << i;
+  return r;
+}
+// step (k, j) of a bitonic sort keeps the larger key where (lane & k) == 0
+// and (lane & j) == 0 agree (blocks of k lanes alternate direction)
+__host__ __device__ constexpr uint64_t sort_keep_max(int k, int j) {
+  return ~(lanes_where_zero(k) ^ lanes_where_zero(j));
+}
+
+// Compare-exchange of lanes i and i ^ j: a lane whose bit is set in
+// `keep_max` (a wave-uniform mask) keeps the larger of its key and its
+// partner's, the other the smaller. For j = 16, 32 the permlane swap leaves
+// the pair's two keys in (a, b) of both lanes, in the same order, which is
+// all a compare-exchange needs.
 template <int j>
-__device__ inline uint64_t cx64(uint64_t x, bool keep_max) {
+__device__ inline uint64_t cx64(uint64_t x, uint64_t keep_max) {
   uint64_t a = x, b;
   if constexpr (j >= 16) {
     const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
@@ -132,53 +148,54 @@ __device__ inline uint64_t cx64(uint64_t x, bool keep_max) {
   } else {
     b = xor_lane_u64<j>(x);
   }
-  return (a > b) == keep_max ? a : b;
+  return (a > b) == __builtin_amdgcn_inverse_ballot_w64(keep_max) ? a : b;
 }
-// step (k, j) of a bitonic sort: blocks of k lanes alternate direction
+// step (k, j) of a bitonic sort; flip = 0 sorts descending, ~0 ascending
 template <int k, int j>
-__device__ inline uint64_t sort_step(uint64_t x, int lane, bool desc) {
-  return cx64<j>(x, (((lane & k) == 0) == ((lane & j) == 0)) == desc);
+__device__ inline uint64_t sort_step(uint64_t x, uint64_t flip) {
+  return cx64<j>(x, sort_keep_max(k, j) ^ flip);
 }
 // Sorts one key per lane across the wave: descending (lane 0 largest) when
-// `desc`, else ascending.
-__device__ inline uint64_t wave_sort(uint64_t x, int lane, bool desc) {
-  x = sort_step<2, 1>(x, lane, desc);
-  x = sort_step<4, 2>(x, lane, desc);
-  x = sort_step<4, 1>(x, lane, desc);
-  x = sort_step<8, 4>(x, lane, desc);
-  x = sort_step<8, 2>(x, lane, desc);
-  x = sort_step<8, 1>(x, lane, desc);
-  x = sort_step<16, 8>(x, lane, desc);
-  x = sort_step<16, 4>(x, lane, desc);
-  x = sort_step<16, 2>(x, lane, desc);
-  x = sort_step<16, 1>(x, lane, desc);
-  x = sort_step<32, 16>(x, lane, desc);
-  x = sort_step<32, 8>(x, lane, desc);
-  x = sort_step<32, 4>(x, lane, desc);
-  x = sort_step<32, 2>(x, lane, desc);
-  x = sort_step<32, 1>(x, lane, desc);
-  x = sort_step<64, 32>(x, lane, desc);
-  x = sort_step<64, 16>(x, lane, desc);
-  x = sort_step<64, 8>(x, lane, desc);
-  x = sort_step<64, 4>(x, lane, desc);
-  x = sort_step<64, 2>(x, lane, desc);
-  x = sort_step<64, 1>(x, lane, desc);
+// `desc` (wave-uniform), else ascending.
+__device__ inline uint64_t wave_sort(uint64_t x, bool desc) {
+  const uint64_t flip = __builtin_amdgcn_readfirstlane((int)desc) ? 0ull : ~0ull;
+  x = sort_step<2, 1>(x, flip);
+  x = sort_step<4, 2>(x, flip);
+  x = sort_step<4, 1>(x, flip);
+  x = sort_step<8, 4>(x, flip);
+  x = sort_step<8, 2>(x, flip);
+  x = sort_step<8, 1>(x, flip);
+  x = sort_step<16, 8>(x, flip);
+  x = sort_step<16, 4>(x, flip);
+  x = sort_step<16, 2>(x, flip);
+  x = sort_step<16, 1>(x, flip);
+  x = sort_step<32, 16>(x, flip);
+  x = sort_step<32, 8>(x, flip);
+  x = sort_step<32, 4>(x, flip);
+  x = sort_step<32, 2>(x, flip);
+  x = sort_step<32, 1>(x, flip);
+  x = sort_step<64, 32>(x, flip);
+  x = sort_step<64, 16>(x, flip);
+  x = sort_step<64, 8>(x, flip);
+  x = sort_step<64, 4>(x, flip);
+  x = sort_step<64, 2>(x, flip);
+  x = sort_step<64, 1>(x, flip);
   return x;
 }
 // Sorts a bitonic sequence across the wave, descending.
-__device__ inline uint64_t bitonic_merge_desc(uint64_t t, int lane) {
-  t = cx64<32>(t, (lane & 32) == 0);
-  t = cx64<16>(t, (lane & 16) == 0);
-  t = cx64<8>(t, (lane & 8) == 0);
-  t = cx64<4>(t, (lane & 4) == 0);
-  t = cx64<2>(t, (lane & 2) == 0);
-  t = cx64<1>(t, (lane & 1) == 0);
+__device__ inline uint64_t bitonic_merge_desc(uint64_t t) {
+  t = cx64<32>(t, lanes_where_zero(32));
+  t = cx64<16>(t, lanes_where_zero(16));
+  t = cx64<8>(t, lanes_where_zero(8));
+  t = cx64<4>(t, lanes_where_zero(4));
+  t = cx64<2>(t, lanes_where_zero(2));
+  t = cx64<1>(t, lanes_where_zero(1));
   return t;
 }
 // Top 64 of a descending list and an ascending chunk, descending: their
 // lane-wise maximum holds the 64 largest as a bitonic sequence.
-__device__ inline uint64_t wave_merge(uint64_t list_desc, uint64_t chunk_asc, int lane) {
-  return bitonic_merge_desc(umax64(list_desc, chunk_asc), lane);
+__device__ inline uint64_t wave_merge(uint64_t list_desc, uint64_t chunk_asc) {
+  return bitonic_merge_desc(umax64(list_desc, chunk_asc));
 }
 // Merges the descending lists of W waves (W = 2 or 4, at most 64 / W keys
 // each; list w at lists + 64 w) into one descending list. The lists sit side
@@ -189,15 +206,15 @@ __device__ inline uint64_t merge_lists(const uint64_t* lists, int W, int lane) {
     const int sg = lane >> 4, i = lane & 15;
     uint64_t x = lists[sg * 64 + ((sg & 1) ? 15 - i : i)];
     // pairs of segments into 32-lane runs, the first descending, the second ascending
-    x = cx64<16>(x, ((lane & 32) == 0) == ((lane & 16) == 0));
-    x = cx64<8>(x, ((lane & 32) == 0) == ((lane & 8) == 0));
-    x = cx64<4>(x, ((lane & 32) == 0) == ((lane & 4) == 0));
-    x = cx64<2>(x, ((lane & 32) == 0) == ((lane & 2) == 0));
-    x = cx64<1>(x, ((lane & 32) == 0) == ((lane & 1) == 0));
-    return bitonic_merge_desc(x, lane);
+    x = cx64<16>(x, sort_keep_max(32, 16));
+    x = cx64<8>(x, sort_keep_max(32, 8));
+    x = cx64<4>(x, sort_keep_max(32, 4));
+    x = cx64<2>(x, sort_keep_max(32, 2));
+    x = cx64<1>(x, sort_keep_max(32, 1));
+    return bitonic_merge_desc(x);
   }
   const int sg = lane >> 5, i = lane & 31;
-  return bitonic_merge_desc(lists[sg * 64 + (sg ? 31 - i : i)], lane);
+  return bitonic_merge_desc(lists[sg * 64 + (sg ? 31 - i : i)]);
 }
 
 // ---- LDS layout ------------------------------------------------------------
@@ -319,8 +336,8 @@ struct RegTop {
     if (live == 0) return;
     // the first chunk is sorted descending into the list, later ones
     // ascending and merged with it
-    uint64_t t = wave_sort(x, lane, n == 0);
-    if (n > 0) t = wave_merge(L, t, lane);
+    uint64_t t = wave_sort(x, n == 0);
+    if (n > 0) t = wave_merge(L, t);
     L = lane < cap ? t : 0ull;
     n = min(cap, n + __popcll(live));
   }
@@ -644,7 +661,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
         if (W > 1 && W * cap <= 64) {
           r = merge_lists(ql0, W, lane);
         } else {
-          for (int jj = 1; jj < W; ++jj) r = wave_merge(r, ql0[jj * 64 + 63 - lane], lane);
+          for (int jj = 1; jj < W; ++jj) r = wave_merge(r, ql0[jj * 64 + 63 - lane]);
         }
         const uint64_t ql = lane < cap ? r : 0ull;
         const int qc = __popcll(__ballot(ql != 0ull));
