@@ -182,6 +182,21 @@ __device__ inline uint64_t wave_sort(uint64_t x, bool desc) {
   x = sort_step<64, 1>(x, flip);
   return x;
 }
+// Sorts lanes 0..15 descending (10 steps; the other lanes are sorted in
+// 16-lane blocks of their own).
+__device__ inline uint64_t sort16_desc(uint64_t x) {
+  x = sort_step<2, 1>(x, 0ull);
+  x = sort_step<4, 2>(x, 0ull);
+  x = sort_step<4, 1>(x, 0ull);
+  x = sort_step<8, 4>(x, 0ull);
+  x = sort_step<8, 2>(x, 0ull);
+  x = sort_step<8, 1>(x, 0ull);
+  x = sort_step<16, 8>(x, 0ull);
+  x = sort_step<16, 4>(x, 0ull);
+  x = sort_step<16, 2>(x, 0ull);
+  x = sort_step<16, 1>(x, 0ull);
+  return x;
+}
 // Sorts a bitonic sequence across the wave, descending.
 __device__ inline uint64_t bitonic_merge_desc(uint64_t t) {
   t = cx64<32>(t, lanes_where_zero(32));
@@ -341,6 +356,14 @@ struct RegTop {
     L = lane < cap ? t : 0ull;
     n = min(cap, n + __popcll(live));
   }
+  // First push of at most 16 keys, in lanes 0..15 (the other lanes empty).
+  __device__ inline void push16(uint64_t x, int lane) {
+    const uint64_t live = __ballot(x != 0ull);
+    if (live == 0) return;
+    const uint64_t t = sort16_desc(x);
+    L = lane < cap ? t : 0ull;
+    n = min(cap, __popcll(live));
+  }
 };
 
 // LDS list (any cap up to ICE_MAX_BEAM), sorted descending. A push ranks
@@ -392,6 +415,15 @@ struct LdsTop {
     wave_sync();
   }
 };
+
+// v[lane] = val for one lane: v_writelane_b32, a vector-register write of a
+// scalar value (val and lane are wave-uniform; the lane index goes through
+// m0, which this code uses for nothing else)
+__device__ inline void write_lane(uint32_t& v, uint32_t val, int lane) {
+  const int l = __builtin_amdgcn_readfirstlane(lane);
+  const uint32_t x = (uint32_t)__builtin_amdgcn_readfirstlane((int)val);
+  asm volatile("s_mov_b32 m0, %2\n\tv_writelane_b32 %0, %1, m0" : "+v"(v) : "s"(x), "s"(l) : "m0");
+}
 
 // number of keys greater than x in a descending list of n keys
 __device__ inline int count_greater(const uint64_t* l, int n, uint64_t x) {
@@ -776,7 +808,9 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
       const int32_t* next = at<int32_t>(hb, L.off_pg_next[0]);
       const T* pgK = at<T>(hb, L.off_pgK[0]);
       const int n_own = qn[g], P = qp[g];
-      uint64_t pk = 0ull;
+      // page keys gather in lanes 0..fill-1: each is formed once on the scalar
+      // unit and written into its lane
+      uint32_t pk_hi = 0u, pk_lo = 0u;
       int fill = 0;
       for (int t0 = 0, nb; (nb = deal_pages(A, OT, n_own, P, j, W, t0, next, lane)) > 0; t0 += 64) {
         for (int b0 = 0; b0 < nb; b0 += QG::GB0) {
@@ -784,8 +818,9 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
           int pg[QG::GB0], cv[QG::GB0];
 #pragma unroll
           for (int b = 0; b < QG::GB0; ++b) {
-            pg[b] = b0 + b < nb ? A.cand[b0 + b] : -1;
-            cv[b] = b0 + b < nb ? A.cval[b0 + b] : 0;
+            // the same LDS word in every lane: uniform values
+            pg[b] = __builtin_amdgcn_readfirstlane(b0 + b < nb ? A.cand[b0 + b] : -1);
+            cv[b] = __builtin_amdgcn_readfirstlane(b0 + b < nb ? A.cval[b0 + b] : 0);
             const bool ok = pg[b] >= 0 && row < cv[b];
             qs.fetch(ok, pgK + ((int64_t)(ok ? pg[b] : 0) * ICE_PAGE_CAP + row) * D, buf[b]);
           }
@@ -795,17 +830,28 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
             float s = qs.dot(buf[b]);
             if (row >= cv[b]) s = -INFINITY;
             s = rows_max(s);
-            if (lane == fill) pk = make_key(s, pg[b]);
+            const uint32_t hi = ordered_bits(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s))));
+            const uint32_t lo = ~(uint32_t)__builtin_amdgcn_readfirstlane(pg[b]);
+            write_lane(pk_hi, hi, fill);
+            write_lane(pk_lo, lo, fill);
             if (++fill == 64) {
-              tl.push(A, pk, lane);
-              pk = 0ull;
+              tl.push(A, ((uint64_t)pk_hi << 32) | pk_lo, lane);
+              pk_hi = pk_lo = 0u;
               fill = 0;
             }
           }
         }
         wave_sync();
       }
-      if (fill) tl.push(A, pk, lane);
+      if (fill) {
+        const uint64_t pk = ((uint64_t)pk_hi << 32) | pk_lo;
+        if constexpr (!BIG) {
+          if (fill <= 16 && tl.n == 0) tl.push16(pk, lane);
+          else tl.push(A, pk, lane);
+        } else {
+          tl.push(A, pk, lane);
+        }
+      }
     }
     combine(tl, kpg, -1, -1);
   }
