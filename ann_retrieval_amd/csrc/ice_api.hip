@@ -310,6 +310,7 @@ int ice_insert(ice_index* idx, const void* k_new, const void* v_new, int32_t n_n
   if (n_new < 0) return fail(ICE_ERR_ARG, "n_new must be >= 0");
   if (n_new == 0) return ICE_OK;
   if (!k_new || !v_new) return fail(ICE_ERR_ARG, "k_new or v_new is null");
+  if (!aligned16(k_new)) return fail(ICE_ERR_ARG, "k_new must be 16-byte aligned");
   if ((int64_t)idx->n_tokens + n_new > idx->p.capacity)
     return fail(ICE_ERR_CAPACITY, "insert of %d tokens exceeds capacity %d (holds %d)", n_new, idx->p.capacity,
                 idx->n_tokens);

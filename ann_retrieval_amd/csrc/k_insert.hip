@@ -74,10 +74,76 @@ __device__ bool place_token(const DevLayout& L, void* hb, Hdr* hdr, int tb, int 
   return true;
 }
 
+// The parent search's row dot products: 4 lanes per row, lane part p holding
+// the row's 16-byte pieces p, p + 4, ... (one 64-byte segment per load across
+// the row's lanes); bf16 rows use v_dot2 (exact products, fp32 sums).
 template <int D, class T>
-__global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T* knew, const T* vnew, int n_new,
-                                                int t0) {
-  using G = RowGeo<D, T>;
+struct QuadRow {
+  static constexpr int NL = D * (int)sizeof(T) / 64;   // 16-byte pieces per lane
+  V4 q[NL];
+  __device__ inline void load(const T* row, int part) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) q[i] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(row) + 16 * (part + 4 * i));
+  }
+  __device__ inline void fetch(const T* row, int part, V4 (&out)[NL]) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) out[i] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(row) + 16 * (part + 4 * i));
+  }
+  // q . row over the row's 4 lanes (every one of them gets the sum)
+  __device__ inline float dot(const V4 (&k)[NL]) const {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, k[i].x), __builtin_bit_cast(bf2, q[i].x), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, k[i].y), __builtin_bit_cast(bf2, q[i].y), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, k[i].z), __builtin_bit_cast(bf2, q[i].z), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, k[i].w), __builtin_bit_cast(bf2, q[i].w), s, false);
+      } else {
+        s = fmaf(__uint_as_float(k[i].x), __uint_as_float(q[i].x), s);
+        s = fmaf(__uint_as_float(k[i].y), __uint_as_float(q[i].y), s);
+        s = fmaf(__uint_as_float(k[i].z), __uint_as_float(q[i].z), s);
+        s = fmaf(__uint_as_float(k[i].w), __uint_as_float(q[i].w), s);
+      }
+    }
+    s += xor_lane_f<1>(s);
+    s += xor_lane_f<2>(s);
+    return s;
+  }
+};
+
+// (score desc, token asc) running best and runner-up
+struct BestTok {
+  float best = -INFINITY, second = -INFINITY;
+  int tok = 0x7fffffff;
+  __device__ inline void push(float s, int t) {
+    if (s > best || (s == best && t < tok)) {
+      second = best;
+      best = s;
+      tok = t;
+    } else {
+      second = fmaxf(second, s);
+    }
+  }
+  __device__ inline void merge(float ob, float os, int ot) {
+    if (ob > best || (ob == best && ot < tok)) {
+      second = fmaxf(best, os);
+      best = ob;
+      tok = ot;
+    } else {
+      second = fmaxf(second, ob);
+    }
+  }
+};
+
+constexpr int kInsertWaves = 16;
+
+template <int D, class T>
+__global__ __launch_bounds__(kInsertWaves * 64) void k_insert(DevLayout L, void* blob, const T* knew, const T* vnew,
+                                                              int n_new, int t0) {
+  using QR = QuadRow<D, T>;
+  constexpr int NW = kInsertWaves;
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   void* hb = head_base(blob, L, h);
@@ -87,10 +153,9 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
   int8_t* lev = at<int8_t>(hb, L.off_lev);
   float* eall = at<float>(hb, L.off_e);
 
-  __shared__ __attribute__((aligned(16))) float kf[D];
-  __shared__ double red_d[4];
-  __shared__ float red_s[4], red_s2[4];
-  __shared__ int red_t[4];
+  __shared__ double red_d[NW];
+  __shared__ float red_s[NW], red_s2[NW];
+  __shared__ int red_t[NW];
   __shared__ Place plc;
   __shared__ float e_sh;
 
@@ -102,20 +167,20 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
     double sq = 0.0;
     if (tid < D) {
       const float x = Elt<T>::load(krow, tid);
-      kf[tid] = x;
       sq = (double)x * (double)x;
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) sq += __shfl_xor(sq, m, 64);
     if (lane == 0) red_d[wave] = sq;
     __syncthreads();
-    const double n2 = red_d[0] + red_d[1] + red_d[2] + red_d[3];
+    double n2 = 0.0;
+    for (int w = 0; w < NW; ++w) n2 += red_d[w];
     const float et = (float)sqrt(fmax(0.0, M2 - n2));
     const int lam = min(Ltop, draw_level(L.seed, h, t, L.L, L.plog2));
 
-    // parent at level lam among the current points of level lam+1
-    float best = -INFINITY, second = -INFINITY;
-    int btok = 0x7fffffff;
+    // parent at level lam among the current points of level lam+1: 16 rows
+    // per wave pass, U passes' loads in flight, then a (score desc, token
+    // asc) reduction over the lanes, the waves and the block
     if (lam < Ltop) {
       const int tb = lam + 1;
       const bool from_top = tb == Ltop;
@@ -123,69 +188,46 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
       const int32_t* toks = from_top ? at<int32_t>(hb, L.off_top_tok) : at<int32_t>(hb, L.off_pg_tok[tb]);
       const T* rows = from_top ? at<T>(hb, L.off_top_K) : at<T>(hb, L.off_pgK[tb]);
       const float* es = from_top ? at<float>(hb, L.off_top_E) : at<float>(hb, L.off_pgE[tb]);
-      float q[G::EPL];
+      const int part = lane & 3;
+      QR qr;
+      qr.load(krow, part);
+      BestTok bt;
+      constexpr int U = QR::NL > 4 ? 1 : 2;   // fp32 d=128 rows fill the registers with one pass
+      for (int r0 = wave * 16; r0 < nrows; r0 += U * NW * 16) {
+        V4 buf[U][QR::NL];
+        int tok[U];
+        float ev[U];
 #pragma unroll
-      for (int i = 0; i < G::EPL; ++i) q[i] = kf[(lane % G::LPR) * G::EPL + i];
-      for (int r0 = wave * G::RPP; r0 < nrows; r0 += 4 * G::RPP) {
-        const int r = r0 + lane / G::LPR;
-        const int tok = r < nrows ? toks[r] : -1;
-        float s = 0.0f;
-        if (tok >= 0) {
-          const V4 v = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(rows + (int64_t)r * D) +
-                                                    (lane % G::LPR) * 16);
-          float f[G::EPL];
-          Elt<T>::unpack(v, f);
-#pragma unroll
-          for (int i = 0; i < G::EPL; ++i) s = fmaf(q[i], f[i], s);
+        for (int u = 0; u < U; ++u) {
+          const int r = r0 + u * NW * 16 + (lane >> 2);
+          const int rc = r < nrows ? r : nrows - 1;     // loads are unconditional so they batch
+          tok[u] = r < nrows ? toks[rc] : -1;
+          ev[u] = es[rc];
+          qr.fetch(rows + (int64_t)rc * D, part, buf[u]);
         }
-        s = group_sum<G::LPR>(s);
-        if (tok >= 0) {
-          s = fmaf(et, es[r], s);
-          if (s > best || (s == best && tok < btok)) {
-            second = best;
-            best = s;
-            btok = tok;
-          } else {
-            second = fmaxf(second, s);
-          }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float sc = fmaf(et, ev[u], qr.dot(buf[u]));
+          if (tok[u] >= 0) bt.push(sc, tok[u]);
         }
       }
-      // reduce (score desc, token asc) over the wave, then the block
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const float ob = __shfl_xor(best, m, 64), os = __shfl_xor(second, m, 64);
-        const int ot = __shfl_xor(btok, m, 64);
-        if (ob > best || (ob == best && ot < btok)) {
-          second = fmaxf(best, os);
-          best = ob;
-          btok = ot;
-        } else {
-          second = fmaxf(second, ob);
-        }
-      }
+      for (int m = 1; m < 64; m <<= 1)
+        bt.merge(__shfl_xor(bt.best, m, 64), __shfl_xor(bt.second, m, 64), __shfl_xor(bt.tok, m, 64));
       if (lane == 0) {
-        red_s[wave] = best;
-        red_s2[wave] = second;
-        red_t[wave] = btok;
+        red_s[wave] = bt.best;
+        red_s2[wave] = bt.second;
+        red_t[wave] = bt.tok;
       }
     }
     __syncthreads();
     if (tid == 0) {
       int p = -1;
       if (lam < Ltop) {
-        best = red_s[0];
-        second = red_s2[0];
-        btok = red_t[0];
-        for (int w = 1; w < 4; ++w) {
-          if (red_s[w] > best || (red_s[w] == best && red_t[w] < btok)) {
-            second = fmaxf(best, red_s2[w]);
-            best = red_s[w];
-            btok = red_t[w];
-          } else {
-            second = fmaxf(second, red_s[w]);
-          }
-        }
-        p = btok;
+        BestTok bt;
+        for (int w = 0; w < NW; ++w) bt.merge(red_s[w], red_s2[w], red_t[w]);
+        const float best = bt.best, second = bt.second;
+        p = bt.tok;
         if (p < 0 || p >= t || lev[p] < lam + 1) {
           // only when every score was NaN (non-finite input): take any point
           // of the next level instead of indexing out of range
@@ -233,17 +275,17 @@ __global__ __launch_bounds__(256) void k_insert(DevLayout L, void* blob, const T
     for (int l = 0; l < Ltop || l == 0; ++l) {
       if (plc.page[l] < 0 || plc.slot[l] != 0) continue;
       const int64_t base = (int64_t)plc.page[l] * ICE_PAGE_CAP;
-      for (int i = tid + D; i < ICE_PAGE_CAP * D; i += 256) {
+      for (int i = tid + D; i < ICE_PAGE_CAP * D; i += NW * 64) {
         at<T>(hb, L.off_pgK[l])[base * D + i] = T(0);
         if (l != 0 && i % D == 0) at<float>(hb, L.off_pgE[l])[base + i / D] = 0.0f;
       }
       // V pages ([slot group][dim][4 slots]): every element but slot 0's
       if (l == 0)
-        for (int i = tid; i < ICE_PAGE_CAP * D; i += 256)
+        for (int i = tid; i < ICE_PAGE_CAP * D; i += NW * 64)
           if (i % 4 != 0 || i >= 4 * D) reinterpret_cast<T*>(v_pages(L, hb, h))[base * D + i] = T(0);
     }
     // rows into the pools
-    for (int i = tid; i < D; i += 256) {
+    for (int i = tid; i < D; i += NW * 64) {
       const T kv = krow[i];
       if (plc.page[0] >= 0) {
         const int64_t row = (int64_t)plc.page[0] * ICE_PAGE_CAP + plc.slot[0];
@@ -277,13 +319,13 @@ hipError_t launch_insert(const DevLayout& L, void* blob, const void* k_new, cons
   if (L.dtype == ICE_BF16) {
     const uint16_t* k = static_cast<const uint16_t*>(k_new);
     const uint16_t* v = static_cast<const uint16_t*>(v_new);
-    if (L.d == 128) k_insert<128, uint16_t><<<grid, 256, 0, s>>>(L, blob, k, v, n_new, t0);
-    else k_insert<64, uint16_t><<<grid, 256, 0, s>>>(L, blob, k, v, n_new, t0);
+    if (L.d == 128) k_insert<128, uint16_t><<<grid, kInsertWaves * 64, 0, s>>>(L, blob, k, v, n_new, t0);
+    else k_insert<64, uint16_t><<<grid, kInsertWaves * 64, 0, s>>>(L, blob, k, v, n_new, t0);
   } else {
     const float* k = static_cast<const float*>(k_new);
     const float* v = static_cast<const float*>(v_new);
-    if (L.d == 128) k_insert<128, float><<<grid, 256, 0, s>>>(L, blob, k, v, n_new, t0);
-    else k_insert<64, float><<<grid, 256, 0, s>>>(L, blob, k, v, n_new, t0);
+    if (L.d == 128) k_insert<128, float><<<grid, kInsertWaves * 64, 0, s>>>(L, blob, k, v, n_new, t0);
+    else k_insert<64, float><<<grid, kInsertWaves * 64, 0, s>>>(L, blob, k, v, n_new, t0);
   }
   return hipGetLastError();
 }

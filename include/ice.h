@@ -125,7 +125,8 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
 
 /* Incremental insert (the article's section 3: no rebuild; the notes' key
  * design 2: a node over the page size splits off a new page). k_new, v_new:
- * device, [H][n_new][d] contiguous. Tokens are inserted one after another at
+ * device, [H][n_new][d] contiguous, k_new 16-byte aligned (ICE_ERR_ARG
+ * otherwise). Tokens are inserted one after another at
  * the next positions: each draws its level (capped at the build's top level),
  * takes the nearest point of the next level as parent, and is appended to
  * its owner's last page, or to a newly split page if that one is full.
