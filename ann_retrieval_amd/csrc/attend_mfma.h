@@ -121,6 +121,66 @@ __device__ inline void stage_q(const uint16_t* Qh, int G, float* part) {
   }
 }
 
+// One page into a wave's running softmax state (m, l, acc): the scores of
+// its first `cnt` tokens for every query (S^T = K Q^T), their weights
+// against the running base, and O^T += V^T P^T. k: the lane's K pieces, v:
+// its V pieces (mload_k / mload_v); q_lds: the staged Q^T; c2: the scale in
+// base 2. cnt = 0 leaves the state unchanged.
+template <int D>
+__device__ inline void page_update(const V4 (&k)[MGeo<D>::KC], const uint2 (&v)[MGeo<D>::VC], int cnt, float c2,
+                                   const V4* q_lds, int lane, float& m, float& l, float4v (&acc)[MGeo<D>::VC]) {
+  using M = MGeo<D>;
+  const int qt = lane >> 4;     // 4-token group of the lane (its query is lane % 16)
+  float4v s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < M::KC; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, k[c]), __builtin_bit_cast(bf16x8, q_lds[c * 64 + lane]), s, 0, 0, 0);
+  float x[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = 4 * qt + j < cnt ? s[j] * c2 : -INFINITY;
+    mx = fmaxf(mx, x[j]);
+  }
+  mx = fmaxf(mx, xor_lane_f<16>(mx));
+  mx = fmaxf(mx, xor_lane_f<32>(mx));
+  // The running base m moves only when a page's max exceeds it by more
+  // than kSlack (weights stay below 2^kSlack, harmless in fp32), so the
+  // accumulators are rescaled on few pages only.
+  const bool move = mx > m + kSlack;
+  const float mn = move ? mx : m;
+  const float corr = move ? (m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn)) : 1.0f;
+  const bool any_move = __ballot(move) != 0;   // uniform over the wave
+  float p[4], rs = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p[j] = x[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[j] - mn);
+    rs += p[j];
+  }
+  rs += xor_lane_f<16>(rs);
+  rs += xor_lane_f<32>(rs);
+  l = l * corr + rs;
+  m = mn;
+  // P = hi + lo in bf16 (round to nearest even), as the B operand (query
+  // qn, tokens 4qt .. 4qt+3)
+  short4v phi, plo;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 hi = (__bf16)p[j];
+    phi[j] = __builtin_bit_cast(short, hi);
+    plo[j] = __builtin_bit_cast(short, (__bf16)(p[j] - (float)hi));
+  }
+  if (any_move)
+#pragma unroll
+    for (int c = 0; c < M::VC; ++c) acc[c] *= corr;
+#pragma unroll
+  for (int c = 0; c < M::VC; ++c) {
+    const short4v va = __builtin_bit_cast(short4v, v[c]);
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[c], 0, 0, 0);
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[c], 0, 0, 0);
+  }
+}
+
 // One wave attends pages u[wi], u[wi + ws], ... of the nu page ids u[0..nu)
 // (global or LDS; ids outside the head's page table are skipped) for the
 // head's G query heads, into `st`. part holds the staged Q^T. With staged V
@@ -131,7 +191,6 @@ __device__ void attend_pages(const DevLayout& L, const void* hb, int h, int G, c
   using M = MGeo<D>;
   const V4* q_lds = reinterpret_cast<const V4*>(part);
   const int lane = threadIdx.x & 63;
-  const int qt = lane >> 4;     // 4-token group of the lane (its query is lane % 16)
   const char* pgK = at<char>(hb, L.off_pgK[0]);
   const bool staged = L.vstage != nullptr;
   const char* pgV = staged ? L.vstage + (int64_t)h * L.vstage_pages * (ICE_PAGE_CAP * M::ROWB) : v_pages(L, hb, h);
@@ -173,54 +232,8 @@ __device__ void attend_pages(const DevLayout& L, const void* hb, int h, int G, c
       uint2 vcur[M::VC];
       if constexpr (!PREFETCH_V) mload_v<D>(pgV, cnt > 0 ? (staged ? wi + ws * (k0 + kc) : pg_k) : 0, cnt, lane, vcur);
       issue(k + 1, nxt);
-      float4v s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int c = 0; c < M::KC; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, cur.k[c]), __builtin_bit_cast(bf16x8, q_lds[c * 64 + lane]), s, 0, 0, 0);
-      float x[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = 4 * qt + j < cnt ? s[j] * c2 : -INFINITY;
-        mx = fmaxf(mx, x[j]);
-      }
-      mx = fmaxf(mx, xor_lane_f<16>(mx));
-      mx = fmaxf(mx, xor_lane_f<32>(mx));
-      // The running base m moves only when a page's max exceeds it by more
-      // than kSlack (weights stay below 2^kSlack, harmless in fp32), so the
-      // accumulators are rescaled on few pages only.
-      const bool move = mx > m + kSlack;
-      const float mn = move ? mx : m;
-      const float corr = move ? (m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn)) : 1.0f;
-      const bool any_move = __ballot(move) != 0;   // uniform over the wave
-      float p[4], rs = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = x[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[j] - mn);
-        rs += p[j];
-      }
-      rs += xor_lane_f<16>(rs);
-      rs += xor_lane_f<32>(rs);
-      l = l * corr + rs;
-      m = mn;
-      // P = hi + lo in bf16 (round to nearest even), as the B operand (query
-      // qn, tokens 4qt .. 4qt+3)
-      short4v phi, plo;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const __bf16 hi = (__bf16)p[j];
-        phi[j] = __builtin_bit_cast(short, hi);
-        plo[j] = __builtin_bit_cast(short, (__bf16)(p[j] - (float)hi));
-      }
-      if (any_move)
-#pragma unroll
-        for (int c = 0; c < M::VC; ++c) acc[c] *= corr;
-#pragma unroll
-      for (int c = 0; c < M::VC; ++c) {
-        const short4v va = __builtin_bit_cast(short4v, PREFETCH_V ? cur.v[c] : vcur[c]);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[c], 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[c], 0, 0, 0);
-      }
+      if constexpr (PREFETCH_V) page_update<D>(cur.k, cur.v, cnt, c2, q_lds, lane, m, l, acc);
+      else page_update<D>(cur.k, vcur, cnt, c2, q_lds, lane, m, l, acc);
     };
     for (int k = 0; k < nk; k += 2) {
       step(k, bufA, bufB);
@@ -231,6 +244,24 @@ __device__ void attend_pages(const DevLayout& L, const void* hb, int h, int G, c
   st.l = l;
 #pragma unroll
   for (int c = 0; c < M::VC; ++c) st.acc[c] = acc[c];
+}
+
+// One wave attends one page whose id and valid rows it already holds
+// (wave-uniform; an id outside [0, n_pages) or a page without rows adds
+// nothing). V from the head's device pool.
+template <int D>
+__device__ inline void attend_one(const DevLayout& L, const void* hb, int h, int n_pages, int pg, int n, float c2,
+                                  const float* part, WaveAcc<D>& st) {
+  using M = MGeo<D>;
+  const V4* q_lds = reinterpret_cast<const V4*>(part);
+  const int lane = threadIdx.x & 63;
+  const bool ok = pg >= 0 && pg < n_pages && n > 0;
+  n = ok ? n : 0;
+  MPage<D> a;
+  uint2 va[M::VC];
+  mload_k<D>(at<char>(hb, L.off_pgK[0]), ok ? pg : 0, n, lane, a);
+  mload_v<D>(v_pages(L, hb, h), ok ? pg : 0, n, lane, va);
+  page_update<D>(a.k, va, n, c2, q_lds, lane, st.m, st.l, st.acc);
 }
 
 // A wave's partials (m, l and o of query qn; every lane group holds m and l,

@@ -52,7 +52,9 @@ int check_params(const ice_params* p) {
   if (p->page_cap != ICE_PAGE_CAP) return fail(ICE_ERR_ARG, "page_cap must be %d", ICE_PAGE_CAP);
   if (p->levels < 1 || p->levels > ICE_MAX_LEVELS) return fail(ICE_ERR_ARG, "levels must be in [1, %d]", ICE_MAX_LEVELS);
   if (p->promote_log2 < 1 || p->promote_log2 > 16) return fail(ICE_ERR_ARG, "promote_log2 must be in [1, 16]");
-  if (p->capacity < 1 || p->capacity > (1 << 28)) return fail(ICE_ERR_ARG, "capacity must be in [1, 2^28]");
+  // at most 2^26 tokens per head keeps every page id below 2^27, the range a
+  // page's selection key holds
+  if (p->capacity < 1 || p->capacity > (1 << 26)) return fail(ICE_ERR_ARG, "capacity must be in [1, 2^26]");
   if (p->flags & ~ICE_HOST_POOL) return fail(ICE_ERR_ARG, "unknown flags 0x%x", p->flags);
   return ICE_OK;
 }

@@ -416,6 +416,13 @@ struct LdsTop {
   }
 };
 
+// Page (level-0) keys: the low word is (~page << 5) | valid rows, so equal
+// scores still rank by ascending page id and a selected page's row count
+// comes with it (page ids stay below 2^27, rows 1 .. 16).
+__device__ inline uint32_t page_key_lo(int pg, int rows) { return ((~(uint32_t)pg) << 5) | (uint32_t)rows; }
+__device__ inline int32_t key_page(uint64_t k) { return (int32_t)(0x07ffffffu - ((uint32_t)k >> 5)); }
+__device__ inline int32_t key_rows(uint64_t k) { return (int32_t)(k & 31u); }
+
 // v[lane] = val for one lane: v_writelane_b32, a vector-register write of a
 // scalar value (val and lane are wave-uniform; the lane index goes through
 // m0, which this code uses for nothing else)
@@ -590,13 +597,17 @@ __device__ int write_union(int G, int kpg, int32_t* sel_all, int32_t* wn, int32_
   return base;
 }
 
-// Claims of the fused decode step (LDS): a bit per page id of the head, and
-// per query head the pages it claimed first and their count.
+// Claims of the fused decode step (LDS): a bit per page id of the head, per
+// query head the pages it claimed first and their count, and the counter
+// that deals the claimed pages out to the block's waves.
 struct ClaimLds {
   uint32_t* bits;
-  int32_t* pages;     // [G][kpg]
-  int32_t* count;     // [G]
+  int32_t* pages;     // [G][kpg]: query head g's claims, then -1
+  int32_t* rows;      // [G][kpg]: their valid rows
+  int32_t* sel_rows;  // [G][kpg]: valid rows of the selected pages, in selection order
+  int32_t* count;     // [G]: claims of query head g, -1 until they are published
   int32_t* done;      // query heads whose claims are complete (zero on entry)
+  int32_t* next;      // the next chunk of pages to attend (zero on entry)
 };
 
 // Selection of head h by the whole block; returns the size of the group's
@@ -697,12 +708,13 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
         }
         const uint64_t ql = lane < cap ? r : 0ull;
         const int qc = __popcll(__ballot(ql != 0ull));
-        const int id = lane < qc ? key_id(ql) : -1;
+        const int id = lane < qc ? (cut >= 0 ? key_id(ql) : key_page(ql)) : -1;
         if (cut >= 0) {
           if (tr && lane < beam) tr[cut * beam + lane] = id;
         } else if (lane < kpg) {
           sel[((int64_t)h * G + g) * kpg + lane] = id;
           sel_all[g * kpg + lane] = id;
+          if (cl) cl->sel_rows[g * kpg + lane] = lane < qc ? key_rows(ql) : 0;
         }
         if (lvl >= 0) build_table(lvl, qc, [&](int) { return id; });
       }
@@ -724,7 +736,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
       qsync();
       if (lead) {
         const int qc = min(cap, tot);
-        auto id_of = [&](int i) { return i < qc ? key_id(qlist[i]) : -1; };
+        auto id_of = [&](int i) { return i < qc ? (cut >= 0 ? key_id(qlist[i]) : key_page(qlist[i])) : -1; };
         if (cut >= 0) {
           if (tr)
             for (int i = lane; i < beam; i += 64) tr[cut * beam + i] = id_of(i);
@@ -831,7 +843,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
             if (row >= cv[b]) s = -INFINITY;
             s = rows_max(s);
             const uint32_t hi = ordered_bits(__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s))));
-            const uint32_t lo = ~(uint32_t)__builtin_amdgcn_readfirstlane(pg[b]);
+            const uint32_t lo = page_key_lo(__builtin_amdgcn_readfirstlane(pg[b]), cv[b]);
             write_lane(pk_hi, hi, fill);
             write_lane(pk_lo, lo, fill);
             if (++fill == 64) {
@@ -860,18 +872,29 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
     // has claimed yet, in selection order: these its waves attend
     if (lead) {
       const int p = lane < kpg ? sel_all[g * kpg + lane] : -1;
+      const int pr = lane < kpg ? cl->sel_rows[g * kpg + lane] : 0;
       bool mine = false;
       if (p >= 0) {
         const uint32_t bit = 1u << (p & 31);
         mine = (atomicOr(&cl->bits[p >> 5], bit) & bit) == 0u;
       }
       const uint64_t mk = __ballot(mine);
-      if (mine) cl->pages[g * kpg + __popcll(mk & ((1ull << lane) - 1ull))] = p;
-      if (lane == 0) cl->count[g] = __popcll(mk);
+      const int n = __popcll(mk);
+      if (mine) {
+        const int at_ = g * kpg + __popcll(mk & ((1ull << lane) - 1ull));
+        cl->pages[at_] = p;
+        cl->rows[at_] = pr;
+      }
+      if (lane >= n && lane < kpg) {
+        cl->pages[g * kpg + lane] = -1;
+        cl->rows[g * kpg + lane] = 0;
+      }
+      // publish: the pages are visible before the count
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __atomic_store_n(&cl->count[g], n, __ATOMIC_RELAXED);
       // the last query head to finish sees every selection: it writes the
       // union right away when one wave can sort it
       int done = 0;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       if (lane == 0) done = atomicAdd(cl->done, 1);
       done = __shfl(done, 0, 64);
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -902,7 +925,7 @@ __global__ __launch_bounds__(1024) void k_select(DevLayout L, const void* blob, 
 // LDS: the selection's area, attention's Q^T and partials, the claim bits
 // (one per page id of the head), the claimed pages and their counts.
 struct DecLds {
-  int off_part, off_bits, off_pages, off_count, words, total;
+  int off_part, off_bits, off_pages, off_rows, off_sel_rows, off_count, words, total;
 };
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 __host__ __device__ inline DecLds dec_lds(int G, int beam, int kpg, int nw, int D, int pcap0) {
@@ -912,8 +935,10 @@ __host__ __device__ inline DecLds dec_lds(int G, int beam, int kpg, int nw, int 
   d.off_bits = align16(d.off_part + mfma_attend::part_floats(nw, G, D) * 4);
   d.words = (pcap0 + 31) / 32;
   d.off_pages = align16(d.off_bits + d.words * 4);
-  d.off_count = d.off_pages + G * kpg * 4;
-  d.total = align16(d.off_count + (G + 1) * 4);
+  d.off_rows = d.off_pages + G * kpg * 4;
+  d.off_sel_rows = d.off_rows + G * kpg * 4;
+  d.off_count = d.off_sel_rows + G * kpg * 4;
+  d.total = align16(d.off_count + (G + 2) * 4);
   return d;
 }
 constexpr int kDecodeMaxLds = 160 * 1024;
@@ -926,19 +951,51 @@ __global__ __launch_bounds__(1024) void k_decode(DevLayout L, const void* blob, 
   const int h = blockIdx.x, G = L.G, nw = blockDim.x >> 6, kpg = budget / ICE_PAGE_CAP;
   const DecLds DL = dec_lds(G, beam, kpg, nw, D, L.pcap[0]);
   float* part = reinterpret_cast<float*>(smem + DL.off_part);
+  int32_t* cnt = reinterpret_cast<int32_t*>(smem + DL.off_count);
   ClaimLds cl{reinterpret_cast<uint32_t*>(smem + DL.off_bits), reinterpret_cast<int32_t*>(smem + DL.off_pages),
-              reinterpret_cast<int32_t*>(smem + DL.off_count), reinterpret_cast<int32_t*>(smem + DL.off_count) + G};
+              reinterpret_cast<int32_t*>(smem + DL.off_rows), reinterpret_cast<int32_t*>(smem + DL.off_sel_rows), cnt,
+              cnt + G, cnt + G + 1};
   const uint16_t* Qh = Q + (int64_t)h * G * D;
   // ordered before any use by the selection's first block barrier
   mfma_attend::stage_q<D>(Qh, G, part);
   for (int i = threadIdx.x; i < DL.words; i += blockDim.x) cl.bits[i] = 0u;
-  if (threadIdx.x == 0) *cl.done = 0;
+  if (threadIdx.x < G) cl.count[threadIdx.x] = -1;
+  if (threadIdx.x == 0) *cl.done = *cl.next = 0;
   select_head<D, uint16_t, false>(L, blob, Q, budget, beam, sel, uni, n_uni, nullptr, smem, h, nullptr, &cl);
-  const int W = waves_per_query(G), wv = threadIdx.x >> 6, g = wv / W, j = wv % W;
+  // Attention: the claimed pages of all query heads, in query-head order,
+  // are dealt out one at a time to whichever wave asks next, so waves whose
+  // query head finished its selection early take the pages of the later
+  // ones. A wave asks once its own selection has ended, and a page waits for
+  // its query head to publish (a bounded wait: past kSpinLimit polls it
+  // counts a timeout and skips the page, so the kernel always ends).
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n_items = G * kpg;
+  const void* hb = head_base(blob, L, h);
+  int* timeouts = const_cast<int*>(&at<Hdr>(hb, L.off_hdr)->sync_timeouts);
+  const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
   mfma_attend::WaveAcc<D> st;
   st.init();
-  mfma_attend::attend_pages<D, false>(L, head_base(blob, L, h), h, G, cl.pages + g * kpg, cl.count[g], j, W,
-                                      scale * mfma_attend::kLog2e, part, st);
+  for (;;) {
+    int i = 0;
+    if (lane == 0) i = atomicAdd(cl.next, 1);
+    i = __builtin_amdgcn_readfirstlane(__shfl(i, 0, 64));
+    if (i >= n_items) break;
+    const int gq = i / kpg;
+    int spins = 0;
+    bool ok = true;
+    while (__atomic_load_n(&cl.count[gq], __ATOMIC_RELAXED) < 0) {
+      if (++spins > kSpinLimit) {
+        if (lane == 0) atomicAdd(timeouts, 1);
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // the page id and rows: the same LDS words in every lane
+    const int pg = __builtin_amdgcn_readfirstlane(cl.pages[i]), n = __builtin_amdgcn_readfirstlane(cl.rows[i]);
+    if (ok && pg >= 0) mfma_attend::attend_one<D>(L, hb, h, n_pages, pg, n, scale * mfma_attend::kLog2e, part, st);
+  }
   mfma_attend::write_partial<D>(st, wv, G, part, nw);
   __syncthreads();
   mfma_attend::merge_partials<D>(G, part, nw, O + (int64_t)h * G * D, lse ? lse + (int64_t)h * G : nullptr);

@@ -62,7 +62,7 @@ typedef struct ice_params {
   int32_t  page_cap;      /* must be ICE_PAGE_CAP                                         */
   int32_t  levels;        /* L in [1, ICE_MAX_LEVELS]: levels 0..L-1, bottom included      */
   int32_t  promote_log2;  /* promotion probability per level = 2^-promote_log2, in [1,16] */
-  int32_t  capacity;      /* max tokens per head, build plus inserts, >= 1                */
+  int32_t  capacity;      /* max tokens per head, build plus inserts, 1 .. 2^26          */
   uint32_t flags;         /* 0 or ICE_HOST_POOL                                           */
   uint64_t seed;          /* seed of the promotion draws                                  */
 } ice_params;
