@@ -192,18 +192,34 @@ __global__ __launch_bounds__(kInsertWaves * 64) void k_insert(DevLayout L, void*
       QR qr;
       qr.load(krow, part);
       BestTok bt;
-      constexpr int U = QR::NL > 4 ? 1 : 2;   // fp32 d=128 rows fill the registers with one pass
-      for (int r0 = wave * 16; r0 < nrows; r0 += U * NW * 16) {
-        V4 buf[U][QR::NL];
+      // passes in flight per wave (within 128 VGPRs)
+      constexpr int U = QR::NL >= 8 ? 1 : 2;
+      constexpr int STEP = U * NW * 16;
+      // token ids run one iteration ahead of the rows, so that the empty
+      // slots of partly filled pages (token -1) are never read
+      auto tok_at = [&](int r) { return r < nrows ? toks[r] : -1; };
+      int tokn[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) tokn[u] = tok_at(wave * 16 + u * NW * 16 + (lane >> 2));
+      for (int r0 = wave * 16; r0 < nrows; r0 += STEP) {
         int tok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          tok[u] = tokn[u];
+          tokn[u] = tok_at(r0 + STEP + u * NW * 16 + (lane >> 2));
+        }
+        V4 buf[U][QR::NL] = {};
         float ev[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int r = r0 + u * NW * 16 + (lane >> 2);
-          const int rc = r < nrows ? r : nrows - 1;     // loads are unconditional so they batch
-          tok[u] = r < nrows ? toks[rc] : -1;
-          ev[u] = es[rc];
-          qr.fetch(rows + (int64_t)rc * D, part, buf[u]);
+          // an empty slot's lanes load nothing and score 0, never pushed (a
+          // row's 4 lanes agree, so the quad sum stays within the row)
+          ev[u] = 0.0f;
+          if (tok[u] >= 0) {
+            ev[u] = es[r];
+            qr.fetch(rows + (int64_t)r * D, part, buf[u]);
+          }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
