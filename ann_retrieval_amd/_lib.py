@@ -19,7 +19,7 @@ c_size, c_void_p, c_char_p = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
 ICE_OK, ICE_ERR_ARG, ICE_ERR_DTYPE, ICE_ERR_STATE, ICE_ERR_CAPACITY, ICE_ERR_HIP = 0, -1, -2, -3, -4, -5
 ICE_F32, ICE_BF16 = 0, 1
 ICE_HOST_POOL = 1
-ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM = 16, 4, 16, 256
+ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM, ICE_MAX_RESIDENT = 16, 4, 16, 256, 4096
 (ICE_EXP_LEVEL, ICE_EXP_LIFT, ICE_EXP_PARENT, ICE_EXP_PAGE_TOK, ICE_EXP_PAGE_CNT, ICE_EXP_PAGE_NEXT,
  ICE_EXP_PAGE_OWNER, ICE_EXP_OWNER_FIRST, ICE_EXP_OWNER_TAIL, ICE_EXP_TOP, ICE_EXP_PAGE_K, ICE_EXP_PAGE_V,
  ICE_EXP_HEADER, ICE_EXP_OWNER_RUN, ICE_EXP_OWNER_COUNT) = range(15)
@@ -28,13 +28,13 @@ ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM = 16, 4, 16, 256
 class IceParams(ctypes.Structure):
     _fields_ = [("n_heads", c_i32), ("group", c_i32), ("d", c_i32), ("dtype", c_i32), ("page_cap", c_i32),
                 ("levels", c_i32), ("promote_log2", c_i32), ("capacity", c_i32), ("flags", ctypes.c_uint32),
-                ("seed", c_u64)]
+                ("seed", c_u64), ("resident", c_i32)]
 
 
 class IceHeadStats(ctypes.Structure):
     _fields_ = [("n_tokens", c_i32), ("top_level", c_i32), ("n_top", c_i32), ("n_pages", c_i32 * ICE_MAX_LEVELS),
                 ("clamps", c_i32), ("splits", c_i32), ("near_ties", c_i32), ("overflow", c_i32),
-                ("sync_timeouts", c_i32), ("reserved1", c_i32), ("M2", ctypes.c_double)]
+                ("sync_timeouts", c_i32), ("n_resident", c_i32), ("dense", c_i32), ("M2", ctypes.c_double)]
 
 
 _SIGNATURES = {
@@ -52,6 +52,8 @@ _SIGNATURES = {
                                   c_void_p, c_size, c_void_p]),
     "ice_decode": (ctypes.c_int, [c_void_p, c_void_p, c_i32, c_i32, c_void_p, c_void_p, c_void_p, c_f32, c_void_p,
                                   c_void_p, c_void_p, c_size, c_void_p]),
+    "ice_set_resident": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p]),
+    "ice_set_dense": (ctypes.c_int, [c_void_p, c_void_p, c_void_p]),
     "ice_export_bytes": (c_size, [c_void_p, c_i32, c_i32]),
     "ice_export": (ctypes.c_int, [c_void_p, c_i32, c_i32, c_i32, c_void_p, c_size, c_void_p]),
     "ice_n_tokens": (c_i32, [c_void_p]),

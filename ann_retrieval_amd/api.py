@@ -58,10 +58,10 @@ class PinnedHost:
 
 
 def make_params(n_heads: int, group: int, d: int, dtype: str, capacity: int, levels: int = 3,
-                promote_log2: int = 4, seed: int = 0, host_pool: bool = False) -> IceParams:
+                promote_log2: int = 4, seed: int = 0, host_pool: bool = False, resident: int = 0) -> IceParams:
     return IceParams(n_heads=n_heads, group=group, d=d, dtype=_DT[dtype][0], page_cap=_lib.ICE_PAGE_CAP,
                      levels=levels, promote_log2=promote_log2, capacity=capacity,
-                     flags=_lib.ICE_HOST_POOL if host_pool else 0, seed=seed)
+                     flags=_lib.ICE_HOST_POOL if host_pool else 0, seed=seed, resident=resident)
 
 
 def ice_index_bytes(p: IceParams) -> int:
@@ -78,12 +78,15 @@ class IceIndex:
     ``ice_build`` / ``ice_insert`` / ``ice_select`` / ``ice_attend`` map one to
     one onto the C entry points of the same names. With ``host_pool=True`` the
     V pages live in a pinned host tensor (``self.pool``) and every attend
-    gathers the union's pages over the host link first.
+    gathers the union's pages over the host link first. ``resident`` reserves
+    room for that many resident (sink and window) tokens per head, set with
+    ``set_resident``; ``set_dense`` flags heads whose attention covers every
+    indexed token.
     """
 
     def __init__(self, n_heads: int, group: int, d: int, dtype: str, capacity: int, levels: int = 3,
                  promote_log2: int = 4, seed: int = 0, max_budget: int = 256, device="cuda",
-                 host_pool: bool = False):
+                 host_pool: bool = False, resident: int = 0):
         self.lib = _lib.load()
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
@@ -91,7 +94,7 @@ class IceIndex:
         self.device = dev
         self.dtype = dtype
         self.tdtype = _DT[dtype][1]
-        self.p = make_params(n_heads, group, d, dtype, capacity, levels, promote_log2, seed, host_pool)
+        self.p = make_params(n_heads, group, d, dtype, capacity, levels, promote_log2, seed, host_pool, resident)
         self.H, self.G, self.d, self.capacity, self.levels = n_heads, group, d, capacity, levels
         self.max_budget = max_budget
         nbytes = ice_index_bytes(self.p)
@@ -143,6 +146,30 @@ class IceIndex:
             raise ValueError("k_new and v_new must be contiguous [H, n_new, d]")
         check(self.lib.ice_insert(self.handle, _ptr(k_new), _ptr(v_new), k_new.shape[1], _ptr(self.ws),
                                   self.ws_bytes, _stream_ptr(self.device)), "ice_insert")
+
+    def set_resident(self, K: torch.Tensor | None, V: torch.Tensor | None) -> None:
+        """Resident tokens [H, n, d] (sink, then window) attended beside the pages; None clears them."""
+        if K is None or V is None or K.shape[1] == 0:
+            check(self.lib.ice_set_resident(self.handle, None, None, 0, 0, _stream_ptr(self.device)),
+                  "ice_set_resident")
+            return
+        self._check_kv(K, "K")
+        self._check_kv(V, "V")
+        if K.shape != V.shape or K.stride() != V.stride():
+            raise ValueError("K and V must have the same shape and strides")
+        check(self.lib.ice_set_resident(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0),
+                                        _stream_ptr(self.device)), "ice_set_resident")
+
+    def set_dense(self, dense) -> None:
+        """Per-head dense flags (a sequence of H booleans, or None for none)."""
+        if dense is None:
+            check(self.lib.ice_set_dense(self.handle, None, _stream_ptr(self.device)), "ice_set_dense")
+            return
+        flags = np.ascontiguousarray(np.asarray(dense, dtype=bool).astype(np.uint8))
+        if flags.shape != (self.H,):
+            raise ValueError(f"dense must have {self.H} entries")
+        check(self.lib.ice_set_dense(self.handle, flags.ctypes.data_as(ctypes.c_void_p), _stream_ptr(self.device)),
+              "ice_set_dense")
 
     def ice_select(self, Q: torch.Tensor, budget_tokens: int, beam: int | None = None, trace: bool = False):
         """Returns (sel [H,G,k], uni [H,G*k], n_uni [H]) int32 device tensors (+ trace [H,G,L,beam])."""
@@ -208,4 +235,4 @@ class IceIndex:
                                   _stream_ptr(self.device)), "ice_export")
         return dict(n_tokens=st.n_tokens, top_level=st.top_level, n_top=st.n_top, n_pages=list(st.n_pages),
                     clamps=st.clamps, splits=st.splits, near_ties=st.near_ties, overflow=st.overflow,
-                    sync_timeouts=st.sync_timeouts, M2=st.M2)
+                    sync_timeouts=st.sync_timeouts, n_resident=st.n_resident, dense=st.dense, M2=st.M2)

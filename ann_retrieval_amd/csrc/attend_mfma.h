@@ -181,13 +181,15 @@ __device__ inline void page_update(const V4 (&k)[MGeo<D>::KC], const uint2 (&v)[
   }
 }
 
-// One wave attends pages u[wi], u[wi + ws], ... of the nu page ids u[0..nu)
-// (global or LDS; ids outside the head's page table are skipped) for the
-// head's G query heads, into `st`. part holds the staged Q^T. With staged V
-// (host-pool mode) the V page of list entry i is staging entry i.
+// One wave attends entries wi, wi + ws, ... of the head's page source (the
+// union or, for a dense head, every page; then the resident pages; union ids
+// outside the head's page table are skipped) for the head's G query heads,
+// into `st`. part holds the staged Q^T. With staged V (host-pool mode, which
+// has neither dense heads nor resident pages) the V page of entry i is
+// staging entry i.
 template <int D, bool PREFETCH_V>
-__device__ void attend_pages(const DevLayout& L, const void* hb, int h, int G, const int32_t* u, int nu, int wi,
-                             int ws, float c2, const float* part, WaveAcc<D>& st) {
+__device__ void attend_pages(const DevLayout& L, const void* hb, int h, int G, const PageSrc& src, int wi, int ws,
+                             float c2, const float* part, WaveAcc<D>& st) {
   using M = MGeo<D>;
   const V4* q_lds = reinterpret_cast<const V4*>(part);
   const int lane = threadIdx.x & 63;
@@ -195,20 +197,19 @@ __device__ void attend_pages(const DevLayout& L, const void* hb, int h, int G, c
   const bool staged = L.vstage != nullptr;
   const char* pgV = staged ? L.vstage + (int64_t)h * L.vstage_pages * (ICE_PAGE_CAP * M::ROWB) : v_pages(L, hb, h);
   const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
-  const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
   float m = st.m, l = st.l;
   float4v acc[M::VC];
 #pragma unroll
   for (int c = 0; c < M::VC; ++c) acc[c] = st.acc[c];
   (void)G;
 
+  const int nu = src.count();
   const int npw = nu > wi ? (nu - wi + ws - 1) / ws : 0;
   for (int k0 = 0; k0 < npw; k0 += 64) {
     int my_pg = -1, my_cnt = 0;
     if (k0 + lane < npw) {
-      my_pg = u[wi + ws * (k0 + lane)];
-      if (my_pg < 0 || my_pg >= n_pages) my_pg = -1;
-      else my_cnt = pg_cnt[my_pg];
+      my_pg = src.at(wi + ws * (k0 + lane));
+      if (my_pg >= 0) my_cnt = pg_cnt[my_pg];
     }
     const int nk = min(64, npw - k0);
     // Two page buffers with fixed roles in each half of an unrolled pair of
@@ -310,8 +311,9 @@ __device__ inline void merge_partials(int G, const float* part, int nw, float* O
   }
 }
 
-// Attention of head h for its G query heads over the nu page ids u[0..nu),
-// by the whole block: wave w takes pages w, w + nw, ... Qh: the head's
+// Attention of head h for its G query heads over the nu page ids u[0..nu)
+// (or every page, for a dense head) and the head's resident pages, by the
+// whole block: wave w takes entries w, w + nw, ... Qh: the head's
 // [G][D] queries; Oh: [G][D] outputs; lseh nullable. part: LDS of
 // part_floats(nw, G, D) floats; nw: waves of the block (all of them call).
 template <int D, bool PREFETCH_V>
@@ -322,7 +324,7 @@ __device__ void attend_head(const DevLayout& L, const void* hb, const uint16_t* 
   __syncthreads();
   WaveAcc<D> st;
   st.init();
-  attend_pages<D, PREFETCH_V>(L, hb, blockIdx.x, G, u, nu, wv, nw, scale * kLog2e, part, st);
+  attend_pages<D, PREFETCH_V>(L, hb, blockIdx.x, G, page_src(L, hb, u, nu), wv, nw, scale * kLog2e, part, st);
   write_partial<D>(st, wv, G, part, nw);
   __syncthreads();
   merge_partials<D>(G, part, nw, Oh, lseh);

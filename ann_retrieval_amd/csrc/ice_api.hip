@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <new>
+#include <cstddef>
 #include <string>
 #include <vector>
 
@@ -22,6 +23,7 @@ struct ice_index {
   size_t blob_bytes;
   void* host_pool;        // host-pool mode: the caller's pinned V pool (host address)
   int32_t n_tokens;
+  int32_t n_dense;        // heads flagged dense (ice_set_dense)
   bool built;
 };
 
@@ -56,6 +58,10 @@ int check_params(const ice_params* p) {
   // page's selection key holds
   if (p->capacity < 1 || p->capacity > (1 << 26)) return fail(ICE_ERR_ARG, "capacity must be in [1, 2^26]");
   if (p->flags & ~ICE_HOST_POOL) return fail(ICE_ERR_ARG, "unknown flags 0x%x", p->flags);
+  if (p->resident < 0 || p->resident > ICE_MAX_RESIDENT)
+    return fail(ICE_ERR_ARG, "resident must be in [0, %d]", ICE_MAX_RESIDENT);
+  if (p->resident > 0 && (p->flags & ICE_HOST_POOL))
+    return fail(ICE_ERR_ARG, "resident tokens need the device V pool (no ICE_HOST_POOL)");
   return ICE_OK;
 }
 
@@ -104,6 +110,7 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
     L->pcap[l] = page_bound(L->ncap[l], owners);
   }
   L->topcap = p->levels >= 2 ? std::max(L->ncap[1], 1) : 0;
+  L->res_pages = (p->resident + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP;
   const int64_t d = p->d, elt = L->elt, cap = p->capacity;
   Cursor c;
   L->off_hdr = c.take(sizeof(Hdr));
@@ -111,7 +118,8 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
   L->off_e = c.take(cap * 4);
   for (int l = 0; l < L->ntab; ++l) L->off_parent[l] = c.take(cap * 4);
   for (int l = 0; l < L->ntab; ++l) {
-    const int64_t P = L->pcap[l];
+    // table 0 also holds the resident pages, after its pcap[0] pages
+    const int64_t P = L->pcap[l] + (l == 0 ? L->res_pages : 0);
     L->off_pg_tok[l] = c.take(P * ICE_PAGE_CAP * 4);
     L->off_pg_cnt[l] = c.take(P * 4);
     L->off_pg_next[l] = c.take(P * 4);
@@ -247,6 +255,7 @@ int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_ind
   idx->blob_bytes = index_bytes;
   idx->host_pool = nullptr;
   idx->n_tokens = 0;
+  idx->n_dense = 0;
   idx->built = false;
   *out = idx;
   return ICE_OK;
@@ -295,7 +304,7 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
                 (long long)idx->W.build_bytes);
   if (((uintptr_t)ws & 255u) != 0) return fail(ICE_ERR_ARG, "workspace must be 256-byte aligned");
   if (host_mode(idx->L) && !idx->L.vpool) return fail(ICE_ERR_STATE, "build before ice_attach_host_pool");
-  hipError_t e = launch_build(idx->L, idx->W, idx->blob, K, V, n_tokens, head_stride, ws,
+  hipError_t e = launch_build(idx->L, idx->W, idx->blob, K, V, n_tokens, head_stride, ws, idx->built,
                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ice_build launch");
   idx->n_tokens = n_tokens;
@@ -359,6 +368,40 @@ int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const in
   if (e != hipSuccess) return hip_fail(e, "ice_attend launch");
   return ICE_OK;
 }
+int ice_set_resident(ice_index* idx, const void* K, const void* V, int32_t n, int64_t head_stride, void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (!idx->built) return fail(ICE_ERR_STATE, "resident tokens before build");
+  if (n < 0 || n > idx->p.resident) return fail(ICE_ERR_ARG, "n must be in [0, %d] (params.resident)", idx->p.resident);
+  if (n > 0) {
+    if (!K || !V) return fail(ICE_ERR_ARG, "K or V is null");
+    if (head_stride < (int64_t)n * idx->p.d) return fail(ICE_ERR_ARG, "head_stride must be >= n*d");
+    if (!aligned16(K) || !aligned16(V) || (head_stride * idx->L.elt) % 16 != 0)
+      return fail(ICE_ERR_ARG, "K, V and the head stride must be 16-byte aligned");
+  }
+  if (idx->L.res_pages == 0) return ICE_OK;   // nothing resident, nothing to clear
+  hipError_t e = launch_set_resident(idx->L, idx->blob, K, V, n, head_stride, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ice_set_resident launch");
+  return ICE_OK;
+}
+
+int ice_set_dense(ice_index* idx, const uint8_t* dense, void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (!idx->built) return fail(ICE_ERR_STATE, "dense flags before build");
+  std::vector<int32_t> flags(idx->p.n_heads, 0);
+  int n_dense = 0;
+  if (dense)
+    for (int h = 0; h < idx->p.n_heads; ++h) n_dense += (flags[h] = dense[h] ? 1 : 0);
+  if (n_dense > 0 && host_mode(idx->L)) return fail(ICE_ERR_ARG, "dense heads need the device V pool (no ICE_HOST_POOL)");
+  // the stream's earlier work finishes first, then one strided copy into the headers
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)
+    e = hipMemcpy2D(static_cast<char*>(idx->blob) + idx->L.off_hdr + offsetof(Hdr, dense), (size_t)idx->L.head_bytes,
+                    flags.data(), sizeof(int32_t), sizeof(int32_t), (size_t)idx->p.n_heads, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "ice_set_dense copy");
+  idx->n_dense = n_dense;
+  return ICE_OK;
+}
+
 int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32_t beam, int32_t* sel, int32_t* uni,
                int32_t* n_uni, float scale, float* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");
@@ -370,7 +413,7 @@ int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32
   if (!aligned16(Q)) return fail(ICE_ERR_ARG, "Q must be 16-byte aligned");
   const int uni_stride = idx->p.group * (budget_tokens / ICE_PAGE_CAP);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!host_mode(idx->L) && decode_fused(idx->L, budget_tokens, beam)) {
+  if (!host_mode(idx->L) && idx->n_dense == 0 && decode_fused(idx->L, budget_tokens, beam)) {
     hipError_t e = launch_decode(idx->L, idx->blob, Q, budget_tokens, beam, sel, uni, n_uni, scale, O, lse, s);
     if (e != hipSuccess) return hip_fail(e, "ice_decode launch");
     return ICE_OK;

@@ -25,7 +25,8 @@ struct Hdr {
   int32_t near_ties;
   int32_t overflow;        // page table full (ruled out within capacity)
   int32_t sync_timeouts;
-  int32_t reserved1;
+  int32_t n_resident;      // resident tokens attended beside the pages
+  int32_t dense;           // nonzero: attention covers every indexed page
   double M2;
 };
 static_assert(sizeof(Hdr) == sizeof(ice_head_stats), "header mirrors ice_head_stats");
@@ -40,6 +41,7 @@ struct DevLayout {
   uint64_t seed;
   int32_t ncap[ICE_MAX_LEVELS];  // max over heads of #positions < cap with level >= l
   int32_t pcap[ICE_MAX_LEVELS];  // page capacity of table l
+  int32_t res_pages;             // resident pages per head, after table 0's pcap[0] pages
   int32_t topcap;                // capacity of the top list
   int32_t elt;                   // bytes per element of K/V/Q
   int64_t head_bytes;            // stride between heads
@@ -103,6 +105,35 @@ template <class T>
 __host__ __device__ inline const T* at(const void* base, int64_t off) {
   return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
 }
+
+// The pages one head attends: the explicit ids u[0..nu) (the group's union;
+// ids outside the head's page table are skipped as -1) or, for a dense head,
+// every page [0, n_pages); then its resident pages, which follow the page
+// pool's pcap[0] pages.
+struct PageSrc {
+  const int32_t* u;
+  int nu, n_pages, dense, res_base, nr;
+  __device__ inline int count() const { return (dense ? n_pages : nu) + nr; }
+  __device__ inline int at(int i) const {
+    const int n0 = dense ? n_pages : nu;
+    if (i >= n0) return res_base + (i - n0);
+    if (dense) return i;
+    const int p = u[i];
+    return p >= 0 && p < n_pages ? p : -1;
+  }
+};
+__device__ inline PageSrc page_src(const DevLayout& L, const void* hb, const int32_t* u, int nu) {
+  const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
+  PageSrc s;
+  s.u = u;
+  s.nu = nu;
+  s.n_pages = hdr->n_pages[0];
+  s.dense = hdr->dense;
+  s.res_base = L.pcap[0];
+  s.nr = (hdr->n_resident + 15) / 16;
+  return s;
+}
+
 
 __host__ __device__ inline void* head_base(void* blob, const DevLayout& L, int h) {
   return static_cast<char*>(blob) + (int64_t)h * L.head_bytes;

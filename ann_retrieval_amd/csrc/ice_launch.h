@@ -6,8 +6,9 @@
 namespace ice {
 
 // k_build.hip
+// keep: a rebuild, which keeps the headers' resident counts and dense flags
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
-                        int n_tokens, int64_t head_stride, void* ws, hipStream_t s);
+                        int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s);
 // k_gemm.hip: nearest parent of every level-`level` point among the level-(level+1) points
 hipError_t launch_parent_gemm(const DevLayout& L, const WsLayout& W, void* blob, const void* K,
                               int64_t head_stride, void* ws, int level, hipStream_t s);
@@ -30,6 +31,8 @@ hipError_t launch_attend(const DevLayout& L, const void* blob, const void* Q, co
 hipError_t launch_gather_v(const DevLayout& L, const void* blob, const int32_t* uni, const int32_t* n_uni,
                            int uni_stride, hipStream_t s);
 // fills `n` int32 words at byte offset `off` of every head region
+hipError_t launch_set_resident(const DevLayout& L, void* blob, const void* K, const void* V, int n, int64_t hstride,
+                               hipStream_t s);
 hipError_t launch_fill_heads(void* base, int64_t head_bytes, int H, int64_t off, int64_t n, int32_t value,
                              hipStream_t s);
 

@@ -143,9 +143,9 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend_f32(DevLayout L, cons
   const bool staged = L.vstage != nullptr;
   const char* pgV = staged ? L.vstage + (int64_t)h * L.vstage_pages * (ICE_PAGE_CAP * D * 4) : v_pages(L, hb, h);
   const int32_t* pg_cnt = at<int32_t>(hb, L.off_pg_cnt[0]);
-  const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
-  const int nu = min(n_uni[h], uni_stride);
-  const int32_t* u = uni + (int64_t)h * uni_stride;
+  // the union (or every page of a dense head), then the resident pages
+  const PageSrc src = page_src(L, hb, uni + (int64_t)h * uni_stride, min(n_uni[h], uni_stride));
+  const int nu = src.count();
   const float c2 = scale * kLog2e;
   const int krow = lane >> 2;
   const int rg = lane / A::VL;
@@ -169,9 +169,8 @@ __global__ __launch_bounds__(kAttWaves * 64) void k_attend_f32(DevLayout L, cons
     for (int k0 = 0; k0 < npw; k0 += 64) {
       int my_pg = -1, my_cnt = 0;
       if (k0 + lane < npw) {
-        my_pg = u[wv + kAttWaves * (k0 + lane)];
-        if (my_pg < 0 || my_pg >= n_pages) my_pg = -1;
-        else my_cnt = pg_cnt[my_pg];
+        my_pg = src.at(wv + kAttWaves * (k0 + lane));
+        if (my_pg >= 0) my_cnt = pg_cnt[my_pg];
       }
       const int nk = min(64, npw - k0);
       FPage<D> bufA, bufB;
@@ -338,6 +337,54 @@ hipError_t launch_attend(const DevLayout& L, const void* blob, const void* Q, co
     const float* q = static_cast<const float*>(Q);
     if (L.d == 128) k_attend_f32<128><<<grid, kAttWaves * 64, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, O, lse);
     else k_attend_f32<64><<<grid, kAttWaves * 64, 0, s>>>(L, blob, q, uni, n_uni, uni_stride, scale, O, lse);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+
+// Resident pages: the caller's n tokens of each head (row-major K and V)
+// into pages pcap[0] .. pcap[0] + res_pages - 1 of the page pool, K as
+// [slot][d] and V as [slot group][d][4 slots] like every KV page, zeros past
+// n; then the pages' row counts and the header's resident count. One wave
+// per resident page.
+template <int D, class T>
+__global__ __launch_bounds__(64) void k_set_resident(DevLayout L, void* blob, const T* K, const T* V, int n,
+                                                     int64_t hstride) {
+  const int p = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  void* hb = head_base(blob, L, h);
+  const int pg = L.pcap[0] + p;
+  T* pk = at<T>(hb, L.off_pgK[0]) + (int64_t)pg * ICE_PAGE_CAP * D;
+  T* pv = reinterpret_cast<T*>(v_pages(L, hb, h)) + (int64_t)pg * ICE_PAGE_CAP * D;
+  const T* Kh = K + (int64_t)h * hstride;
+  const T* Vh = V + (int64_t)h * hstride;
+  for (int i = lane; i < ICE_PAGE_CAP * D; i += 64) {
+    const int sl = i / D, c = i % D, t = ICE_PAGE_CAP * p + sl;
+    const bool in = t < n;
+    pk[i] = in ? Kh[(int64_t)t * D + c] : T(0);
+    pv[((sl / 4) * D + c) * 4 + sl % 4] = in ? Vh[(int64_t)t * D + c] : T(0);
+  }
+  if (lane == 0) {
+    at<int32_t>(hb, L.off_pg_cnt[0])[pg] = max(0, min(ICE_PAGE_CAP, n - ICE_PAGE_CAP * p));
+    if (p == 0) at<Hdr>(hb, L.off_hdr)->n_resident = n;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_set_resident(const DevLayout& L, void* blob, const void* K, const void* V, int n, int64_t hstride,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)L.res_pages, (unsigned)L.H);
+  if (L.dtype == ICE_BF16) {
+    const uint16_t* k = static_cast<const uint16_t*>(K);
+    const uint16_t* v = static_cast<const uint16_t*>(V);
+    if (L.d == 128) k_set_resident<128, uint16_t><<<grid, 64, 0, s>>>(L, blob, k, v, n, hstride);
+    else k_set_resident<64, uint16_t><<<grid, 64, 0, s>>>(L, blob, k, v, n, hstride);
+  } else {
+    const float* k = static_cast<const float*>(K);
+    const float* v = static_cast<const float*>(V);
+    if (L.d == 128) k_set_resident<128, float><<<grid, 64, 0, s>>>(L, blob, k, v, n, hstride);
+    else k_set_resident<64, float><<<grid, 64, 0, s>>>(L, blob, k, v, n, hstride);
   }
   return hipGetLastError();
 }

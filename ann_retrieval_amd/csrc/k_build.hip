@@ -454,7 +454,7 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 
 template <int D, class T>
 hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const void* Kv, const void* Vv,
-                       int n, int64_t hstride, void* ws, hipStream_t s) {
+                       int n, int64_t hstride, void* ws, bool keep, hipStream_t s) {
   const T* K = static_cast<const T*>(Kv);
   const T* V = static_cast<const T*>(Vv);
   const unsigned H = (unsigned)L.H;
@@ -463,8 +463,16 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
   do {                                               \
     if ((err = hipGetLastError()) != hipSuccess) return err; \
   } while (0)
-  // fresh header, parent links and owner heads
-  if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_hdr, sizeof(Hdr) / 4, 0, s))) return err;
+  // fresh header, parent links and owner heads; `keep` (a rebuild) keeps
+  // the header's resident count and dense flag
+  if (!keep) {
+    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_hdr, sizeof(Hdr) / 4, 0, s))) return err;
+  } else {
+    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_hdr, offsetof(Hdr, n_resident) / 4, 0, s))) return err;
+    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_hdr + offsetof(Hdr, M2),
+                                 (sizeof(Hdr) - offsetof(Hdr, M2)) / 4, 0, s)))
+      return err;
+  }
   for (int l = 0; l < L.ntab; ++l) {
     if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_parent[l], L.cap, -1, s))) return err;
     if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_first[l], L.cap + 1, -1, s))) return err;
@@ -529,13 +537,13 @@ hipError_t launch_fill_heads(void* base, int64_t head_bytes, int H, int64_t off,
 }
 
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
-                        int n_tokens, int64_t head_stride, void* ws, hipStream_t s) {
+                        int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s) {
   if (L.dtype == ICE_BF16) {
-    if (L.d == 128) return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, s);
-    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, s);
+    if (L.d == 128) return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s);
+    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s);
   }
-  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, s);
-  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, s);
+  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s);
+  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s);
 }
 
 }  // namespace ice

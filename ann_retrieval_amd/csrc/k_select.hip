@@ -963,16 +963,18 @@ __global__ __launch_bounds__(1024) void k_decode(DevLayout L, const void* blob, 
   if (threadIdx.x == 0) *cl.done = *cl.next = 0;
   select_head<D, uint16_t, false>(L, blob, Q, budget, beam, sel, uni, n_uni, nullptr, smem, h, nullptr, &cl);
   // Attention: the claimed pages of all query heads, in query-head order,
-  // are dealt out one at a time to whichever wave asks next, so waves whose
-  // query head finished its selection early take the pages of the later
-  // ones. A wave asks once its own selection has ended, and a page waits for
-  // its query head to publish (a bounded wait: past kSpinLimit polls it
-  // counts a timeout and skips the page, so the kernel always ends).
+  // then the head's resident pages, are dealt out one at a time to whichever
+  // wave asks next, so waves whose query head finished its selection early
+  // take the pages of the later ones. A wave asks once its own selection has
+  // ended, and a claimed page waits for its query head to publish (a bounded
+  // wait: past kSpinLimit polls it counts a timeout and skips the page, so
+  // the kernel always ends).
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n_items = G * kpg;
   const void* hb = head_base(blob, L, h);
-  int* timeouts = const_cast<int*>(&at<Hdr>(hb, L.off_hdr)->sync_timeouts);
-  const int n_pages = at<Hdr>(hb, L.off_hdr)->n_pages[0];
+  const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
+  int* timeouts = const_cast<int*>(&hdr->sync_timeouts);
+  const int n_pages = hdr->n_pages[0], n_res = hdr->n_resident;
+  const int n_claim = G * kpg, n_items = n_claim + (n_res + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP;
   mfma_attend::WaveAcc<D> st;
   st.init();
   for (;;) {
@@ -980,6 +982,12 @@ __global__ __launch_bounds__(1024) void k_decode(DevLayout L, const void* blob, 
     if (lane == 0) i = atomicAdd(cl.next, 1);
     i = __builtin_amdgcn_readfirstlane(__shfl(i, 0, 64));
     if (i >= n_items) break;
+    if (i >= n_claim) {     // a resident page: nothing to wait for
+      const int r = i - n_claim;
+      mfma_attend::attend_one<D>(L, hb, h, L.pcap[0] + L.res_pages, L.pcap[0] + r,
+                                 min(ICE_PAGE_CAP, n_res - ICE_PAGE_CAP * r), scale * mfma_attend::kLog2e, part, st);
+      continue;
+    }
     const int gq = i / kpg;
     int spins = 0;
     bool ok = true;

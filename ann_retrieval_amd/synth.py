@@ -152,6 +152,15 @@ def new_tokens(w: Workload, gen: torch.Generator, device="cpu") -> tuple[torch.T
     return to_dtype(k, w.dtype), to_dtype(v, w.dtype)
 
 
+def resident_tokens(w: Workload, n: int, gen: torch.Generator, device="cpu") -> tuple[torch.Tensor, torch.Tensor]:
+    """n (k, v) per head from the same mixture, [H, n, d] each: stand-ins for
+    the sink and window tokens kept beside the index."""
+    h, c, d = w.mix.centres.shape
+    k = draw_keys(w.mix, n, gen, device)
+    v = draw_values(h, n, d, gen, device)
+    return to_dtype(k, w.dtype), to_dtype(v, w.dtype)
+
+
 def needle_workload(n_heads: int, group: int, n_tokens: int, d: int, n_centres: int, depth: float,
                     seed: int, dtype: str = "bf16", device="cpu", span: int = 16,
                     cosine: float = 0.9):

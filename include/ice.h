@@ -53,6 +53,7 @@ extern "C" {
 #define ICE_MAX_LEVELS 4
 #define ICE_MAX_GROUP  16   /* query heads per KV head                          */
 #define ICE_MAX_BEAM   256  /* beam width and pages per query                    */
+#define ICE_MAX_RESIDENT 4096 /* resident (sink + window) tokens per head         */
 
 typedef struct ice_params {
   int32_t  n_heads;       /* H >= 1: independent indexes (sequence x layer x KV head)     */
@@ -65,6 +66,9 @@ typedef struct ice_params {
   int32_t  capacity;      /* max tokens per head, build plus inserts, 1 .. 2^26          */
   uint32_t flags;         /* 0 or ICE_HOST_POOL                                           */
   uint64_t seed;          /* seed of the promotion draws                                  */
+  int32_t  resident;      /* resident tokens per head kept beside the index (sink and
+                             recent window, see ice_set_resident), 0 .. ICE_MAX_RESIDENT;
+                             0 with ICE_HOST_POOL                                          */
 } ice_params;
 
 /* Host-pool mode (the notes' overall framework, step 3, and the aitangshan.cn
@@ -163,6 +167,30 @@ int ice_attend(const ice_index* idx, const void* Q, const int32_t* uni, const in
                int32_t uni_stride, float scale, float* O, float* lse,
                void* ws, size_t ws_bytes, void* stream);
 
+/* Resident tokens (the aitangshan.cn IceCache article, section 6: the first
+ * "sink" tokens and the most recent window stay on the GPU, outside the
+ * index; only the tokens in between are indexed and retrieved). K, V:
+ * device, [H][n][d] at head_stride elements per head (>= n*d), the index's
+ * dtype, 16-byte aligned; 0 <= n <= params.resident (ICE_ERR_ARG otherwise).
+ * They are copied into per-head resident pages beside the page pool, and
+ * every later ice_attend / ice_decode attends them together with the pages
+ * it attends, in one softmax, until the next call replaces them (n = 0
+ * clears them). The selection never sees them. A caller moving a token out
+ * of the window inserts it (ice_insert) and passes the shorter window.
+ * After ice_build (ICE_ERR_STATE before); later builds keep them. */
+int ice_set_resident(ice_index* idx, const void* K, const void* V, int32_t n, int64_t head_stride, void* stream);
+
+/* Dense heads (the notes' discussion of the method's limits: the first two
+ * layers are left out of retrieval because their attention is not sparse).
+ * dense: host, [H] bytes, nonzero = that head's attention covers every
+ * indexed token (and its resident tokens) instead of the selected pages;
+ * nullable = none. Selection still runs for such heads, and its output is
+ * not used by their attention. ice_decode runs as separate select and attend
+ * kernels while any head is dense. ICE_ERR_ARG with ICE_HOST_POOL. After
+ * ice_build (ICE_ERR_STATE before); later builds keep them. Waits for
+ * `stream`, then copies the flags synchronously. */
+int ice_set_dense(ice_index* idx, const uint8_t* dense, void* stream);
+
 /* One decode step of the hot path (the framework's steps 2 and 3 together):
  * ice_select (without trace) followed by ice_attend over its union, with
  * uni_stride = G * budget_tokens / 16. The outputs and argument rules are
@@ -209,7 +237,8 @@ typedef struct ice_head_stats {
   int32_t sync_timeouts;   /* selection-kernel barrier waits that hit their spin
                               limit (a bound that keeps kernels finite; 0 in
                               correct operation)                                 */
-  int32_t reserved1;
+  int32_t n_resident;      /* resident tokens attended beside the pages          */
+  int32_t dense;           /* nonzero: attention covers every indexed token      */
   double  M2;              /* largest squared key norm at build                   */
 } ice_head_stats;
 

@@ -12,12 +12,15 @@ Sources, cited by page and section:
   section 二 (pages of 16 tokens, semantic instead of sequential pages),
   section 三 (DCI tree: lift, random promotion, nearest parent, same parent =
   same page, incremental insert), section 四 (bulk loading), section 六
-  (TK/TQ transform, GQA union).
+  (TK/TQ transform, GQA union; sink and window tokens stay resident on the
+  GPU, only the tokens in between are indexed).
 * [N] papernotes.org notes "IceCache: Memory-Efficient KV-cache Management for
   Long-Sequence LLMs": "Overall framework" (index / page selection / bulk
   load), key design 1 (semantic pages, the sparse-attention weight formula),
   key design 2 (M-DCI: promotion, parents, top-down search, incremental insert,
-  page split), key design 3 (per-head selection, GQA union).
+  page split), key design 3 (per-head selection, GQA union); the
+  limitations section (the first two layers are left out of retrieval, their
+  attention being dense).
 
 Where the pages leave a step open, the reading taken is marked ``[reading]``;
 each one is listed in the design notes. Every function here is pinned by
@@ -560,17 +563,30 @@ def gqa_union(sel_lists) -> list:
 # [reading] the caller passes the scale (1/sqrt(d) in the formula); the result
 # also returns the log-sum-exp of the scaled logits.
 
-def attend(idx: HeadIndex, q, pages, scale: float):
+def attend(idx: HeadIndex, q, pages, scale: float, resident=None, dense: bool = False):
+    """[N key design 1] softmax attention over the tokens of ``pages``.
+
+    [A §六] ``resident`` = (K_r, V_r), the head's sink and window tokens kept
+    beside the index, join the same softmax. [N limitations] a ``dense`` head
+    attends every indexed token instead of the selected pages. [reading] The
+    resident tokens are given by the caller as plain rows; they are never
+    indexed or selected.
+    """
     q = np.asarray(q, np.float64).reshape(-1)
-    toks = [t for pg in pages for t in idx.pages[pg]]
-    if not toks:
+    if dense:
+        pages = range(len(idx.pages))
+    toks = np.asarray([t for pg in pages for t in idx.pages[pg]], dtype=np.int64)
+    Kx, Vx = idx.K[toks], idx.V[toks]
+    if resident is not None:
+        Kx = np.concatenate([Kx, np.asarray(resident[0], np.float64).reshape(-1, idx.d)])
+        Vx = np.concatenate([Vx, np.asarray(resident[1], np.float64).reshape(-1, idx.d)])
+    if Kx.shape[0] == 0:
         return np.zeros(idx.d), -np.inf
-    toks = np.asarray(toks, dtype=np.int64)
-    logits = (idx.K[toks] @ q) * scale
+    logits = (Kx @ q) * scale
     m = logits.max()
     w = np.exp(logits - m)
     l = w.sum()
-    return (w @ idx.V[toks]) / l, float(m + np.log(l))
+    return (w @ Vx) / l, float(m + np.log(l))
 
 
 # --------------------------------------------------------------------------

@@ -208,11 +208,12 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def build_case(H, N, d, dtype, C, seed, G=4, levels=3, plog2=4, capacity=None, budget=256, rotate=False):
+def build_case(H, N, d, dtype, C, seed, G=4, levels=3, plog2=4, capacity=None, budget=256, rotate=False,
+               resident=0):
     from ann_retrieval_amd.api import IceIndex
-    say(f"build H={H} N={N} d={d} {dtype} C={C} seed={seed} G={G} L={levels} p=2^-{plog2}")
+    say(f"build H={H} N={N} d={d} {dtype} C={C} seed={seed} G={G} L={levels} p=2^-{plog2} resident={resident}")
     w, gen = synth.clustered_kv(H, N, d, C, dtype, seed, device="cpu", rotate=rotate)
-    ix = IceIndex(H, G, d, dtype, capacity or max(N, 1), levels, plog2, seed, max_budget=budget)
+    ix = IceIndex(H, G, d, dtype, capacity or max(N, 1), levels, plog2, seed, max_budget=budget, resident=resident)
     ix.ice_build(w.K.cuda(), w.V.cuda())
     torch.cuda.synchronize()
     return w, gen, ix
@@ -281,9 +282,11 @@ def check_decode(w, ix, refs, Q, budget, beam, scale=None):
     return out["sel"], out["uni"], out["nuni"]
 
 
-def compare_decode(ix, refs, out):
+def compare_decode(ix, refs, out, resident=None, dense=()):
     """Selections of the heads in `refs` exact after tie-tolerant replay, the
-    union exact, attention within the dtype's tolerance."""
+    union exact, attention within the dtype's tolerance. resident: optional
+    (K_r, V_r) host tensors [H, n, d] attended beside the pages; dense: heads
+    whose attention covers every indexed token."""
     Q, budget, beam, scale = out["Q"], out["budget"], out["beam"], out["scale"]
     sel, uni, nuni, tr, O, lse = out["sel"], out["uni"], out["nuni"], out["tr"], out["O"], out["lse"]
     scale = 1.0 / math.sqrt(ix.d) if scale is None else scale
@@ -296,9 +299,10 @@ def compare_decode(ix, refs, out):
         want = sorted(set(int(x) for x in sel[h].ravel() if x >= 0))
         assert int(nuni[h]) == len(want)
         assert list(uni[h, :len(want)]) == want and np.all(uni[h, len(want):] == -1)
+        res = None if resident is None else (to64(resident[0][h]), to64(resident[1][h]))
         for g in range(ix.G):
-            o_ref, lse_ref = ic.attend(ref, to64(Q[h, g]), want, scale)
-            if want:
+            o_ref, lse_ref = ic.attend(ref, to64(Q[h, g]), want, scale, resident=res, dense=h in dense)
+            if lse_ref > -np.inf:
                 err = attn_error(O[h, g], o_ref)
                 worst = max(worst, err)
                 assert err <= ATOL[ix.dtype], f"head {h} q {g}: attention error {err:.3g}"

@@ -68,6 +68,26 @@ def test_invalid_params_give_zero_sizes(lib):
     p.page_cap = 8
     assert lib.ice_index_bytes(ctypes.byref(p)) == 0
     assert b"page_cap" in lib.ice_last_error()
+    # resident tokens: bounded, and only with the device V pool
+    for kw in [dict(resident=-1), dict(resident=L.ICE_MAX_RESIDENT + 1), dict(resident=16, host_pool=True),
+               dict(capacity=(1 << 26) + 1)]:
+        base = dict(n_heads=2, group=4, d=128, dtype="bf16", capacity=100)
+        base.update(kw)
+        assert lib.ice_index_bytes(ctypes.byref(make_params(**base))) == 0
+    # resident pages add to the blob: 100 tokens -> 7 pages of K and V per head
+    n0 = lib.ice_index_bytes(ctypes.byref(make_params(2, 4, 128, "bf16", 100)))
+    n1 = lib.ice_index_bytes(ctypes.byref(make_params(2, 4, 128, "bf16", 100, resident=100)))
+    assert n1 - n0 >= 2 * 7 * (2 * 16 * 128 * 2 + 4) and n1 - n0 <= 2 * (7 * (2 * 16 * 128 * 2 + 4) + 3 * 256)
+
+
+def test_resident_and_dense_need_a_build(lib):
+    p = make_params(1, 2, 64, "f32", 64, resident=16)
+    h = _fake_handle(lib, p)
+    try:
+        assert lib.ice_set_resident(h, None, None, 0, 0, None) == L.ICE_ERR_STATE
+        assert lib.ice_set_dense(h, None, None) == L.ICE_ERR_STATE
+    finally:
+        lib.ice_destroy(h)
 
 
 def test_argument_checks_run_before_any_launch(lib):

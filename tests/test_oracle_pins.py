@@ -421,6 +421,49 @@ def test_attention_split_combine_identity():
     assert np.allclose(o, o2, rtol=1e-12, atol=1e-14)
 
 
+def test_attention_resident_only_equals_sdpa():
+    """Resident tokens with no selected page: plain softmax attention over them."""
+    r = _rng(11)
+    K, V, _ = _clustered(300, 16, 6, 12)
+    idx = ic.build_head(K, V, 0, 12)
+    Kr, Vr = r.standard_normal((37, 16)), r.standard_normal((37, 16))
+    q = r.standard_normal(16)
+    o, lse = ic.attend(idx, q, [], 0.25, resident=(Kr, Vr))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None, None, None, :], torch.tensor(Kr)[None, None], torch.tensor(Vr)[None, None], scale=0.25)
+    assert np.allclose(o, ref[0, 0, 0].numpy(), rtol=1e-12, atol=1e-12)
+    assert abs(lse - float(torch.logsumexp(torch.tensor(Kr @ q * 0.25), 0))) < 1e-12
+
+
+def test_attention_with_resident_combines_two_softmaxes():
+    """Pages plus resident tokens = the lse-weighted merge of the two parts."""
+    r = _rng(12)
+    K, V, cent = _clustered(800, 8, 10, 13)
+    idx = ic.build_head(K, V, 0, 13)
+    Kr, Vr = r.standard_normal((20, 8)), r.standard_normal((20, 8))
+    q = cent[2]
+    pages = list(range(0, len(idx.pages), 3))
+    o, lse = ic.attend(idx, q, pages, 0.4, resident=(Kr, Vr))
+    a, la = ic.attend(idx, q, pages, 0.4)
+    b, lb = ic.attend(idx, q, [], 0.4, resident=(Kr, Vr))
+    m = max(la, lb)
+    wa, wb = math.exp(la - m), math.exp(lb - m)
+    assert np.allclose(o, (wa * a + wb * b) / (wa + wb), rtol=1e-12, atol=1e-12)
+    assert abs(lse - (m + math.log(wa + wb))) < 1e-12
+
+
+def test_attention_dense_head_ignores_the_selection():
+    """A dense head attends every indexed token, whatever pages are passed."""
+    K, V, cent = _clustered(500, 16, 8, 14)
+    idx = ic.build_head(K, V, 0, 14)
+    q = cent[1]
+    o, lse = ic.attend(idx, q, [0], 0.25, dense=True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None, None, None, :], torch.tensor(K)[None, None], torch.tensor(V)[None, None], scale=0.25)
+    assert np.allclose(o, ref[0, 0, 0].numpy(), rtol=1e-12, atol=1e-12)
+    assert abs(lse - float(torch.logsumexp(torch.tensor(K @ q * 0.25), 0))) < 1e-12
+
+
 # --------------------------------------------------------------------------
 # planted mistakes: each must break at least one pin above
 # --------------------------------------------------------------------------
