@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-host-pool", action="store_true", help="skip the host-pool mode measurement")
+    ap.add_argument("--resident", type=int, default=68,
+                    help="resident (sink + window) tokens per head for the resident-token leg; 0 skips it")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="print a markdown summary of rocprofv3 output instead of benchmarking: one "
@@ -351,7 +353,8 @@ def main():
     w, gen = synth.clustered_kv(H, N, d, C, dtype, a.seed, device=dev, rotate=rotate)
     elt = 2 if dtype == "bf16" else 4
     n_ins = a.steps + a.warmup
-    ix = IceIndex(H, G, d, dtype, N + n_ins, seed=a.seed, max_budget=max(budgets), device=dev)
+    ix = IceIndex(H, G, d, dtype, N + n_ins, seed=a.seed, max_budget=max(budgets), device=dev,
+                  resident=max(a.resident, 0))
 
     # ---- index build: median of a few full builds
     bt = []
@@ -445,6 +448,35 @@ def main():
     if not a.no_host_pool:
         host_pool = time_host_pool(w, Qs, a, H, G, N, d, dtype, a.budget, results[a.budget]["attend_ms"], n_ins)
 
+    # ---- resident sink + window tokens beside the selected pages: the same
+    # decode steps with a.resident extra tokens per head in every softmax
+    resident = None
+    if a.resident > 0:
+        Kr, Vr = synth.resident_tokens(w, a.resident, gen, device=dev)
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record()
+        ix.set_resident(Kr, Vr)
+        r1.record()
+        torch.cuda.synchronize()
+        set_ms = r0.elapsed_time(r1)
+        for s in range(min(a.warmup, 3)):
+            ix.ice_decode(Qs[s], a.budget, a.budget // 16)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(5e7))
+        r0.record()
+        for s in range(a.steps):
+            ix.ice_decode(Qs[a.warmup + s], a.budget, a.budget // 16)
+        r1.record()
+        torch.cuda.synchronize()
+        res_ms = r0.elapsed_time(r1) / a.steps
+        ix.set_resident(None, None)
+        torch.cuda.synchronize()
+        resident = {"tokens_per_head": a.resident, "ms_per_step": res_ms, "set_resident_ms": set_ms,
+                    "extra_bytes_per_step": 2 * H * a.resident * d * elt}
+        print(f"[bench] resident {a.resident} tokens/head T={a.budget}: {res_ms*1000:.1f} us/step; "
+              f"set_resident {set_ms*1000:.1f} us", file=sys.stderr, flush=True)
+
     # ---- insert: one token per head per step
     knew = [synth.new_tokens(w, gen, device=dev) for _ in range(n_ins)]
     torch.cuda.synchronize()
@@ -489,6 +521,8 @@ def main():
     }
     if host_pool is not None:
         out["host_pool"] = host_pool
+    if resident is not None:
+        out["resident"] = resident
     if not a.no_cpu:
         heads = list(range(min(a.cpu_heads, H)))
         t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(3)], a.budget, a.budget // 16,
