@@ -24,7 +24,9 @@ struct ice_index {
   void* host_pool;        // host-pool mode: the caller's pinned V pool (host address)
   int32_t n_tokens;
   int32_t n_dense;        // heads flagged dense (ice_set_dense)
-  bool built;
+  std::vector<uint8_t> dense;       // the flags, host copy
+  std::vector<uint8_t> head_built;  // heads built since the handle was created
+  bool built;             // every head built
 };
 
 namespace {
@@ -256,6 +258,8 @@ int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_ind
   idx->host_pool = nullptr;
   idx->n_tokens = 0;
   idx->n_dense = 0;
+  idx->dense.assign(p->n_heads, 0);
+  idx->head_built.assign(p->n_heads, 0);
   idx->built = false;
   *out = idx;
   return ICE_OK;
@@ -287,12 +291,20 @@ int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes
 
 int32_t ice_n_tokens(const ice_index* idx) { return idx ? idx->n_tokens : -1; }
 
-int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, void* ws,
-              size_t ws_bytes, void* stream) {
+int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, int32_t h0,
+                    int32_t n_heads, void* ws, size_t ws_bytes, void* stream) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  const int H = idx->p.n_heads;
+  if (h0 < 0 || n_heads < 1 || h0 > H - n_heads)
+    return fail(ICE_ERR_ARG, "heads [%d, %d) outside [0, %d)", h0, h0 + n_heads, H);
   if (n_tokens < 0) return fail(ICE_ERR_ARG, "n_tokens must be >= 0");
   if (n_tokens > idx->p.capacity)
     return fail(ICE_ERR_CAPACITY, "n_tokens %d exceeds capacity %d", n_tokens, idx->p.capacity);
+  bool any_built = false, range_built = true;
+  for (int h = 0; h < H; ++h) any_built |= idx->head_built[h] != 0;
+  for (int h = h0; h < h0 + n_heads; ++h) range_built &= idx->head_built[h] != 0;
+  if (n_heads < H && any_built && n_tokens != idx->n_tokens)
+    return fail(ICE_ERR_ARG, "every head holds %d tokens; a build of some heads must keep that count", idx->n_tokens);
   if (n_tokens > 0) {
     if (!K || !V) return fail(ICE_ERR_ARG, "K or V is null");
     if (head_stride < (int64_t)n_tokens * idx->p.d) return fail(ICE_ERR_ARG, "head_stride smaller than n_tokens*d");
@@ -304,12 +316,34 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
                 (long long)idx->W.build_bytes);
   if (((uintptr_t)ws & 255u) != 0) return fail(ICE_ERR_ARG, "workspace must be 256-byte aligned");
   if (host_mode(idx->L) && !idx->L.vpool) return fail(ICE_ERR_STATE, "build before ice_attach_host_pool");
-  hipError_t e = launch_build(idx->L, idx->W, idx->blob, K, V, n_tokens, head_stride, ws, idx->built,
+  // the range as an index of its own: blob, workspace and host pool start at
+  // head h0, and the promotion draws use the absolute head numbers
+  DevLayout L = idx->L;
+  L.H = n_heads;
+  L.h0 = h0;
+  if (L.vpool) L.vpool += (int64_t)h0 * L.vpool_head_bytes;
+  char* blob = static_cast<char*>(idx->blob) + (int64_t)h0 * L.head_bytes;
+  char* wsr = static_cast<char*>(ws) + (int64_t)h0 * idx->W.head_bytes;
+  hipError_t e = launch_build(L, idx->W, blob, K, V, n_tokens, head_stride, wsr, range_built,
                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ice_build launch");
+  if (!range_built)     // headers were cleared: no dense flags there any more
+    for (int h = h0; h < h0 + n_heads; ++h) {
+      idx->n_dense -= idx->dense[h];
+      idx->dense[h] = 0;
+    }
+  for (int h = h0; h < h0 + n_heads; ++h) idx->head_built[h] = 1;
   idx->n_tokens = n_tokens;
-  idx->built = true;
+  bool all = true;
+  for (int h = 0; h < H; ++h) all &= idx->head_built[h] != 0;
+  idx->built = all;
   return ICE_OK;
+}
+
+int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, void* ws,
+              size_t ws_bytes, void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  return ice_build_heads(idx, K, V, n_tokens, head_stride, 0, idx->p.n_heads, ws, ws_bytes, stream);
 }
 
 int ice_insert(ice_index* idx, const void* k_new, const void* v_new, int32_t n_new, void* ws, size_t ws_bytes,
@@ -399,6 +433,7 @@ int ice_set_dense(ice_index* idx, const uint8_t* dense, void* stream) {
                     flags.data(), sizeof(int32_t), sizeof(int32_t), (size_t)idx->p.n_heads, hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "ice_set_dense copy");
   idx->n_dense = n_dense;
+  for (int h = 0; h < idx->p.n_heads; ++h) idx->dense[h] = (uint8_t)flags[h];
   return ICE_OK;
 }
 

@@ -38,6 +38,7 @@ static_assert(sizeof(Hdr) == sizeof(ice_head_stats), "header mirrors ice_head_st
 // which is stored at owner slot `cap`.
 struct DevLayout {
   int32_t H, G, d, dtype, L, plog2, cap, ntab;
+  int32_t h0;                    // absolute number of head 0 (a build of a head range)
   uint64_t seed;
   int32_t ncap[ICE_MAX_LEVELS];  // max over heads of #positions < cap with level >= l
   int32_t pcap[ICE_MAX_LEVELS];  // page capacity of table l

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, voi
     acc = group_sum_d<G::LPR>(acc);
     if (t < n && (lane % G::LPR) == 0) {
       n2[t] = acc;
-      lev[t] = (int8_t)draw_level(L.seed, h, t, L.L, L.plog2);
+      lev[t] = (int8_t)draw_level(L.seed, L.h0 + h, t, L.L, L.plog2);
       mx = fmax(mx, acc);
     }
   }

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kInsertWaves * 64) void k_insert(DevLayout L, void*
     double n2 = 0.0;
     for (int w = 0; w < NW; ++w) n2 += red_d[w];
     const float et = (float)sqrt(fmax(0.0, M2 - n2));
-    const int lam = min(Ltop, draw_level(L.seed, h, t, L.L, L.plog2));
+    const int lam = min(Ltop, draw_level(L.seed, L.h0 + h, t, L.L, L.plog2));
 
     // parent at level lam among the current points of level lam+1: 16 rows
     // per wave pass, U passes' loads in flight, then a (score desc, token

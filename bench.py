@@ -58,6 +58,7 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-host-pool", action="store_true", help="skip the host-pool mode measurement")
+    ap.add_argument("--no-pipeline", action="store_true", help="skip the per-layer build pipeline measurement")
     ap.add_argument("--resident", type=int, default=68,
                     help="resident (sink + window) tokens per head for the resident-token leg; 0 skips it")
     ap.add_argument("--seed", type=int, default=0)
@@ -246,6 +247,85 @@ def head_meta(ix, H, cap):
             m["blocks1"] = np.bincount(own1, minlength=cap + 1)
         meta.append(m)
     ix.meta = meta
+
+
+def time_pipeline(ix, w, a, H, N, heads_per_layer=8):
+    """Prefill with the index built one layer at a time beside the model's
+    work (the pages' pipeline of index construction and computation). The
+    model's work per layer is stood in for by the three MLP GEMMs of a
+    Llama-3.1-8B layer over the prompt (bf16, 4096 x 14336, N rows), about
+    12.7 TFLOP at 36k tokens. Serial: every layer's GEMMs, then its build, on
+    one stream. Pipelined: the build of layer i runs on a second stream once
+    layer i's GEMMs are done, while layer i+1's GEMMs proceed. The index is
+    the same either way (a build of head ranges equals a build of all heads)."""
+    import torch
+    n_layers = H // heads_per_layer
+    dev = w.K.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(a.seed + 7)
+    dm, df = 4096, 14336
+    X = (torch.randn(N, dm, device=dev, generator=gen) * 0.05).to(torch.bfloat16)
+    Wg = (torch.randn(dm, df, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    Wu = (torch.randn(dm, df, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    Wd = (torch.randn(df, dm, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+
+    def model_layer():
+        h = torch.nn.functional.silu(X @ Wg) * (X @ Wu)
+        return h @ Wd
+
+    def build_layer(i, stream=None):
+        h0 = i * heads_per_layer
+        ix.ice_build_heads(w.K[h0:h0 + heads_per_layer], w.V[h0:h0 + heads_per_layer], h0, stream=stream)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    model_layer()
+    build_layer(0)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for i in range(n_layers):
+        model_layer()
+    e1.record()
+    torch.cuda.synchronize()
+    model_ms = e0.elapsed_time(e1)
+    e0.record()
+    for i in range(n_layers):
+        build_layer(i)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    e0.record()
+    for i in range(n_layers):
+        model_layer()
+        build_layer(i)
+    e1.record()
+    torch.cuda.synchronize()
+    serial_ms = e0.elapsed_time(e1)
+    side = torch.cuda.Stream(device=dev)
+    main = torch.cuda.current_stream(dev)
+    e0.record()
+    for i in range(n_layers):
+        model_layer()
+        done = ev()
+        done.record(main)
+        side.wait_event(done)
+        build_layer(i, stream=side)
+    end_side = ev()
+    end_side.record(side)
+    main.wait_event(end_side)
+    e1.record()
+    torch.cuda.synchronize()
+    pipe_ms = e0.elapsed_time(e1)
+    del X, Wg, Wu, Wd
+    torch.cuda.empty_cache()
+    hidden = (serial_ms - pipe_ms) / build_ms if build_ms > 0 else 0.0
+    print(f"[bench] prefill pipeline, {n_layers} layers: model {model_ms:.1f} ms, per-layer builds {build_ms:.1f} ms, "
+          f"serial {serial_ms:.1f} ms, pipelined {pipe_ms:.1f} ms ({hidden * 100:.0f}% of the build hidden)",
+          file=sys.stderr, flush=True)
+    return {"layers": n_layers, "heads_per_layer": heads_per_layer, "model_ms": model_ms,
+            "per_layer_build_ms": build_ms, "serial_ms": serial_ms, "pipelined_ms": pipe_ms,
+            "build_hidden_frac": hidden,
+            "model_stand_in": "Llama-3.1-8B MLP GEMMs (bf16, 4096 x 14336) over the prompt, per layer"}
 
 
 def time_host_pool(w, Qs, a, H, G, N, d, dtype, budget, dev_attend_ms, n_ins):
@@ -448,6 +528,12 @@ def main():
     if not a.no_host_pool:
         host_pool = time_host_pool(w, Qs, a, H, G, N, d, dtype, a.budget, results[a.budget]["attend_ms"], n_ins)
 
+    pipeline = None
+    if not a.no_pipeline and H % 8 == 0 and H // 8 >= 2:
+        pipeline = time_pipeline(ix, w, a, H, N)
+        ix.ice_build(w.K, w.V)       # the index as a whole build leaves it, for the legs below
+        torch.cuda.synchronize()
+
     # ---- resident sink + window tokens beside the selected pages: the same
     # decode steps with a.resident extra tokens per head in every softmax
     resident = None
@@ -523,6 +609,8 @@ def main():
         out["host_pool"] = host_pool
     if resident is not None:
         out["resident"] = resident
+    if pipeline is not None:
+        out["prefill_pipeline"] = pipeline
     if not a.no_cpu:
         heads = list(range(min(a.cpu_heads, H)))
         t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(3)], a.budget, a.budget // 16,

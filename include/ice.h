@@ -127,6 +127,20 @@ int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes
 int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
               void* ws, size_t ws_bytes, void* stream);
 
+/* Build of heads h0 .. h0+n_heads-1 only, as ice_build does it for every
+ * head (the aitangshan.cn article, section 4: the index of one layer is built
+ * while the model works on the next; the notes' overall framework). K, V:
+ * device, the rows of those heads, [n_heads][n_tokens][d] at head_stride.
+ * Every head of an index holds the same token count: once any head is built,
+ * a build of fewer than all heads must pass that count (ICE_ERR_ARG
+ * otherwise). Builds of disjoint head ranges may run at the same time on
+ * different streams with one workspace, each head using its own part of it.
+ * Select, attend, decode and insert need every head built (ICE_ERR_STATE
+ * before). A range rebuilt as a whole keeps its resident tokens and dense
+ * flags; heads built for the first time start with neither. */
+int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
+                    int32_t h0, int32_t n_heads, void* ws, size_t ws_bytes, void* stream);
+
 /* Incremental insert (the article's section 3: no rebuild; the notes' key
  * design 2: a node over the page size splits off a new page). k_new, v_new:
  * device, [H][n_new][d] contiguous, k_new 16-byte aligned (ICE_ERR_ARG
@@ -198,7 +212,9 @@ int ice_set_dense(ice_index* idx, const uint8_t* dense, void* stream);
  * fp32 sums in the attention. For bf16 keys with beam and budget/16 at most
  * 64 it runs as one kernel per step (each head selects, then attends its own
  * union, with no pass through memory in between); otherwise it enqueues the
- * two calls' kernels. */
+ * two calls' kernels. The one-kernel step deals pages to its waves as they
+ * become free, so its fp32 outputs may differ between runs in the last bits;
+ * selections and unions are exact. */
 int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32_t beam,
                int32_t* sel, int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse,
                void* ws, size_t ws_bytes, void* stream);

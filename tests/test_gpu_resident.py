@@ -93,3 +93,4 @@ def test_resident_argument_errors():
     with pytest.raises(ValueError):
         ix.set_dense([True])                           # wrong length
     assert ix.stats(0)["n_resident"] == 0
+
