@@ -47,6 +47,8 @@ _SIGNATURES = {
     "ice_build": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p, c_size, c_void_p]),
     "ice_build_heads": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_i32, c_i32, c_void_p, c_size,
                                        c_void_p]),
+    "ice_build_reuse": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_void_p,
+                                       c_size, c_void_p]),
     "ice_insert": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_void_p, c_size, c_void_p]),
     "ice_select": (ctypes.c_int, [c_void_p, c_void_p, c_i32, c_i32, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_size, c_void_p]),

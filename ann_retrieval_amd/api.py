@@ -150,6 +150,16 @@ class IceIndex:
         check(self.lib.ice_build_heads(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0), h0, K.shape[0],
                                        _ptr(self.ws), self.ws_bytes, s), "ice_build_heads")
 
+    def ice_build_reuse(self, K: torch.Tensor, V: torch.Tensor, h0: int, src_h0: int, stream=None) -> None:
+        """Heads h0 .. h0 + K.shape[0] - 1 take the layout of heads src_h0 .. and their own rows K, V."""
+        if K.device != self.device or K.dtype != self.tdtype or K.dim() != 3 or K.shape[2] != self.d:
+            raise TypeError(f"K must be a {self.tdtype} [n_heads, n, {self.d}] tensor on {self.device}")
+        if K.shape != V.shape or K.stride() != V.stride() or K.stride(2) != 1 or K.stride(1) != self.d:
+            raise ValueError("K and V must have the same shape and strides, rows contiguous")
+        s = _stream_ptr(self.device) if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        check(self.lib.ice_build_reuse(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0), h0, K.shape[0], src_h0,
+                                       _ptr(self.ws), self.ws_bytes, s), "ice_build_reuse")
+
     def ice_insert(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
         self._check_kv(k_new, "k_new")
         self._check_kv(v_new, "v_new")

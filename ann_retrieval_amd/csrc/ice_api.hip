@@ -340,6 +340,52 @@ int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_toke
   return ICE_OK;
 }
 
+int ice_build_reuse(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, int32_t h0,
+                    int32_t n_heads, int32_t src_h0, void* ws, size_t ws_bytes, void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  const int H = idx->p.n_heads;
+  if (h0 < 0 || n_heads < 1 || h0 > H - n_heads || src_h0 < 0 || src_h0 > H - n_heads)
+    return fail(ICE_ERR_ARG, "heads [%d, %d) or source heads [%d, %d) outside [0, %d)", h0, h0 + n_heads, src_h0,
+                src_h0 + n_heads, H);
+  if (h0 < src_h0 + n_heads && src_h0 < h0 + n_heads) return fail(ICE_ERR_ARG, "head ranges overlap");
+  for (int h = src_h0; h < src_h0 + n_heads; ++h)
+    if (!idx->head_built[h]) return fail(ICE_ERR_STATE, "source head %d is not built", h);
+  if (n_tokens != idx->n_tokens)
+    return fail(ICE_ERR_ARG, "the source heads hold %d tokens, not %d", idx->n_tokens, n_tokens);
+  if (n_tokens > 0) {
+    if (!K || !V) return fail(ICE_ERR_ARG, "K or V is null");
+    if (head_stride < (int64_t)n_tokens * idx->p.d) return fail(ICE_ERR_ARG, "head_stride smaller than n_tokens*d");
+    if (!aligned16(K) || !aligned16(V) || (head_stride * idx->L.elt) % 16 != 0)
+      return fail(ICE_ERR_ARG, "K, V and the head stride must be 16-byte aligned");
+  }
+  if (!ws || ws_bytes < (size_t)idx->W.build_bytes)
+    return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, build needs %lld", ws_bytes,
+                (long long)idx->W.build_bytes);
+  if (((uintptr_t)ws & 255u) != 0) return fail(ICE_ERR_ARG, "workspace must be 256-byte aligned");
+  bool range_built = true;
+  for (int h = h0; h < h0 + n_heads; ++h) range_built &= idx->head_built[h] != 0;
+  DevLayout L = idx->L;
+  L.H = n_heads;
+  L.h0 = h0;
+  if (L.vpool) L.vpool += (int64_t)h0 * L.vpool_head_bytes;
+  char* blob = static_cast<char*>(idx->blob) + (int64_t)h0 * L.head_bytes;
+  const char* src = static_cast<const char*>(idx->blob) + (int64_t)src_h0 * L.head_bytes;
+  char* wsr = static_cast<char*>(ws) + (int64_t)h0 * idx->W.head_bytes;
+  hipError_t e = launch_build_reuse(L, idx->W, blob, src, K, V, n_tokens, head_stride, wsr, range_built,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ice_build_reuse launch");
+  if (!range_built)
+    for (int h = h0; h < h0 + n_heads; ++h) {
+      idx->n_dense -= idx->dense[h];
+      idx->dense[h] = 0;
+    }
+  for (int h = h0; h < h0 + n_heads; ++h) idx->head_built[h] = 1;
+  bool all = true;
+  for (int h = 0; h < H; ++h) all &= idx->head_built[h] != 0;
+  idx->built = all;
+  return ICE_OK;
+}
+
 int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, void* ws,
               size_t ws_bytes, void* stream) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");

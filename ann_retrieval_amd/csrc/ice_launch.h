@@ -6,6 +6,10 @@
 namespace ice {
 
 // k_build.hip
+// heads of `blob` take the layout of the same-numbered heads of `src` (both
+// range starts) and place their own rows into it
+hipError_t launch_build_reuse(const DevLayout& L, const WsLayout& W, void* blob, const void* src, const void* K,
+                              const void* V, int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s);
 // keep: a rebuild, which keeps the headers' resident counts and dense flags
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
                         int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s);

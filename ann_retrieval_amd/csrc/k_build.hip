@@ -46,10 +46,11 @@ __global__ void k_fill_heads(void* base, int64_t head_bytes, int64_t off, int64_
 }
 
 // |k|^2 in fp64 (exact products for bf16 and fp32 inputs), the promotion
-// level, and the per-head maximum M^2. One block covers 64 tokens of a head.
+// level (unless `draw` is false: a layout taken from another head keeps its
+// levels), and the per-head maximum M^2. One block covers 64 tokens of a head.
 template <int D, class T>
 __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, void* blob, const T* K,
-                                                    int64_t hstride, int n, void* ws) {
+                                                    int64_t hstride, int n, void* ws, bool draw) {
   using G = RowGeo<D, T>;
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, voi
     acc = group_sum_d<G::LPR>(acc);
     if (t < n && (lane % G::LPR) == 0) {
       n2[t] = acc;
-      lev[t] = (int8_t)draw_level(L.seed, L.h0 + h, t, L.L, L.plog2);
+      if (draw) lev[t] = (int8_t)draw_level(L.seed, L.h0 + h, t, L.L, L.plog2);
       mx = fmax(mx, acc);
     }
   }
@@ -481,7 +482,7 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
     if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_ocnt[l], L.cap + 1, 0, s))) return err;
   }
   if (n > 0) {
-    k_norm_level<D, T><<<dim3(blocks_for(n, 64), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws);
+    k_norm_level<D, T><<<dim3(blocks_for(n, 64), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws, true);
     ICE_CHECK();
   }
   k_lift_compact<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
@@ -534,6 +535,89 @@ hipError_t launch_fill_heads(void* base, int64_t head_bytes, int H, int64_t off,
   if (n <= 0) return hipSuccess;
   k_fill_heads<<<dim3(blocks_for(n, 256 * 4), (unsigned)H), 256, 0, s>>>(base, head_bytes, off, n, value);
   return hipGetLastError();
+}
+
+// Header of a head that takes another head's layout: the structure's counts
+// from the source, no parent statistics (no parent was chosen), M^2 zero for
+// the lift to fill, and its own resident count and dense flag when `keep`.
+__global__ void k_reuse_header(DevLayout L, void* blob, const void* src, bool keep) {
+  const int h = blockIdx.x;
+  Hdr* d = at<Hdr>(head_base(blob, L, h), L.off_hdr);
+  const Hdr* sh = at<Hdr>(head_base(src, L, h), L.off_hdr);
+  if (threadIdx.x == 0) {
+    const int nr = keep ? d->n_resident : 0, dn = keep ? d->dense : 0;
+    Hdr x = *sh;
+    x.clamps = x.splits = x.near_ties = x.overflow = x.sync_timeouts = 0;
+    x.n_resident = nr;
+    x.dense = dn;
+    x.M2 = 0.0;
+    *d = x;
+  }
+}
+
+template <int D, class T>
+hipError_t build_reuse_typed(const DevLayout& L, const WsLayout& W, void* blob, const void* src, const void* Kv,
+                             const void* Vv, int n, int64_t hstride, void* ws, bool keep, hipStream_t s) {
+  const T* K = static_cast<const T*>(Kv);
+  const T* V = static_cast<const T*>(Vv);
+  const unsigned H = (unsigned)L.H;
+  hipError_t err;
+  // the layout arrays, head by head (strided copies over the range)
+  auto copy = [&](int64_t off, int64_t bytes) -> hipError_t {
+    if (bytes <= 0) return hipSuccess;
+    return hipMemcpy2DAsync(static_cast<char*>(blob) + off, (size_t)L.head_bytes, static_cast<const char*>(src) + off,
+                            (size_t)L.head_bytes, (size_t)bytes, H, hipMemcpyDeviceToDevice, s);
+  };
+  const int64_t cap = L.cap;
+  if ((err = copy(L.off_lev, cap))) return err;
+  for (int l = 0; l < L.ntab; ++l) {
+    const int64_t P = L.pcap[l];       // the resident pages stay the head's own
+    if ((err = copy(L.off_parent[l], cap * 4))) return err;
+    if ((err = copy(L.off_pg_tok[l], P * ICE_PAGE_CAP * 4))) return err;
+    if ((err = copy(L.off_pg_cnt[l], P * 4))) return err;
+    if ((err = copy(L.off_pg_next[l], P * 4))) return err;
+    if ((err = copy(L.off_pg_owner[l], P * 4))) return err;
+    if ((err = copy(L.off_first[l], (cap + 1) * 4))) return err;
+    if ((err = copy(L.off_tail[l], (cap + 1) * 4))) return err;
+    if ((err = copy(L.off_orun[l], (cap + 1) * 4))) return err;
+    if ((err = copy(L.off_ocnt[l], (cap + 1) * 4))) return err;
+  }
+  if ((err = copy(L.off_top_tok, (int64_t)L.topcap * 4))) return err;
+  k_reuse_header<<<H, 64, 0, s>>>(L, blob, src, keep);
+  if ((err = hipGetLastError())) return err;
+  // the head's own lift
+  if (n > 0) {
+    k_norm_level<D, T><<<dim3(blocks_for(n, 64), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws, false);
+    if ((err = hipGetLastError())) return err;
+  }
+  k_lift_compact<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
+  if ((err = hipGetLastError())) return err;
+  if (n == 0) return hipSuccess;
+  // its own rows into the pages
+  using G = RowGeo<D, T>;
+  const int last = L.L >= 2 ? L.L - 2 : 0;
+  for (int level = 0; level <= last; ++level) {
+    k_copy_pages<D, T><<<dim3(blocks_for((int64_t)L.pcap[level] * ICE_PAGE_CAP, 4 * G::RPP * 8), H), 256, 0, s>>>(
+        L, K, hstride, blob, level);
+    if ((err = hipGetLastError())) return err;
+  }
+  k_copy_vt<D, T><<<dim3(blocks_for(L.pcap[0], 4 * 4), H), 256, 0, s>>>(L, V, hstride, blob);
+  if ((err = hipGetLastError())) return err;
+  if (L.L >= 2) {
+    k_copy_top<D, T><<<dim3(blocks_for(L.topcap, 4 * G::RPP * 4), H), 256, 0, s>>>(L, K, hstride, blob);
+    if ((err = hipGetLastError())) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_build_reuse(const DevLayout& L, const WsLayout& W, void* blob, const void* src, const void* K,
+                              const void* V, int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s) {
+  if (L.dtype == ICE_BF16) {
+    if (L.d == 128) return build_reuse_typed<128, uint16_t>(L, W, blob, src, K, V, n_tokens, head_stride, ws, keep, s);
+    return build_reuse_typed<64, uint16_t>(L, W, blob, src, K, V, n_tokens, head_stride, ws, keep, s);
+  }
+  if (L.d == 128) return build_reuse_typed<128, float>(L, W, blob, src, K, V, n_tokens, head_stride, ws, keep, s);
+  return build_reuse_typed<64, float>(L, W, blob, src, K, V, n_tokens, head_stride, ws, keep, s);
 }
 
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,

@@ -328,6 +328,37 @@ def time_pipeline(ix, w, a, H, N, heads_per_layer=8):
             "model_stand_in": "Llama-3.1-8B MLP GEMMs (bf16, 4096 x 14336) over the prompt, per layer"}
 
 
+def time_reuse(ix, w, a, H, N, heads_per_layer=8):
+    """Index build with inter-layer reuse: every odd layer takes the layout of
+    the layer before it (its own rows and lift, no parent search), against
+    building every layer. Median of 3 runs each."""
+    import torch
+    n_layers = H // heads_per_layer
+    hp = heads_per_layer
+
+    def run(reuse):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n_layers):
+            h0 = i * hp
+            if reuse and i % 2 == 1:
+                ix.ice_build_reuse(w.K[h0:h0 + hp], w.V[h0:h0 + hp], h0, h0 - hp)
+            else:
+                ix.ice_build_heads(w.K[h0:h0 + hp], w.V[h0:h0 + hp], h0)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    run(True)
+    per_layer = sorted(run(False) for _ in range(3))[1]
+    reuse = sorted(run(True) for _ in range(3))[1]
+    print(f"[bench] per-layer builds {per_layer:.1f} ms; with every odd layer reusing the one before {reuse:.1f} ms",
+          file=sys.stderr, flush=True)
+    return {"layers": n_layers, "per_layer_build_ms": per_layer, "reuse_every_other_layer_ms": reuse,
+            "index_keys_per_s_with_reuse": H * N / (reuse / 1000.0)}
+
+
 def time_host_pool(w, Qs, a, H, G, N, d, dtype, budget, dev_attend_ms, n_ins):
     """Host-pool mode on the same workload: V pages in pinned host memory, each
     step gathers the union's V pages over the host link before attending.
@@ -528,9 +559,10 @@ def main():
     if not a.no_host_pool:
         host_pool = time_host_pool(w, Qs, a, H, G, N, d, dtype, a.budget, results[a.budget]["attend_ms"], n_ins)
 
-    pipeline = None
+    pipeline = reuse = None
     if not a.no_pipeline and H % 8 == 0 and H // 8 >= 2:
         pipeline = time_pipeline(ix, w, a, H, N)
+        reuse = time_reuse(ix, w, a, H, N)
         ix.ice_build(w.K, w.V)       # the index as a whole build leaves it, for the legs below
         torch.cuda.synchronize()
 
@@ -611,6 +643,8 @@ def main():
         out["resident"] = resident
     if pipeline is not None:
         out["prefill_pipeline"] = pipeline
+    if reuse is not None:
+        out["index_reuse"] = reuse
     if not a.no_cpu:
         heads = list(range(min(a.cpu_heads, H)))
         t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(3)], a.budget, a.budget // 16,

@@ -128,8 +128,8 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
               void* ws, size_t ws_bytes, void* stream);
 
 /* Build of heads h0 .. h0+n_heads-1 only, as ice_build does it for every
- * head (the aitangshan.cn article, section 4: the index of one layer is built
- * while the model works on the next; the notes' overall framework). K, V:
+ * head (the aitangshan.cn article, section 4, and the notes' key design 4:
+ * the index of one layer is built while the model works on the next). K, V:
  * device, the rows of those heads, [n_heads][n_tokens][d] at head_stride.
  * Every head of an index holds the same token count: once any head is built,
  * a build of fewer than all heads must pass that count (ICE_ERR_ARG
@@ -140,6 +140,19 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
  * flags; heads built for the first time start with neither. */
 int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
                     int32_t h0, int32_t n_heads, void* ws, size_t ws_bytes, void* stream);
+
+/* Index reuse across layers (the aitangshan.cn article, section 5: the
+ * accelerated variant IceCache(reuse) shares the index between layers; the
+ * notes' key design 4 stacks page reuse on the prefill pipeline). Heads h0 .. h0+n_heads-1 take the layout of the built heads
+ * src_h0 .. src_h0+n_heads-1, head by head in order: levels, parents, which
+ * tokens share a page and in what order, the top list. They place their own
+ * K and V rows ([n_heads][n_tokens][d] at head_stride, device) into it and
+ * lift their own keys (M and e). Their selection then scores their own keys
+ * inside the shared structure. n_tokens must equal the source heads' count;
+ * the ranges must not overlap. No parent search runs, so it costs copies
+ * only. Later inserts into these heads follow their own promotion draws. */
+int ice_build_reuse(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
+                    int32_t h0, int32_t n_heads, int32_t src_h0, void* ws, size_t ws_bytes, void* stream);
 
 /* Incremental insert (the article's section 3: no rebuild; the notes' key
  * design 2: a node over the page size splits off a new page). k_new, v_new:

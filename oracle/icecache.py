@@ -361,6 +361,40 @@ def build_head(K, V, head: int, seed: int, levels: int = 3, promote_log2: int = 
                      children=children, top=top)
 
 
+def build_head_reuse(K, V, src: HeadIndex, head: int) -> HeadIndex:
+    """[A §五 IceCache(reuse); N key design 4 "page reuse"] one layer's index
+    serving another layer's head.
+
+    [reading] The pages name inter-layer index reuse without its steps. Here
+    the head takes ``src``'s structure as it stands (levels, parents, which
+    tokens share a page and in what order, the child lists, the top list) and
+    keeps its own keys, values and lift (M and e), so its selection scores its
+    own keys inside the shared structure. Both hold the same token count.
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    if K.shape[0] != src.n:
+        raise ValueError("the reusing head must hold as many tokens as its source")
+    n2, M2, e = lift(K)
+    X = lifted(K, e)
+    dist = []
+    for l in range(src.L_top):
+        par = src.parent[l]
+        dst = np.full(src.n, np.nan)
+        has = np.nonzero(par >= 0)[0]
+        for t in has:
+            dst[t] = float(_sq_dist(X[t], X[par[t]:par[t] + 1])[0])
+        dist.append(dst)
+    return HeadIndex(head=head, seed=src.seed, levels=src.levels, promote_log2=src.promote_log2,
+                     page_cap=src.page_cap, K=K, V=V, n2=n2, e=e, M2=M2, lev=src.lev.copy(), L_top=src.L_top,
+                     parent=[p.copy() for p in src.parent], dist=dist,
+                     second=[np.full(src.n, np.inf) for _ in range(src.L_top)],
+                     pages=[list(p) for p in src.pages], page_owner=list(src.page_owner),
+                     owner_pages={o: list(ps) for o, ps in src.owner_pages.items()},
+                     children={l: {o: list(c) for o, c in ch.items()} for l, ch in src.children.items()},
+                     top=list(src.top))
+
+
 # --------------------------------------------------------------------------
 # Incremental insert [A §三 "no rebuild"; N key design 2 "split on overflow"]
 # --------------------------------------------------------------------------

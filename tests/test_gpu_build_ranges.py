@@ -58,3 +58,46 @@ def test_build_by_head_ranges_on_two_streams():
     # a range build must keep the index's token count
     with pytest.raises(L.IceError):
         part.ice_build_heads(K[:2, :N - 1], V[:2, :N - 1], 0)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_reuse_layout_across_layers(dtype, d):
+    """Heads 2, 3 (a second layer) take the layout of heads 0, 1 and their own
+    rows: the structure equals the source's bit for bit, the lift and the page
+    pool are their own, and select + attend match the oracle's reused index."""
+    import gpu_support as gs
+    from ann_retrieval_amd.api import IceIndex
+    from oracle import icecache as ic
+    H, N = 4, 1800
+    say(f"reuse across layers H={H} N={N} d={d} {dtype}")
+    w, gen = synth.clustered_kv(H, N, d, 16, dtype, 25, device="cpu")
+    K, V = w.K.cuda(), w.V.cuda()
+    ix = IceIndex(H, 2, d, dtype, N + 8, seed=25, max_budget=128)
+    ix.ice_build_heads(K[:2], V[:2], 0)
+    ix.ice_build_reuse(K[2:], V[2:], 2, 0)
+    torch.cuda.synchronize()
+    refs = gs.check_build(w, ix, [0, 1], 25, 3, 4)
+    for h in (2, 3):
+        g, s = gs.read_head(ix, h), gs.read_head(ix, h - 2)
+        assert np.array_equal(g.lev, s.lev) and g.L_top == s.L_top and g.n_top == s.n_top
+        assert all(np.array_equal(a, b) for a, b in zip(g.parent, s.parent))
+        for ta, tb in zip(g.tables, s.tables):
+            assert np.array_equal(ta["tok"], tb["tok"])
+        ref = ic.build_head_reuse(gs.to64(w.K[h]), gs.to64(w.V[h]), refs[h - 2], h)
+        assert abs(g.stats["M2"] - ref.M2) <= 1e-12 * max(ref.M2, 1e-300)
+        assert np.allclose(g.e, ref.e, rtol=2e-6, atol=2e-6 * np.sqrt(ref.M2))
+        assert g.stats["near_ties"] == 0 and g.stats["splits"] == 0
+        P = len(g.tables[0]["pages"])
+        nd = np.int16 if dtype == "bf16" else np.int32
+        kp = ix.export(h, L.ICE_EXP_PAGE_K, 0, np_dtype=nd).reshape(-1, 16, d)[:P]
+        vp = ix.export(h, L.ICE_EXP_PAGE_V, 0, np_dtype=nd).reshape(-1, 16, d)[:P]
+        tok = g.tables[0]["tok"]
+        valid = tok >= 0
+        assert np.array_equal(kp[valid], gs.raw_rows(w.K[h])[tok[valid]])
+        assert np.array_equal(vp[valid], gs.raw_rows(w.V[h])[tok[valid]])
+        refs[h] = ref
+    for _ in range(2):
+        gs.check_decode(w, ix, refs, synth.decode_queries(w, 2, gen), 128, 8)
+    # the source must be built and hold the same count; ranges must not overlap
+    with pytest.raises(L.IceError):
+        ix.ice_build_reuse(K[1:3], V[1:3], 1, 0)

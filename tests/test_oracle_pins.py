@@ -464,6 +464,30 @@ def test_attention_dense_head_ignores_the_selection():
     assert abs(lse - float(torch.logsumexp(torch.tensor(K @ q * 0.25), 0))) < 1e-12
 
 
+def test_reuse_keeps_the_structure_and_lifts_its_own_keys():
+    K, V, cent = _clustered(900, 16, 10, 15)
+    src = ic.build_head(K, V, 0, 15)
+    r = _rng(16)
+    K2, V2 = K + 0.1 * r.standard_normal(K.shape), r.standard_normal(V.shape)
+    idx = ic.build_head_reuse(K2, V2, src, 1)
+    assert idx.pages == src.pages and idx.top == src.top and np.array_equal(idx.lev, src.lev)
+    assert all(np.array_equal(a, b) for a, b in zip(idx.parent, src.parent))
+    # its own lift: the largest key has e = 0 and every lifted norm is M
+    assert idx.M2 == float((K2 * K2).sum(1).max())
+    assert np.allclose((idx.X() ** 2).sum(1), idx.M2, rtol=1e-12)
+    # attention reads its own rows
+    q = cent[4]
+    o, _ = ic.attend(idx, q, [0, 1], 0.25)
+    toks = idx.pages[0] + idx.pages[1]
+    w = np.exp(K2[toks] @ q * 0.25 - (K2[toks] @ q * 0.25).max())
+    assert np.allclose(o, (w @ V2[toks]) / w.sum(), rtol=1e-12, atol=1e-12)
+    # with the same keys the reused index selects exactly as its source
+    same = ic.build_head_reuse(K, V, src, 1)
+    for g in range(4):
+        qq = cent[g] + 0.2 * r.standard_normal(16)
+        assert ic.select(same, qq, 64, 4)["sel"] == ic.select(src, qq, 64, 4)["sel"]
+
+
 # --------------------------------------------------------------------------
 # planted mistakes: each must break at least one pin above
 # --------------------------------------------------------------------------
