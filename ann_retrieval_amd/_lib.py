@@ -18,7 +18,7 @@ c_size, c_void_p, c_char_p = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
 
 ICE_OK, ICE_ERR_ARG, ICE_ERR_DTYPE, ICE_ERR_STATE, ICE_ERR_CAPACITY, ICE_ERR_HIP = 0, -1, -2, -3, -4, -5
 ICE_F32, ICE_BF16 = 0, 1
-ICE_HOST_POOL = 1
+ICE_HOST_POOL, ICE_SPLIT_RESORT, ICE_RESPLIT_MAX = 1, 2, 1024
 ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM, ICE_MAX_RESIDENT = 16, 4, 16, 256, 4096
 (ICE_EXP_LEVEL, ICE_EXP_LIFT, ICE_EXP_PARENT, ICE_EXP_PAGE_TOK, ICE_EXP_PAGE_CNT, ICE_EXP_PAGE_NEXT,
  ICE_EXP_PAGE_OWNER, ICE_EXP_OWNER_FIRST, ICE_EXP_OWNER_TAIL, ICE_EXP_TOP, ICE_EXP_PAGE_K, ICE_EXP_PAGE_V,

@@ -58,10 +58,12 @@ class PinnedHost:
 
 
 def make_params(n_heads: int, group: int, d: int, dtype: str, capacity: int, levels: int = 3,
-                promote_log2: int = 4, seed: int = 0, host_pool: bool = False, resident: int = 0) -> IceParams:
+                promote_log2: int = 4, seed: int = 0, host_pool: bool = False, resident: int = 0,
+                resort: bool = False) -> IceParams:
+    flags = (_lib.ICE_HOST_POOL if host_pool else 0) | (_lib.ICE_SPLIT_RESORT if resort else 0)
     return IceParams(n_heads=n_heads, group=group, d=d, dtype=_DT[dtype][0], page_cap=_lib.ICE_PAGE_CAP,
                      levels=levels, promote_log2=promote_log2, capacity=capacity,
-                     flags=_lib.ICE_HOST_POOL if host_pool else 0, seed=seed, resident=resident)
+                     flags=flags, seed=seed, resident=resident)
 
 
 def ice_index_bytes(p: IceParams) -> int:
@@ -81,12 +83,13 @@ class IceIndex:
     gathers the union's pages over the host link first. ``resident`` reserves
     room for that many resident (sink and window) tokens per head, set with
     ``set_resident``; ``set_dense`` flags heads whose attention covers every
-    indexed token.
+    indexed token. ``resort=True`` makes inserts split by re-sorting the
+    owner's members over its pages (ICE_SPLIT_RESORT) instead of appending.
     """
 
     def __init__(self, n_heads: int, group: int, d: int, dtype: str, capacity: int, levels: int = 3,
                  promote_log2: int = 4, seed: int = 0, max_budget: int = 256, device="cuda",
-                 host_pool: bool = False, resident: int = 0):
+                 host_pool: bool = False, resident: int = 0, resort: bool = False):
         self.lib = _lib.load()
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
@@ -94,7 +97,8 @@ class IceIndex:
         self.device = dev
         self.dtype = dtype
         self.tdtype = _DT[dtype][1]
-        self.p = make_params(n_heads, group, d, dtype, capacity, levels, promote_log2, seed, host_pool, resident)
+        self.p = make_params(n_heads, group, d, dtype, capacity, levels, promote_log2, seed, host_pool, resident,
+                             resort)
         self.H, self.G, self.d, self.capacity, self.levels = n_heads, group, d, capacity, levels
         self.max_budget = max_budget
         nbytes = ice_index_bytes(self.p)

@@ -59,7 +59,9 @@ int check_params(const ice_params* p) {
   // at most 2^26 tokens per head keeps every page id below 2^27, the range a
   // page's selection key holds
   if (p->capacity < 1 || p->capacity > (1 << 26)) return fail(ICE_ERR_ARG, "capacity must be in [1, 2^26]");
-  if (p->flags & ~ICE_HOST_POOL) return fail(ICE_ERR_ARG, "unknown flags 0x%x", p->flags);
+  if (p->flags & ~(ICE_HOST_POOL | ICE_SPLIT_RESORT)) return fail(ICE_ERR_ARG, "unknown flags 0x%x", p->flags);
+  if ((p->flags & ICE_HOST_POOL) && (p->flags & ICE_SPLIT_RESORT))
+    return fail(ICE_ERR_ARG, "ICE_SPLIT_RESORT moves V rows: it needs the device V pool (no ICE_HOST_POOL)");
   if (p->resident < 0 || p->resident > ICE_MAX_RESIDENT)
     return fail(ICE_ERR_ARG, "resident must be in [0, %d]", ICE_MAX_RESIDENT);
   if (p->resident > 0 && (p->flags & ICE_HOST_POOL))
@@ -96,6 +98,7 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
   L->cap = p->capacity;
   L->ntab = std::max(1, p->levels - 1);
   L->seed = p->seed;
+  L->resort = (p->flags & ICE_SPLIT_RESORT) ? 1 : 0;
   L->elt = p->dtype == ICE_BF16 ? 2 : 4;
   // level counts over every position a head can ever hold
   L->ncap[0] = p->capacity;

@@ -45,6 +45,7 @@ struct DevLayout {
   int32_t res_pages;             // resident pages per head, after table 0's pcap[0] pages
   int32_t topcap;                // capacity of the top list
   int32_t elt;                   // bytes per element of K/V/Q
+  int32_t resort;                // nonzero: inserts split by re-sorting (ICE_SPLIT_RESORT)
   int64_t head_bytes;            // stride between heads
   int64_t off_hdr, off_lev, off_e;
   int64_t off_parent[ICE_MAX_LEVELS];

@@ -8,7 +8,10 @@
 // the token is its own parent; a parent search is a GEMV of the lifted key
 // against the current points of the next level (ties to the lower token id);
 // the token joins its owner's last page or, if that page is full, a newly
-// split page that becomes the owner's last page. Resident tokens never move.
+// split page that becomes the owner's last page. Placed tokens keep their
+// slots, unless the index was created with ICE_SPLIT_RESORT: then a split
+// also re-packs the owner's level-0 members over its pages in the build's
+// order (distance to the owner, then token id), the new page last.
 //
 // One block per head; the new tokens of a call are inserted one after the
 // other, so a token promoted by one insert is a candidate parent for the
@@ -139,6 +142,118 @@ struct BestTok {
 
 constexpr int kInsertWaves = 16;
 
+// LDS of the re-sort split: the owner's chain, its members in chain order,
+// their keys and destinations, and a staging area for the row moves.
+struct ResplitLds {
+  int32_t pages[ICE_RESPLIT_MAX / ICE_PAGE_CAP];
+  int32_t tok[ICE_RESPLIT_MAX];
+  int32_t dst[ICE_RESPLIT_MAX];
+  double key[ICE_RESPLIT_MAX];
+  int32_t opos, bad;
+  alignas(16) char stage[32768];
+};
+
+// Position r of the owner's chain -> row of the page pool.
+__device__ inline int64_t chain_row(const ResplitLds& R, int r) {
+  return (int64_t)R.pages[r / ICE_PAGE_CAP] * ICE_PAGE_CAP + r % ICE_PAGE_CAP;
+}
+
+// Re-packs the n members of `owner` (chain pages already in R.pages, n <=
+// ICE_RESPLIT_MAX, every page full but the last) in the order the build packs
+// them: the owner first, then ascending lifted squared distance to the owner
+// (fp64, from the stored rows and lift coordinates), ties by token id. Page
+// ids, counts and chains stay; the page table's token ids and the K and V
+// rows are permuted. Called by every thread of the block.
+template <int D, class T, int NT>
+__device__ void resplit_owner(const DevLayout& L, void* hb, int h, int owner, int n, ResplitLds& R) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = NT / 64;
+  constexpr int EPL = D / 64;              // row elements per lane
+  int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[0]);
+  T* K = at<T>(hb, L.off_pgK[0]);
+  T* V = reinterpret_cast<T*>(v_pages(L, hb, h));
+  const float* eall = at<float>(hb, L.off_e);
+  if (tid == 0) {
+    R.opos = n;
+    R.bad = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) {
+    const int t = pg_tok[chain_row(R, i)];
+    R.tok[i] = t;
+    if (t == owner) atomicMin(&R.opos, i);
+    if (t < 0 || t >= L.cap) atomicOr(&R.bad, 1);
+  }
+  __syncthreads();
+  const int opos = R.opos;
+  // the owner missing from its chain, or an empty slot among the members:
+  // not a layout the inserts build, so the pages are left as they are
+  if (opos >= n || R.bad) return;
+  // squared distance to the owner: one wave per member, lanes over the dims
+  float ko[EPL];
+  const int64_t orow = chain_row(R, opos) * D;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) ko[j] = Elt<T>::load(K, orow + lane + 64 * j);
+  const double eo = (double)eall[owner];
+  for (int i = wave; i < n; i += NW) {
+    const int64_t row = chain_row(R, i) * D;
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const double df = (double)Elt<T>::load(K, row + lane + 64 * j) - (double)ko[j];
+      acc += df * df;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (lane == 0) {
+      const double de = (double)eall[R.tok[i]] - eo;
+      double dk = acc + de * de;
+      if (!(dk >= 0.0)) dk = INFINITY;     // NaN rows sort last, so the order stays total
+      R.key[i] = i == opos ? -1.0 : dk;    // the owner leads its run
+    }
+  }
+  __syncthreads();
+  // destination = rank under (key, token): a strict total order, so the
+  // ranks are a permutation of 0..n-1
+  for (int i = tid; i < n; i += NT) {
+    const double ki = R.key[i];
+    const int ti = R.tok[i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const double kj = R.key[j];
+      rank += (kj < ki || (kj == ki && R.tok[j] < ti)) ? 1 : 0;
+    }
+    R.dst[i] = rank;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) pg_tok[chain_row(R, R.dst[i])] = R.tok[i];
+  // rows move through LDS, C dims of every member at a time
+  T* stg = reinterpret_cast<T*>(R.stage);
+  constexpr int E = (int)(sizeof(R.stage) / sizeof(T));
+  int C = D;
+  while (n * C > E) C >>= 1;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int c0 = 0; c0 < D; c0 += C) {
+      for (int x = tid; x < n * C; x += NT) {
+        const int i = x / C, c = x % C;
+        const int64_t r = chain_row(R, i);
+        const int64_t src = pass == 0 ? r * D + c0 + c
+                                      : ((r / ICE_PAGE_CAP * 4 + r % ICE_PAGE_CAP / 4) * D + c0 + c) * 4 + r % 4;
+        stg[R.dst[i] * C + c] = pass == 0 ? K[src] : V[src];
+      }
+      __syncthreads();
+      for (int x = tid; x < n * C; x += NT) {
+        const int i = x / C, c = x % C;
+        const int64_t r = chain_row(R, i);
+        const int64_t dst = pass == 0 ? r * D + c0 + c
+                                      : ((r / ICE_PAGE_CAP * 4 + r % ICE_PAGE_CAP / 4) * D + c0 + c) * 4 + r % 4;
+        (pass == 0 ? K : V)[dst] = stg[i * C + c];
+      }
+      __syncthreads();
+    }
+  }
+}
+
 template <int D, class T>
 __global__ __launch_bounds__(kInsertWaves * 64) void k_insert(DevLayout L, void* blob, const T* knew, const T* vnew,
                                                               int n_new, int t0) {
@@ -158,6 +273,8 @@ __global__ __launch_bounds__(kInsertWaves * 64) void k_insert(DevLayout L, void*
   __shared__ int red_t[NW];
   __shared__ Place plc;
   __shared__ float e_sh;
+  __shared__ int rs_owner, rs_n;
+  __shared__ ResplitLds rs;
 
   for (int j = 0; j < n_new; ++j) {
     const int t = t0 + j;
@@ -284,6 +401,27 @@ __global__ __launch_bounds__(kInsertWaves * 64) void k_insert(DevLayout L, void*
       eall[t] = et;
       if (!ok) hdr->overflow = 1;   // page table overflow (ruled out by the capacity bound)
       e_sh = et;
+      // re-sort split: a token owner whose chain just grew a page (the new
+      // token took slot 0 of a page that is not its first)
+      rs_n = 0;
+      rs_owner = owner0;
+      if (L.resort && owner0 != ICE_ROOT && plc.page[0] >= 0 && plc.slot[0] == 0) {
+        const int32_t* first0 = at<int32_t>(hb, L.off_first[0]);
+        const int32_t* orun0 = at<int32_t>(hb, L.off_orun[0]);
+        const int32_t* next0 = at<int32_t>(hb, L.off_pg_next[0]);
+        const int n_mem = at<int32_t>(hb, L.off_ocnt[0])[owner0];
+        const int n_pg = (n_mem + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP;
+        if (first0[owner0] != plc.page[0] && n_mem <= ICE_RESPLIT_MAX) {
+          // the chain: the contiguous run from first[], then the links
+          const int run = max(1, min(orun0[owner0], n_pg));
+          int pg = first0[owner0];
+          int k = 0;
+          for (; k < run; ++k) rs.pages[k] = pg + k;
+          pg = next0[pg + run - 1];
+          for (; k < n_pg && pg >= 0; ++k, pg = next0[pg]) rs.pages[k] = pg;
+          if (k == n_pg && rs.pages[n_pg - 1] == plc.page[0]) rs_n = n_mem;
+        }
+      }
     }
     __syncthreads();
     // a page created by this insert gets zero rows besides the new token, so
@@ -322,6 +460,11 @@ __global__ __launch_bounds__(kInsertWaves * 64) void k_insert(DevLayout L, void*
     }
     __threadfence_block();
     __syncthreads();
+    if (rs_n > 0) {
+      resplit_owner<D, T, NW * 64>(L, hb, h, rs_owner, rs_n, rs);
+      __threadfence_block();
+      __syncthreads();
+    }
   }
   if (tid == 0) hdr->n_tokens = t0 + n_new;
 }

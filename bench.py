@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-pipeline", action="store_true", help="skip the per-layer build pipeline measurement")
     ap.add_argument("--resident", type=int, default=68,
                     help="resident (sink + window) tokens per head for the resident-token leg; 0 skips it")
+    ap.add_argument("--drift-steps", type=int, default=4096,
+                    help="generated steps of the split-reading recall comparison (0 skips it)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="print a markdown summary of rocprofv3 output instead of benchmarking: one "
@@ -359,6 +361,65 @@ def time_reuse(ix, w, a, H, N, heads_per_layer=8):
             "index_keys_per_s_with_reuse": H * N / (reuse / 1000.0)}
 
 
+def split_drift(a):
+    """Long generation under both split readings, on the same inputs: one
+    Qwen3-32B-shaped layer (8 KV heads x 8 query heads, d=128 bf16, 512-centre
+    mixture keys with per-head rotations), an 8192-token prompt, then
+    ``a.drift_steps`` steps that each insert one key/value per head, queries
+    walking between mixture centres. Every 256 steps, the selection's token
+    recall at a 256-token budget: the share of each query head's exact
+    top-256 keys by q.k that lie in its selected pages (mean over the 64 query
+    heads). Also the mean time of one insert call (8 heads) per split reading."""
+    import torch
+    from ann_retrieval_amd import _lib as L
+    from ann_retrieval_amd import synth
+    from ann_retrieval_amd.api import IceIndex
+    H, G, N, d, budget, steps = 8, 8, 8192, 128, 256, a.drift_steps
+    w, gen = synth.clustered_kv(H, N, d, 512, "bf16", a.seed + 7, device="cpu", rotate=True)
+    walk = synth.QueryWalk(w, G, gen, seg=64)
+    seq = [walk.step() for _ in range(steps)]
+    Q = torch.stack([x[0] for x in seq]).cuda()
+    Kn = torch.stack([x[1] for x in seq]).cuda()
+    Vn = torch.stack([x[2] for x in seq]).cuda()
+    # every key, transposed once: [H, d, N + steps] fp32
+    KT = torch.cat([w.K.cuda(), Kn[:, :, 0].transpose(0, 1)], 1).float().transpose(1, 2).contiguous()
+    marks = sorted(set(range(0, steps, 256)) | {steps - 1})
+    out = {"workload": (f"one layer of 8 KV heads x 8 query heads, d=128 bf16, {N}-token prompt, {steps} steps "
+                        f"inserting one token per head; recall at a {budget}-token budget every 256 steps")}
+    for mode in ("append", "resort"):
+        ix = IceIndex(H, G, d, "bf16", N + steps, 3, 4, a.seed + 7, max_budget=budget, resort=mode == "resort")
+        ix.ice_build(w.K.cuda(), w.V.cuda())
+        torch.cuda.synchronize()
+        recall, ev = [], []
+        for s in range(steps):
+            if s in marks:
+                n = N + s
+                sel, _, _ = ix.ice_select(Q[s], budget, budget // 16)
+                top = torch.topk(torch.bmm(Q[s].float(), KT[:, :, :n]), budget, dim=-1).indices
+                hit = 0
+                for h in range(H):
+                    tok = torch.from_numpy(ix.export(h, L.ICE_EXP_PAGE_TOK, 0).reshape(-1, 16)).cuda()
+                    stok = tok[sel[h].long().clamp(min=0)].reshape(G, -1)
+                    stok = torch.where((sel[h] >= 0).repeat_interleave(16, dim=1), stok, -1)
+                    for g in range(G):
+                        hit += int(torch.isin(top[h, g], stok[g]).sum())
+                recall.append(hit / (H * G * budget))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ix.ice_insert(Kn[s], Vn[s])
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ins_us = 1000.0 * sum(x.elapsed_time(y) for x, y in ev) / steps
+        splits = sum(ix.stats(h)["splits"] for h in range(H))
+        out[mode] = {"recall": [round(r, 4) for r in recall], "recall_at_steps": marks, "insert_us": ins_us,
+                     "splits": splits}
+        print(f"[bench] {mode} split: recall {recall[0]:.4f} at step 0, {recall[-1]:.4f} at step {steps - 1}, "
+              f"mean {np.mean(recall):.4f}; insert {ins_us:.1f} us/step; {splits} splits", file=sys.stderr, flush=True)
+        del ix
+    return out
+
+
 def time_host_pool(w, Qs, a, H, G, N, d, dtype, budget, dev_attend_ms, n_ins):
     """Host-pool mode on the same workload: V pages in pinned host memory, each
     step gathers the union's V pages over the host link before attending.
@@ -645,6 +706,8 @@ def main():
         out["prefill_pipeline"] = pipeline
     if reuse is not None:
         out["index_reuse"] = reuse
+    if a.drift_steps > 0:
+        out["split_drift"] = split_drift(a)
     if not a.no_cpu:
         heads = list(range(min(a.cpu_heads, H)))
         t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(3)], a.budget, a.budget // 16,

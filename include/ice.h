@@ -64,7 +64,7 @@ typedef struct ice_params {
   int32_t  levels;        /* L in [1, ICE_MAX_LEVELS]: levels 0..L-1, bottom included      */
   int32_t  promote_log2;  /* promotion probability per level = 2^-promote_log2, in [1,16] */
   int32_t  capacity;      /* max tokens per head, build plus inserts, 1 .. 2^26          */
-  uint32_t flags;         /* 0 or ICE_HOST_POOL                                           */
+  uint32_t flags;         /* 0, ICE_HOST_POOL or ICE_SPLIT_RESORT                         */
   uint64_t seed;          /* seed of the promotion draws                                  */
   int32_t  resident;      /* resident tokens per head kept beside the index (sink and
                              recent window, see ice_set_resident), 0 .. ICE_MAX_RESIDENT;
@@ -81,6 +81,20 @@ typedef struct ice_params {
  * host link) and attends from there. Results equal the device-pool mode's
  * bit for bit. */
 #define ICE_HOST_POOL 1u
+
+/* Re-sort split (the notes' key design 2 leaves open how an overflowing node
+ * splits; this is the other reading, beside the default append split). When
+ * an insert finds its level-0 owner's last page full, the new page is still
+ * appended to the owner's chain, and then all the owner's members, the new
+ * token included, are re-packed over the owner's pages in chain order as the
+ * build packs them: the owner first, then ascending lifted squared distance
+ * to the owner (fp64 from the stored rows), ties by token id. Page ids,
+ * chains and counts are those of the append split; the tokens' pages and
+ * slots, and their K and V rows, move. The virtual root (no promoted token)
+ * and owners with more than ICE_RESPLIT_MAX members split by appending.
+ * Needs the device V pool (ICE_ERR_ARG with ICE_HOST_POOL). */
+#define ICE_SPLIT_RESORT 2u
+#define ICE_RESPLIT_MAX 1024
 
 typedef struct ice_index ice_index;   /* opaque host-side handle */
 
@@ -161,7 +175,8 @@ int ice_build_reuse(ice_index* idx, const void* K, const void* V, int32_t n_toke
  * the next positions: each draws its level (capped at the build's top level),
  * takes the nearest point of the next level as parent, and is appended to
  * its owner's last page, or to a newly split page if that one is full.
- * Resident tokens never move. ICE_ERR_CAPACITY if the count would exceed
+ * Tokens already placed keep their page and slot, except under
+ * ICE_SPLIT_RESORT (see there). ICE_ERR_CAPACITY if the count would exceed
  * capacity (nothing is inserted). */
 int ice_insert(ice_index* idx, const void* k_new, const void* v_new, int32_t n_new,
                void* ws, size_t ws_bytes, void* stream);

@@ -401,13 +401,34 @@ def build_head_reuse(K, V, src: HeadIndex, head: int) -> HeadIndex:
 # [reading] A new token t (next position) draws its level like any token,
 # capped at the build's top level L_top. Below its level it is its own
 # parent. At its level (if below the top) its parent is the nearest point of
-# the *current* next level. No resident token moves or re-parents. At level 0
+# the *current* next level. No token already placed re-parents. At level 0
 # it joins its owner's last page if that page has room; otherwise a new page
-# (next free id) is split off, becomes the owner's last page and takes t. A
-# promoted token opens its own first page. Upper-level child lists grow in
-# arrival order.
+# (next free id) is split off, becomes the owner's last page and takes t
+# (append split: placed tokens keep their slots). A promoted token opens its
+# own first page. Upper-level child lists grow in arrival order. The re-sort
+# split (``resplit``) is described at ``insert``; it touches level-0 pages
+# only, the one level whose page boundaries decide what is selected and
+# attended (upper levels are scored token by token).
 
-def insert(idx: HeadIndex, k, v, lev_override: int | None = None, parent_override: int | None = None):
+RESPLIT_MAX = 1024   # [reading] owners with more members keep the append split
+
+
+def insert(idx: HeadIndex, k, v, lev_override: int | None = None, parent_override: int | None = None,
+           resplit: bool = False):
+    """One new token (module notes above).
+
+    ``resplit`` selects the other reading of the notes' split of an
+    overflowing node [N key design 2]: when the owner's last page is full,
+    a new page is still appended to its chain, and then the owner's members,
+    the new token included, are re-sorted as the build packs them (lifted
+    distance to the owner, the owner itself at 0, ties by token id) and
+    re-cut into the owner's pages in chain order, so the new page ends up
+    holding the farthest member. Page ids, chains and counts are those of
+    the append split; only which member sits in which page and slot
+    changes. [reading] Only owners that are tokens (not the virtual root,
+    whose pages are token-order runs) with at most RESPLIT_MAX members
+    re-sort; the others split by appending.
+    """
     k = np.asarray(k, np.float64).reshape(-1)
     v = np.asarray(v, np.float64).reshape(-1)
     t = idx.n
@@ -466,6 +487,14 @@ def insert(idx: HeadIndex, k, v, lev_override: int | None = None, parent_overrid
             idx.pages.append([t])
             idx.page_owner.append(owner0)
             idx.splits += 1
+            members = [u for pg in idx.owner_pages[owner0] for u in idx.pages[pg]]
+            if resplit and owner0 != ROOT and len(members) <= RESPLIT_MAX:
+                # the build's packing key: D to the owner (0 for the owner
+                # itself), then token id
+                mem = np.asarray(members, dtype=np.int64)
+                mem = mem[np.lexsort((mem, idx.dist[0][mem]))]
+                for i, pg in enumerate(idx.owner_pages[owner0]):
+                    idx.pages[pg] = [int(u) for u in mem[i * idx.page_cap:(i + 1) * idx.page_cap]]
     for l in range(1, idx.L_top):
         if lam > l:
             idx.children[l][t] = [t]

@@ -315,7 +315,7 @@ def compare_decode(ix, refs, out, resident=None, dense=()):
     return ties, worst
 
 
-def replay_inserts(ref, g, k, v, h, seed, levels, plog2):
+def replay_inserts(ref, g, k, v, h, seed, levels, plog2, resplit=False):
     """Applies inserted tokens (rows of k, v) to the oracle index `ref`,
     accepting the GPU's parent choice (from the GPU head `g`) only inside the
     near-tie band of the oracle's nearest point at that moment."""
@@ -332,6 +332,6 @@ def replay_inserts(ref, g, k, v, h, seed, levels, plog2):
                 dg = float(((ic.lifted(ref.K[gp:gp + 1], ref.e[gp:gp + 1])[0] - x) ** 2).sum())
                 assert dg - D1[0] <= BAND * dg, f"insert parent of {t} outside the band"
                 override = gp
-        ic.insert(ref, to64(k[j]), to64(v[j]), parent_override=override)
+        ic.insert(ref, to64(k[j]), to64(v[j]), parent_override=override, resplit=resplit)
 
 

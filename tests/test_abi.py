@@ -3,6 +3,7 @@ function ``include/ice.h`` declares, sizes its blobs from the promotion draws,
 and rejects bad arguments before enqueuing anything.
 """
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -22,6 +23,16 @@ def test_every_declared_function_is_exported(lib):
     assert {"ice_build", "ice_insert", "ice_select", "ice_attend"} <= set(names)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
+
+
+def test_binding_constants_match_the_header():
+    import re
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ice.h")).read()
+    defs = dict(re.findall(r"^#define (ICE_[A-Z0-9_]+)\s+\(?(-?\d+)u?\)?", text, flags=re.M))
+    shared = [n for n in defs if hasattr(L, n)]
+    assert {"ICE_HOST_POOL", "ICE_SPLIT_RESORT", "ICE_RESPLIT_MAX", "ICE_PAGE_CAP"} <= set(shared)
+    for n in shared:
+        assert getattr(L, n) == int(defs[n]), n
 
 
 def test_binding_declares_every_function():
@@ -70,10 +81,16 @@ def test_invalid_params_give_zero_sizes(lib):
     assert b"page_cap" in lib.ice_last_error()
     # resident tokens: bounded, and only with the device V pool
     for kw in [dict(resident=-1), dict(resident=L.ICE_MAX_RESIDENT + 1), dict(resident=16, host_pool=True),
-               dict(capacity=(1 << 26) + 1)]:
+               dict(capacity=(1 << 26) + 1), dict(resort=True, host_pool=True)]:
         base = dict(n_heads=2, group=4, d=128, dtype="bf16", capacity=100)
         base.update(kw)
         assert lib.ice_index_bytes(ctypes.byref(make_params(**base))) == 0
+    # the re-sort split is a flag of its own; unknown flag bits are refused
+    n0 = lib.ice_index_bytes(ctypes.byref(make_params(2, 4, 128, "bf16", 100)))
+    assert lib.ice_index_bytes(ctypes.byref(make_params(2, 4, 128, "bf16", 100, resort=True))) == n0
+    p = make_params(2, 4, 128, "bf16", 100)
+    p.flags = 4
+    assert lib.ice_index_bytes(ctypes.byref(p)) == 0 and b"flags" in lib.ice_last_error()
     # resident pages add to the blob: 100 tokens -> 7 pages of K and V per head
     n0 = lib.ice_index_bytes(ctypes.byref(make_params(2, 4, 128, "bf16", 100)))
     n1 = lib.ice_index_bytes(ctypes.byref(make_params(2, 4, 128, "bf16", 100, resident=100)))

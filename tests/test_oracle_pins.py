@@ -317,6 +317,89 @@ def test_insert_into_empty_index_and_clamp():
 
 
 # --------------------------------------------------------------------------
+# insert with the re-sort split
+# --------------------------------------------------------------------------
+
+def check_resplit_golden():
+    """Runs the hand-worked re-sort case in both split modes; True when every
+    checkpoint's pages are the hand-worked ones."""
+    c = _golden("resplit_case.json")
+    ok = True
+    for mode in ("resplit", "append"):
+        K = np.array(c["keys"])
+        nb = len(c["build_levels"])
+        idx = ic.build_head(K[:nb], np.zeros((nb, 2)), 0, 0, lev=np.array(c["build_levels"]))
+        for t in c["inserts"]:
+            ic.insert(idx, K[t], np.zeros(2), lev_override=0, resplit=mode == "resplit")
+            want = c["after"].get(str(t))
+            if want is not None:
+                ok &= idx.pages == want[mode]
+        ok &= idx.splits == c["splits"] and idx.owner_pages[0] == [0, 1, 2]
+    return bool(ok)
+
+
+def test_resplit_hand_case():
+    assert check_resplit_golden()
+
+
+def _chain_sequences(idx):
+    return {o: [t for p in ps for t in idx.pages[p]] for o, ps in idx.owner_pages.items()}
+
+
+@pytest.mark.parametrize("seed", [6, 7])
+def test_resplit_is_a_sorted_prefix_of_the_append_order(seed):
+    """Closed form against the append split on the same inputs: same page
+    ids, owners, chains and counts; per owner, the members present at its
+    last split (the first 16*(pages-1)+1 of the append order) appear sorted
+    by (distance to the owner, token id), then the later arrivals in arrival
+    order. An owner whose pages never split since the build has a sorted
+    prefix already (the build packs that way), so the form holds for it too."""
+    K, V, cent = _clustered(1200, 8, 12, seed)
+    a = ic.build_head(K, V, 1, seed)
+    b = ic.build_head(K, V, 1, seed)
+    r = _rng(seed + 100)
+    for _ in range(900):
+        m = r.integers(0, len(cent))
+        k = cent[m] + 0.3 * r.standard_normal(8)
+        v = r.standard_normal(8)
+        ra = ic.insert(a, k, v)
+        rb = ic.insert(b, k, v, resplit=True)
+        assert ra == rb
+    assert a.splits == b.splits > 20
+    assert a.page_owner == b.page_owner and a.owner_pages == b.owner_pages
+    assert [len(p) for p in a.pages] == [len(p) for p in b.pages]
+    sa, sb = _chain_sequences(a), _chain_sequences(b)
+    n_sorted = 0
+    for o, seq in sa.items():
+        s = 16 * (len(a.owner_pages[o]) - 1) + 1
+        head = sorted(seq[:s], key=lambda t: (float(np.sum((b.X()[t] - b.X()[o]) ** 2)), t))
+        assert sb[o] == head + seq[s:], f"owner {o}"
+        n_sorted += head != seq[:s]
+    assert n_sorted > 5
+
+
+def test_resplit_limits_keep_the_append_split(monkeypatch):
+    """The virtual root never re-sorts (its pages are token-order runs), and
+    an owner over RESPLIT_MAX members splits by appending."""
+    r = _rng(8)
+    K = r.standard_normal((40, 4))
+    a = ic.build_head(K, K, 0, 0, lev=np.zeros(40, dtype=np.int64))
+    for i in range(30):
+        ic.insert(a, r.standard_normal(4), np.zeros(4), lev_override=0, resplit=True)
+    assert a.pages == [list(range(s, min(s + 16, 70))) for s in range(0, 70, 16)]
+    c = _golden("resplit_case.json")
+    Kc = np.array(c["keys"])
+    monkeypatch.setattr(ic, "RESPLIT_MAX", 16)
+    idx = ic.build_head(Kc[:16], np.zeros((16, 2)), 0, 0, lev=np.array(c["build_levels"]))
+    ic.insert(idx, Kc[16], np.zeros(2), lev_override=0, resplit=True)
+    assert idx.pages == c["after"]["16"]["append"]
+    monkeypatch.setattr(ic, "RESPLIT_MAX", 17)
+    idx = ic.build_head(Kc[:16], np.zeros((16, 2)), 0, 0, lev=np.array(c["build_levels"]))
+    ic.insert(idx, Kc[16], np.zeros(2), lev_override=0, resplit=True)
+    assert idx.pages == c["after"]["16"]["resplit"]
+
+
+# --------------------------------------------------------------------------
 # select and union
 # --------------------------------------------------------------------------
 
@@ -549,6 +632,22 @@ def test_planted_attention_scale_dropped_is_caught(monkeypatch):
         return orig(idx, q, pages, 1.0)
     monkeypatch.setattr(ic, "attend", bad_attend)
     assert not check_attention_golden()
+
+
+def test_planted_resplit_sorted_descending_is_caught(monkeypatch):
+    class FakeNp:
+        def __getattr__(self, name):
+            return getattr(np, name)
+
+        @staticmethod
+        def lexsort(keys, *a, **k):
+            return np.lexsort(keys, *a, **k)[::-1]
+    monkeypatch.setattr(ic, "np", FakeNp())
+    try:
+        assert not check_resplit_golden()
+    finally:
+        monkeypatch.setattr(ic, "np", np)
+    assert check_resplit_golden()
 
 
 _orig_lift = ic.lift
