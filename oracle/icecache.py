@@ -200,8 +200,11 @@ def is_near_tie(D1, D2) -> np.ndarray:
         return np.isfinite(D2) & ((D2 - D1) < NEAR_TIE_REL * D2)
 
 
-def assign_parents(X: np.ndarray, lev: np.ndarray, L_top: int):
+def assign_parents(X: np.ndarray, lev: np.ndarray, L_top: int, pdci=None):
     """Parent of every point at every level below the top.
+
+    ``pdci`` (an ``oracle.pdci.Pdci``) replaces the exact nearest point by the
+    one P-DCI finds; its keys use the lift coordinate rounded to fp32.
 
     Returns lists indexed by level l = 0 .. L_top-1 of arrays over tokens:
     ``parent[l][t]`` (token id of the level-(l+1) owner, -1 if t is not a
@@ -218,7 +221,15 @@ def assign_parents(X: np.ndarray, lev: np.ndarray, L_top: int):
         child = np.nonzero(lev == l)[0]
         par[cand] = cand            # a point of level l+1 is its own parent
         dst[cand] = 0.0
-        if child.size:
+        if child.size and pdci is not None:
+            from oracle import pdci as _pdci
+            X32 = X.copy()
+            X32[:, -1] = X32[:, -1].astype(np.float32)
+            j, D1, D2 = _pdci.nearest_pdci(X[child], X32[child], X[cand], X32[cand], pdci)
+            par[child] = cand[j]
+            dst[child] = D1
+            sec[child] = D2
+        elif child.size:
             j, D1, D2 = nearest(X[child], X[cand])
             par[child] = cand[j]
             dst[child] = D1
@@ -317,13 +328,14 @@ def pack(lev: np.ndarray, L_top: int, parent: list, dist: list, page_cap: int):
 
 
 def build_head(K, V, head: int, seed: int, levels: int = 3, promote_log2: int = 4,
-               page_cap: int = 16, lev: np.ndarray | None = None, parents=None) -> HeadIndex:
+               page_cap: int = 16, lev: np.ndarray | None = None, parents=None, pdci=None) -> HeadIndex:
     """Index of one head from its prefill keys and values [N "Overall framework" step 1].
 
     ``lev`` overrides the promotion draws and ``parents`` the nearest-parent
     search (hand-worked cases; tie-tolerant replay of another implementation's
     choices). ``parents`` is a list over levels of arrays giving, for every
-    level-l point that is not itself at level l+1, its owner token.
+    level-l point that is not itself at level l+1, its owner token. ``pdci``
+    (an ``oracle.pdci.Pdci``) finds parents by P-DCI instead of exactly.
     """
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -335,7 +347,7 @@ def build_head(K, V, head: int, seed: int, levels: int = 3, promote_log2: int = 
     L_top = int(lev.max()) if n else 0
     X = lifted(K, e)
     if parents is None:
-        parent, dist, second = assign_parents(X, lev, L_top)
+        parent, dist, second = assign_parents(X, lev, L_top, pdci)
     else:
         parent, dist, second = [], [], []
         for l in range(L_top):

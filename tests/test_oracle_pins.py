@@ -400,6 +400,79 @@ def test_resplit_limits_keep_the_append_split(monkeypatch):
 
 
 # --------------------------------------------------------------------------
+# P-DCI parents
+# --------------------------------------------------------------------------
+
+from oracle import pdci as pd  # noqa: E402
+
+
+def _dirs(r, rows, d):
+    u = r.standard_normal((rows, d))
+    return (u / np.linalg.norm(u, axis=1, keepdims=True)).astype(np.float32).astype(np.float64)
+
+
+def test_pdci_hand_case_projection_misleads():
+    """Keys A=(0.1, 2), B=(0.5, 0) at level 1, C=(0, 0) at level 0; M^2 =
+    |A|^2 = 4.01, so e_A = 0, e_B = sqrt(3.76), e_C = sqrt(4.01). Lifted
+    D(C,A) = 0.01 + 4 + 4.01 = 8.02 and D(C,B) = 0.25 + (2.00250 - 1.93907)^2
+    = 0.2540, so B is the exact parent. One simple index projecting on the
+    first key coordinate puts A (|0.1 - 0| = 0.1) before B (0.5): with one
+    visit P-DCI returns A, with two it ranks both and returns B."""
+    K = np.array([[0.1, 2.0], [0.5, 0.0], [0.0, 0.0]])
+    lev = np.array([1, 1, 0])
+    dirs = np.array([[1.0, 0.0, 0.0]])
+    ex = ic.build_head(K, K, 0, 0, levels=2, lev=lev)
+    assert ex.parent[0][2] == 1 and abs(ex.dist[0][2] - 0.2540) < 1e-4
+    one = ic.build_head(K, K, 0, 0, levels=2, lev=lev, pdci=pd.Pdci(dirs, 1, 1, 1, 1))
+    assert one.parent[0][2] == 0 and abs(one.dist[0][2] - 8.02) < 1e-9
+    two = ic.build_head(K, K, 0, 0, levels=2, lev=lev, pdci=pd.Pdci(dirs, 1, 1, 2, 2))
+    assert two.parent[0][2] == 1 and np.isfinite(two.second[0][2])
+
+
+def test_pdci_with_unbounded_budgets_is_the_exact_search():
+    K, V, _ = _clustered(700, 6, 8, 12)
+    r = _rng(13)
+    n = 700
+    cfg = pd.Pdci(_dirs(r, 4, 7), m=2, l=2, visits=2 * n, cands=n)
+    a = ic.build_head(K, V, 0, 12, pdci=cfg)
+    b = ic.build_head(K, V, 0, 12)
+    for l in range(b.L_top):
+        assert np.array_equal(a.parent[l], b.parent[l])
+    assert a.pages == b.pages
+
+
+def _visit_rank_candidates(qkey, keys, cfg):
+    """Closed form of one query's candidates: every (point, simple index) pair
+    is visited in ascending (|key - query key|, simple index, point) order, so
+    a point completes at the largest visit rank of its l pairs; a composite
+    index keeps the points completing within its visit budget (at least the
+    first), in completion order, at most cands."""
+    n = keys.shape[0]
+    out = []
+    for j in range(cfg.m):
+        cols = range(j * cfg.l, (j + 1) * cfg.l)
+        pairs = sorted((abs(keys[c, col] - qkey[col]), i, c) for i, col in enumerate(cols) for c in range(n))
+        rank = {}
+        for r_, (_, i, c) in enumerate(pairs):
+            rank[(c, i)] = r_
+        done = sorted((max(rank[(c, i)] for i in range(cfg.l)), c) for c in range(n))
+        keep = [c for rk, c in done if rk < cfg.visits] or [done[0][1]]
+        out.extend(keep[:cfg.cands])
+    return out
+
+
+@pytest.mark.parametrize("m,l,visits,cands", [(1, 1, 5, 3), (1, 2, 40, 6), (2, 2, 25, 4), (3, 3, 90, 8),
+                                              (1, 3, 3, 5)])
+def test_pdci_candidates_follow_the_visit_order(m, l, visits, cands):
+    r = _rng(20 + m + l)
+    keys = r.standard_normal((60, m * l))
+    for _ in range(20):
+        q = r.standard_normal(m * l)
+        cfg = pd.Pdci(np.zeros((m * l, 1)), m, l, visits, cands)
+        assert pd.candidates(q, keys, cfg) == _visit_rank_candidates(q, keys, cfg)
+
+
+# --------------------------------------------------------------------------
 # select and union
 # --------------------------------------------------------------------------
 
