@@ -19,6 +19,7 @@ c_size, c_void_p, c_char_p = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
 ICE_OK, ICE_ERR_ARG, ICE_ERR_DTYPE, ICE_ERR_STATE, ICE_ERR_CAPACITY, ICE_ERR_HIP = 0, -1, -2, -3, -4, -5
 ICE_F32, ICE_BF16 = 0, 1
 ICE_HOST_POOL, ICE_SPLIT_RESORT, ICE_RESPLIT_MAX = 1, 2, 1024
+ICE_PDCI_MAX_KEYS, ICE_PDCI_MAX_L = 16, 4
 ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM, ICE_MAX_RESIDENT = 16, 4, 16, 256, 4096
 (ICE_EXP_LEVEL, ICE_EXP_LIFT, ICE_EXP_PARENT, ICE_EXP_PAGE_TOK, ICE_EXP_PAGE_CNT, ICE_EXP_PAGE_NEXT,
  ICE_EXP_PAGE_OWNER, ICE_EXP_OWNER_FIRST, ICE_EXP_OWNER_TAIL, ICE_EXP_TOP, ICE_EXP_PAGE_K, ICE_EXP_PAGE_V,
@@ -45,6 +46,8 @@ _SIGNATURES = {
     "ice_host_pool_bytes": (c_size, [ctypes.POINTER(IceParams)]),
     "ice_attach_host_pool": (ctypes.c_int, [c_void_p, c_void_p, c_size]),
     "ice_build": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p, c_size, c_void_p]),
+    "ice_build_pdci": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p, c_i32, c_i32, c_i32, c_i32,
+                                      c_void_p, c_size, c_void_p]),
     "ice_build_heads": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_i32, c_i32, c_void_p, c_size,
                                        c_void_p]),
     "ice_build_reuse": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_i32, c_i32, c_i32, c_void_p,

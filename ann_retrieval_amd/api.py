@@ -143,6 +143,22 @@ class IceIndex:
         check(self.lib.ice_build(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0), _ptr(self.ws),
                                  self.ws_bytes, _stream_ptr(self.device)), "ice_build")
 
+    def ice_build_pdci(self, K: torch.Tensor, V: torch.Tensor, dirs: torch.Tensor, m: int, l: int, visits: int,
+                       cands: int) -> None:
+        """ice_build with parents found by P-DCI: dirs is a float32 [m*l, d+1] device tensor of projection
+        directions; m composite indices of l simple indices, `visits` visits and `cands` candidates per
+        composite index."""
+        self._check_kv(K, "K")
+        self._check_kv(V, "V")
+        if K.shape != V.shape or K.stride() != V.stride():
+            raise ValueError("K and V must have the same shape and strides")
+        if dirs.device != self.device or dirs.dtype != torch.float32 or tuple(dirs.shape) != (m * l, self.d + 1) \
+                or not dirs.is_contiguous():
+            raise ValueError(f"dirs must be a contiguous float32 [{m * l}, {self.d + 1}] tensor on {self.device}")
+        check(self.lib.ice_build_pdci(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0), _ptr(dirs), m, l,
+                                      visits, cands, _ptr(self.ws), self.ws_bytes, _stream_ptr(self.device)),
+              "ice_build_pdci")
+
     def ice_build_heads(self, K: torch.Tensor, V: torch.Tensor, h0: int, stream=None) -> None:
         """Builds heads h0 .. h0 + K.shape[0] - 1 from their rows K, V [n_heads, n, d], on `stream`
         (a torch.cuda.Stream; the current stream if None)."""

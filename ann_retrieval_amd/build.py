@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libice.so")
-SOURCES = ["ice_api.hip", "k_build.hip", "k_gemm.hip", "k_insert.hip", "k_select.hip", "k_attend.hip"]
+SOURCES = ["ice_api.hip", "k_build.hip", "k_gemm.hip", "k_pdci.hip", "k_insert.hip", "k_select.hip", "k_attend.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -171,6 +171,7 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
   W->off_bown = w.take(cap * 4);
   W->head_bytes = w.off;
   W->build_bytes = W->head_bytes * p->n_heads;
+  W->pdci_bytes = align256((int64_t)p->n_heads * ICE_PDCI_MAX_KEYS * n1 * 24);
 }
 
 int64_t attend_part_bytes(const DevLayout& L, int uni_stride) {
@@ -229,7 +230,7 @@ size_t ice_workspace_bytes(const ice_params* p, int32_t max_budget_tokens) {
   WsLayout W;
   make_layout(p, &L, &W);
   const int64_t att = attend_ws_bytes(L, p->group * (max_budget_tokens / ICE_PAGE_CAP));
-  return (size_t)std::max<int64_t>(W.build_bytes, att);
+  return (size_t)std::max<int64_t>(W.build_bytes + W.pdci_bytes, att);
 }
 
 size_t ice_host_pool_bytes(const ice_params* p) {
@@ -294,8 +295,12 @@ int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes
 
 int32_t ice_n_tokens(const ice_index* idx) { return idx ? idx->n_tokens : -1; }
 
-int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, int32_t h0,
-                    int32_t n_heads, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int build_range(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, int32_t h0,
+                int32_t n_heads, void* ws, size_t ws_bytes, void* stream, const PdciArgs* pd) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");
   const int H = idx->p.n_heads;
   if (h0 < 0 || n_heads < 1 || h0 > H - n_heads)
@@ -328,7 +333,7 @@ int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_toke
   char* blob = static_cast<char*>(idx->blob) + (int64_t)h0 * L.head_bytes;
   char* wsr = static_cast<char*>(ws) + (int64_t)h0 * idx->W.head_bytes;
   hipError_t e = launch_build(L, idx->W, blob, K, V, n_tokens, head_stride, wsr, range_built,
-                              static_cast<hipStream_t>(stream));
+                              static_cast<hipStream_t>(stream), pd);
   if (e != hipSuccess) return hip_fail(e, "ice_build launch");
   if (!range_built)     // headers were cleared: no dense flags there any more
     for (int h = h0; h < h0 + n_heads; ++h) {
@@ -341,6 +346,44 @@ int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_toke
   for (int h = 0; h < H; ++h) all &= idx->head_built[h] != 0;
   idx->built = all;
   return ICE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, int32_t h0,
+                    int32_t n_heads, void* ws, size_t ws_bytes, void* stream) {
+  return build_range(idx, K, V, n_tokens, head_stride, h0, n_heads, ws, ws_bytes, stream, nullptr);
+}
+
+int ice_build_pdci(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
+                   const float* dirs, int32_t m, int32_t l, int32_t visits, int32_t cands, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (l < 1 || l > ICE_PDCI_MAX_L || m < 1 || m * l > ICE_PDCI_MAX_KEYS)
+    return fail(ICE_ERR_ARG, "P-DCI needs 1 <= l <= %d and 1 <= m, m*l <= %d", ICE_PDCI_MAX_L, ICE_PDCI_MAX_KEYS);
+  if (visits < 1 || cands < 1) return fail(ICE_ERR_ARG, "visits and cands must be >= 1");
+  if (!dirs) return fail(ICE_ERR_ARG, "dirs is null");
+  const WsLayout& W = idx->W;
+  if (!ws || ws_bytes < (size_t)(W.build_bytes + W.pdci_bytes))
+    return fail(ICE_ERR_CAPACITY, "workspace has %zu bytes, a P-DCI build needs %lld", ws_bytes,
+                (long long)(W.build_bytes + W.pdci_bytes));
+  PdciArgs P;
+  P.dirs = dirs;
+  P.m = m;
+  P.l = l;
+  P.mk = m * l;
+  P.visits = visits;
+  P.cands = cands;
+  P.stride = idx->p.levels >= 2 ? idx->L.ncap[1] : 0;
+  const int64_t n_el = (int64_t)idx->p.n_heads * ICE_PDCI_MAX_KEYS * P.stride;
+  char* base = static_cast<char*>(ws) + W.build_bytes;
+  P.keys = reinterpret_cast<double*>(base);
+  P.skeys = reinterpret_cast<double*>(base + n_el * 8);
+  P.sidx = reinterpret_cast<int32_t*>(base + n_el * 16);
+  P.posof = reinterpret_cast<int32_t*>(base + n_el * 20);
+  return build_range(idx, K, V, n_tokens, head_stride, 0, idx->p.n_heads, ws, ws_bytes, stream, &P);
 }
 
 int ice_build_reuse(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, int32_t h0,

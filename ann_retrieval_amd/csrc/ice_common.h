@@ -97,6 +97,22 @@ struct WsLayout {
   int64_t attend_bytes;          // partials of split attention
   int32_t nsplit;                // attention splits per head for the max budget
   int32_t max_pages;             // max union size G*k for the max budget
+  // P-DCI parent search (ice_build_pdci): a region after the per-head
+  // build workspace holding, per head and simple index, ncap[1] keys by
+  // candidate, the sorted keys, the sorted candidates and their positions
+  int64_t pdci_bytes;
+};
+
+// P-DCI parameters and arrays of one build; element (h, k, c) of each array
+// sits at (h * ICE_PDCI_MAX_KEYS + k) * stride + c.
+struct PdciArgs {
+  const float* dirs;             // [mk][d+1] directions, simple index k of composite j is row j*l + k
+  int32_t m, l, mk, visits, cands;
+  int32_t stride;                // ncap[1]
+  double* keys;                  // keys by candidate
+  double* skeys;                 // keys in ascending (key, candidate) order
+  int32_t* sidx;                 // candidates in that order
+  int32_t* posof;                // position of each candidate in that order
 };
 
 template <class T>

@@ -11,10 +11,15 @@ namespace ice {
 hipError_t launch_build_reuse(const DevLayout& L, const WsLayout& W, void* blob, const void* src, const void* K,
                               const void* V, int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s);
 // keep: a rebuild, which keeps the headers' resident counts and dense flags
+// pd: parents by P-DCI instead of the exact search (nullptr: exact)
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
-                        int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s);
+                        int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s,
+                        const PdciArgs* pd = nullptr);
 // k_gemm.hip: nearest parent of every level-`level` point among the level-(level+1) points
 hipError_t launch_parent_gemm(const DevLayout& L, const WsLayout& W, void* blob, const void* K,
+                              int64_t head_stride, void* ws, int level, hipStream_t s);
+// k_pdci.hip: parent of every level-`level` point by P-DCI among the level-(level+1) points
+hipError_t launch_parent_pdci(const DevLayout& L, const WsLayout& W, const PdciArgs& P, void* blob, const void* K,
                               int64_t head_stride, void* ws, int level, hipStream_t s);
 // k_insert.hip
 hipError_t launch_insert(const DevLayout& L, void* blob, const void* k_new, const void* v_new, int n_new,

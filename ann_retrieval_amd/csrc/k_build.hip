@@ -455,7 +455,7 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 
 template <int D, class T>
 hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const void* Kv, const void* Vv,
-                       int n, int64_t hstride, void* ws, bool keep, hipStream_t s) {
+                       int n, int64_t hstride, void* ws, bool keep, hipStream_t s, const PdciArgs* pd) {
   const T* K = static_cast<const T*>(Kv);
   const T* V = static_cast<const T*>(Vv);
   const unsigned H = (unsigned)L.H;
@@ -491,10 +491,14 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
   for (int level = 0; level <= last; ++level) {
     const int npts = L.ncap[level];
     if (L.L >= 2 && n > 0) {
-      k_gather_opA<D, T><<<dim3(blocks_for((int64_t)L.ncap[level + 1] * W.kp, 256 * 8), H), 256, 0, s>>>(
-          L, W, blob, K, hstride, ws, level);
-      ICE_CHECK();
-      if ((err = launch_parent_gemm(L, W, blob, Kv, hstride, ws, level, s))) return err;
+      if (pd) {
+        if ((err = launch_parent_pdci(L, W, *pd, blob, Kv, hstride, ws, level, s))) return err;
+      } else {
+        k_gather_opA<D, T><<<dim3(blocks_for((int64_t)L.ncap[level + 1] * W.kp, 256 * 8), H), 256, 0, s>>>(
+            L, W, blob, K, hstride, ws, level);
+        ICE_CHECK();
+        if ((err = launch_parent_gemm(L, W, blob, Kv, hstride, ws, level, s))) return err;
+      }
     }
     const int nown = (L.L >= 2 ? L.ncap[level + 1] : 0) + 1;
     if ((err = launch_fill_heads(ws, W.head_bytes, L.H, W.off_cnt, nown, 0, s))) return err;
@@ -621,13 +625,13 @@ hipError_t launch_build_reuse(const DevLayout& L, const WsLayout& W, void* blob,
 }
 
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
-                        int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s) {
+                        int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s, const PdciArgs* pd) {
   if (L.dtype == ICE_BF16) {
-    if (L.d == 128) return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s);
-    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s);
+    if (L.d == 128) return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd);
+    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd);
   }
-  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s);
-  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s);
+  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd);
+  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd);
 }
 
 }  // namespace ice

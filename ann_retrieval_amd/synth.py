@@ -161,6 +161,14 @@ def resident_tokens(w: Workload, n: int, gen: torch.Generator, device="cpu") -> 
     return to_dtype(k, w.dtype), to_dtype(v, w.dtype)
 
 
+def projection_dirs(rows: int, d: int, seed: int, device="cpu") -> torch.Tensor:
+    """``rows`` random unit directions over lifted keys [k, e] (d + 1 wide),
+    float32 [rows, d + 1], seeded: the projections of P-DCI's simple indices."""
+    gen = torch.Generator().manual_seed(seed)
+    u = torch.randn(rows, d + 1, generator=gen, dtype=torch.float64)
+    return (u / u.norm(dim=1, keepdim=True)).float().to(device)
+
+
 def needle_workload(n_heads: int, group: int, n_tokens: int, d: int, n_centres: int, depth: float,
                     seed: int, dtype: str = "bf16", device="cpu", span: int = 16,
                     cosine: float = 0.9):

@@ -141,6 +141,28 @@ int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes
 int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
               void* ws, size_t ws_bytes, void* stream);
 
+/* ice_build with parents found by Prioritized DCI instead of the exact
+ * search (the notes' key design 2: M-DCI sits on P-DCI; the article's
+ * section 3 names it as the prior work; composite and simple indices as in
+ * Li and Malik, ICML 2017). dirs: device fp32 [m*l][d+1] projection
+ * directions over lifted keys [k, e], shared by every head and level; simple
+ * index i of composite index j uses row j*l + i. Per child point and
+ * composite index, the l simple indices are walked outward from the child's
+ * key in their sorted order, always visiting the walker front with the
+ * smallest |key - child key| (ties: simple index, then candidate); a
+ * candidate is complete once all l have visited it; the walk ends after
+ * `visits` visits (once it has a candidate) or `cands` complete candidates.
+ * The complete candidates of all composite indices are ranked by lifted
+ * inner product (ties to the lower token id). Keys are fp64 from the stored
+ * rows and fp32 lift coordinate. 1 <= l <= ICE_PDCI_MAX_L, m >= 1,
+ * m*l <= ICE_PDCI_MAX_KEYS, visits >= 1, cands >= 1. The workspace of
+ * ice_workspace_bytes covers it. Everything else is as in ice_build. */
+#define ICE_PDCI_MAX_KEYS 16
+#define ICE_PDCI_MAX_L 4
+int ice_build_pdci(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
+                   const float* dirs, int32_t m, int32_t l, int32_t visits, int32_t cands, void* ws, size_t ws_bytes,
+                   void* stream);
+
 /* Build of heads h0 .. h0+n_heads-1 only, as ice_build does it for every
  * head (the aitangshan.cn article, section 4, and the notes' key design 4:
  * the index of one layer is built while the model works on the next). K, V:

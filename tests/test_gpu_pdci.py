@@ -1,0 +1,89 @@
+"""Builds with P-DCI parents (ice_build_pdci), GPU against the oracle's build
+with the same directions and budgets through the C ABI: levels exact, P-DCI
+parents exact up to near-equal distances among the same candidates, layout
+and pools exact after replay, then selection and attention. With budgets
+that cover every candidate the result is the exact search's. Every case
+prints its name and shape before it touches the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_support as gs
+from ann_retrieval_amd import _lib as L
+from ann_retrieval_amd import synth
+from ann_retrieval_amd.api import IceIndex
+from oracle import icecache as ic
+from oracle import pdci as pd
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_support import say  # noqa: E402
+
+
+def _pdci_case(H, N, d, dtype, C, seed, m, l, visits, cands, levels=3, plog2=4, G=2, budget=64):
+    say(f"pdci build H={H} N={N} d={d} {dtype} m={m} l={l} visits={visits} cands={cands} L={levels} p=2^-{plog2}")
+    w, gen = synth.clustered_kv(H, N, d, C, dtype, seed, device="cpu")
+    dirs = synth.projection_dirs(m * l, d, seed + 1)
+    ix = IceIndex(H, G, d, dtype, N, levels, plog2, seed, max_budget=budget)
+    ix.ice_build_pdci(w.K.cuda(), w.V.cuda(), dirs.cuda(), m, l, visits, cands)
+    torch.cuda.synchronize()
+    cfg = pd.Pdci(dirs.double().numpy(), m, l, visits, cands)
+    refs, ties, differs = {}, 0, 0
+    for h in range(H):
+        g = gs.read_head(ix, h)
+        K64, V64 = gs.to64(w.K[h]), gs.to64(w.V[h])
+        ref = ic.build_head(K64, V64, h, seed, levels, plog2, pdci=cfg)
+        exact = ic.build_head(K64, V64, h, seed, levels, plog2)
+        differs += sum(int(np.sum(ref.parent[lv] != exact.parent[lv])) for lv in range(ref.L_top))
+        assert np.array_equal(g.lev, ref.lev) and g.L_top == ref.L_top
+        gs.check_table_structure(g, ix.capacity)
+        # a P-DCI parent that differs must be a near-tie of the oracle's in
+        # both directions (a better parent than P-DCI finds is a mismatch too)
+        X = ref.X()
+        for lv in range(ref.L_top):
+            for i in np.nonzero(ref.parent[lv] != g.parent[lv])[0]:
+                da = float(((X[i] - X[ref.parent[lv][i]]) ** 2).sum())
+                db = float(((X[i] - X[g.parent[lv][i]]) ** 2).sum())
+                assert abs(da - db) <= gs.BAND * max(da, db), f"level {lv} token {i}: D {db:.9g} vs {da:.9g}"
+        replay, t = gs.validate_parents(ref, g)
+        ties += t
+        if t:
+            ref = gs.oracle_replay(K64, V64, h, seed, levels, plog2, replay)
+        if gs.compare_layout(ref, g, ix.capacity):
+            gs.adopt_gpu_slots(ref, g)
+        refs[h] = ref
+    say(f"pdci parity ok: parent near-ties={ties}, parents differing from the exact search={differs}")
+    for _ in range(2):
+        gs.check_decode(w, ix, refs, synth.decode_queries(w, G, gen), budget, 4)
+    return differs
+
+
+def test_pdci_build_bf16():
+    assert _pdci_case(2, 3000, 128, "bf16", 24, 31, m=2, l=2, visits=32, cands=4) > 0
+
+
+def test_pdci_build_f32_three_simple_indices():
+    assert _pdci_case(1, 2000, 64, "f32", 16, 32, m=1, l=3, visits=16, cands=2) > 0
+
+
+def test_pdci_unbounded_budgets_match_the_exact_search():
+    """Visits and candidates that cover every candidate parent: the exact
+    parents (the oracle's P-DCI then reduces to its exact search)."""
+    assert _pdci_case(2, 1200, 128, "bf16", 12, 33, m=2, l=2, visits=10 ** 6, cands=10 ** 6) == 0
+
+
+def test_pdci_argument_checks():
+    say("pdci argument checks")
+    ix = IceIndex(1, 1, 64, "f32", 64, 3, 4, 0, max_budget=64)
+    K = torch.zeros(1, 8, 64, device="cuda")
+    dirs = torch.zeros(16 * 2, 65, device="cuda")
+    with pytest.raises(L.IceError):
+        ix.ice_build_pdci(K, K, dirs[:5], 1, 5, 4, 1)          # l above ICE_PDCI_MAX_L
+    with pytest.raises(L.IceError):
+        ix.ice_build_pdci(K, K, dirs[:20], 5, 4, 4, 1)         # m*l above ICE_PDCI_MAX_KEYS
+    with pytest.raises(L.IceError):
+        ix.ice_build_pdci(K, K, dirs[:2], 1, 2, 0, 1)          # no visits
