@@ -63,6 +63,8 @@ def parse():
                     help="resident (sink + window) tokens per head for the resident-token leg; 0 skips it")
     ap.add_argument("--drift-steps", type=int, default=4096,
                     help="generated steps of the split-reading recall comparison (0 skips it)")
+    ap.add_argument("--pdci-tokens", type=int, default=100000,
+                    help="context of the P-DCI against exact-parent comparison (0 skips it)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="print a markdown summary of rocprofv3 output instead of benchmarking: one "
@@ -361,6 +363,79 @@ def time_reuse(ix, w, a, H, N, heads_per_layer=8):
             "index_keys_per_s_with_reuse": H * N / (reuse / 1000.0)}
 
 
+def selection_recall(ix, Q, KT, budget):
+    """Share of each query head's exact top-`budget` keys by q.k (Q [H, G, d],
+    KT [H, d, n] fp32) that lie in the pages ice_select picks for it."""
+    import torch
+    from ann_retrieval_amd import _lib as L
+    H, G = Q.shape[0], Q.shape[1]
+    sel, _, _ = ix.ice_select(Q, budget, budget // 16)
+    top = torch.topk(torch.bmm(Q.float(), KT), budget, dim=-1).indices
+    hit = 0
+    for h in range(H):
+        tok = torch.from_numpy(ix.export(h, L.ICE_EXP_PAGE_TOK, 0).reshape(-1, 16)).to(Q.device)
+        stok = tok[sel[h].long().clamp(min=0)].reshape(G, -1)
+        stok = torch.where((sel[h] >= 0).repeat_interleave(16, dim=1), stok, -1)
+        for g in range(G):
+            hit += int(torch.isin(top[h, g], stok[g]).sum())
+    return hit / (H * G * budget)
+
+
+def pdci_leg(a):
+    """Index build with P-DCI parents against the exact MFMA search at a
+    100k-token context (8 KV heads x 4 query heads, d=128 bf16, 1024-centre
+    mixture keys with rotations): build time, the share of level-0 parents
+    equal to the exact ones, and the selection's token recall at a 64-token
+    budget over 16 random decode queries per query head, per P-DCI setting
+    (m composite indices of l simple indices, visits, candidates)."""
+    import torch
+    from ann_retrieval_amd import _lib as L
+    from ann_retrieval_amd import synth
+    from ann_retrieval_amd.api import IceIndex
+    H, G, N, d, budget = 8, 4, a.pdci_tokens, 128, 64
+    w, gen = synth.clustered_kv(H, N, d, 1024, "bf16", a.seed + 11, device="cpu", rotate=True)
+    K, V = w.K.cuda(), w.V.cuda()
+    KT = K.float().transpose(1, 2).contiguous()
+    Qs = [synth.decode_queries(w, G, gen).cuda() for _ in range(16)]
+    ix = IceIndex(H, G, d, "bf16", N, 3, 4, a.seed + 11, max_budget=budget)
+
+    def timed(fn):
+        ms = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return sorted(ms)[1]
+
+    def parents():
+        return [ix.export(h, L.ICE_EXP_PARENT, 0)[:N].copy() for h in range(H)]
+
+    exact_ms = timed(lambda: ix.ice_build(K, V))
+    ref = parents()
+    out = {"workload": f"{N}-token context, 8 KV heads x 4 query heads, d=128 bf16, 1024-centre mixtures",
+           "exact": {"build_ms": exact_ms, "parent_agreement": 1.0,
+                     "recall_at_64": float(np.mean([selection_recall(ix, Q, KT, budget) for Q in Qs]))}}
+    print(f"[bench] exact parents: build {exact_ms:.2f} ms, recall@64 {out['exact']['recall_at_64']:.4f}",
+          file=sys.stderr, flush=True)
+    for m, l, visits, cands in [(2, 2, 64, 8), (4, 2, 256, 32), (4, 2, 1024, 64)]:
+        dirs = synth.projection_dirs(m * l, d, a.seed + 12, device="cuda")
+        ms = timed(lambda: ix.ice_build_pdci(K, V, dirs, m, l, visits, cands))
+        got = parents()
+        lev0 = [ix.export(h, L.ICE_EXP_LEVEL, np_dtype=np.int8)[:N] == 0 for h in range(H)]
+        agree = float(np.mean(np.concatenate([(got[h] == ref[h])[lev0[h]] for h in range(H)])))
+        rec = float(np.mean([selection_recall(ix, Q, KT, budget) for Q in Qs]))
+        key = f"m{m}_l{l}_v{visits}_c{cands}"
+        out[key] = {"build_ms": ms, "parent_agreement": agree, "recall_at_64": rec}
+        print(f"[bench] P-DCI {key}: build {ms:.2f} ms, parents equal to the exact ones {agree:.4f}, "
+              f"recall@64 {rec:.4f}", file=sys.stderr, flush=True)
+    del ix
+    return out
+
+
 def split_drift(a):
     """Long generation under both split readings, on the same inputs: one
     Qwen3-32B-shaped layer (8 KV heads x 8 query heads, d=128 bf16, 512-centre
@@ -371,7 +446,6 @@ def split_drift(a):
     top-256 keys by q.k that lie in its selected pages (mean over the 64 query
     heads). Also the mean time of one insert call (8 heads) per split reading."""
     import torch
-    from ann_retrieval_amd import _lib as L
     from ann_retrieval_amd import synth
     from ann_retrieval_amd.api import IceIndex
     H, G, N, d, budget, steps = 8, 8, 8192, 128, 256, a.drift_steps
@@ -393,17 +467,7 @@ def split_drift(a):
         recall, ev = [], []
         for s in range(steps):
             if s in marks:
-                n = N + s
-                sel, _, _ = ix.ice_select(Q[s], budget, budget // 16)
-                top = torch.topk(torch.bmm(Q[s].float(), KT[:, :, :n]), budget, dim=-1).indices
-                hit = 0
-                for h in range(H):
-                    tok = torch.from_numpy(ix.export(h, L.ICE_EXP_PAGE_TOK, 0).reshape(-1, 16)).cuda()
-                    stok = tok[sel[h].long().clamp(min=0)].reshape(G, -1)
-                    stok = torch.where((sel[h] >= 0).repeat_interleave(16, dim=1), stok, -1)
-                    for g in range(G):
-                        hit += int(torch.isin(top[h, g], stok[g]).sum())
-                recall.append(hit / (H * G * budget))
+                recall.append(selection_recall(ix, Q[s], KT[:, :, :N + s], budget))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             ix.ice_insert(Kn[s], Vn[s])
@@ -708,6 +772,8 @@ def main():
         out["index_reuse"] = reuse
     if a.drift_steps > 0:
         out["split_drift"] = split_drift(a)
+    if a.pdci_tokens > 0:
+        out["pdci"] = pdci_leg(a)
     if not a.no_cpu:
         heads = list(range(min(a.cpu_heads, H)))
         t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(3)], a.budget, a.budget // 16,
