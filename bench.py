@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--budget", type=int, default=256)
     ap.add_argument("--budgets", default="", help="extra budgets to time beside --budget, e.g. 64,128")
     ap.add_argument("--builds", type=int, default=3)
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle's timed sample")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-host-pool", action="store_true", help="skip the host-pool mode measurement")
     ap.add_argument("--no-pipeline", action="store_true", help="skip the per-layer build pipeline measurement")
@@ -552,7 +552,7 @@ def cpu_baseline(w, Qs, budget, beam, heads, seed):
     t0 = time.perf_counter()
     refs = [ic.build_head(K[i], V[i], h, seed) for i, h in enumerate(heads)]
     t_build = time.perf_counter() - t0
-    n_steps = 3
+    n_steps = len(Qs)
     t0 = time.perf_counter()
     for s in range(n_steps):
         Q = Qs[s][:len(heads)].float().cpu().double().numpy()
@@ -777,13 +777,14 @@ def main():
         out["pdci"] = pdci_leg(a)
     if not a.no_cpu:
         heads = list(range(min(a.cpu_heads, H)))
-        t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(3)], a.budget, a.budget // 16,
-                                               heads, a.seed)
+        n_cpu_steps = min(a.steps, 50)
+        t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(n_cpu_steps)], a.budget,
+                                               a.budget // 16, heads, a.seed)
         per_head_step = t_dec / len(heads)
         out["cpu_baseline"] = {
             "value": 1.0 / (per_head_step * H), "unit": "decode steps/s", "cores": threads, "kind": "oracle",
             "sample": (f"fp64 oracle on {len(heads)} of {H} heads ({N} tokens each): its own index build, then "
-                       f"select+attend for {G} query heads over 3 steps at T={a.budget}; per-head time scaled to "
+                       f"select+attend for {G} query heads over {n_cpu_steps} steps at T={a.budget}; per-head time scaled to "
                        f"{H} heads"),
             "index_keys_per_s": len(heads) * N / t_build,
             "cpu": platform.processor() or platform.machine(),
