@@ -367,6 +367,7 @@ template <int D, class T>
 __global__ __launch_bounds__(256) void k_copy_pages(DevLayout L, const T* K, int64_t hstride, void* blob,
                                                     int level) {
   using G = RowGeo<D, T>;
+  constexpr int UNR = 4;                 // rows per thread with their loads in flight together
   const int h = blockIdx.y;
   void* hb = head_base(blob, L, h);
   const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
@@ -380,15 +381,28 @@ __global__ __launch_bounds__(256) void k_copy_pages(DevLayout L, const T* K, int
   const float* e = at<float>(hb, L.off_e);
   const T* Kh = K + (int64_t)h * hstride;
   const int nrows = n_pages * ICE_PAGE_CAP;
-  for (int r0 = (blockIdx.x * 4 + wave) * G::RPP; r0 < nrows; r0 += gridDim.x * 4 * G::RPP) {
-    const int r = r0 + lane / G::LPR;
-    if (r >= nrows) continue;
-    const int tok = pg_tok[r];
-    const int64_t so = (lane % G::LPR) * 16;
-    V4 kv = {0, 0, 0, 0};
-    if (tok >= 0) kv = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Kh + (int64_t)tok * D) + so);
-    *reinterpret_cast<V4*>(reinterpret_cast<char*>(pk + (int64_t)r * D) + so) = kv;
-    if (pe && (lane % G::LPR) == 0) pe[r] = tok >= 0 ? e[tok] : 0.0f;
+  const int64_t so = (lane % G::LPR) * 16;
+  const int step = gridDim.x * 4 * G::RPP;
+  for (int r0 = (blockIdx.x * 4 + wave) * G::RPP + lane / G::LPR; r0 < nrows; r0 += step * UNR) {
+    int tok[UNR];
+    V4 kv[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int r = r0 + u * step;
+      tok[u] = r < nrows ? pg_tok[r] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      kv[u] = V4{0, 0, 0, 0};
+      if (tok[u] >= 0) kv[u] = *reinterpret_cast<const V4*>(reinterpret_cast<const char*>(Kh + (int64_t)tok[u] * D) + so);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int r = r0 + u * step;
+      if (r >= nrows) continue;
+      *reinterpret_cast<V4*>(reinterpret_cast<char*>(pk + (int64_t)r * D) + so) = kv[u];
+      if (pe && (lane % G::LPR) == 0) pe[r] = tok[u] >= 0 ? e[tok[u]] : 0.0f;
+    }
   }
 }
 
@@ -398,7 +412,14 @@ __global__ __launch_bounds__(256) void k_copy_pages(DevLayout L, const T* K, int
 // dimension sit together. One wave per page; empty slots are zero.
 template <int D, class T>
 __global__ __launch_bounds__(256) void k_copy_vt(DevLayout L, const T* V, int64_t hstride, void* blob) {
-  constexpr int DPL = D / ICE_WAVE;      // dimensions per lane
+  // One wave per page: its 16 rows arrive as 16-byte pieces (all of a lane's
+  // loads in flight together) into an LDS copy of the page, from which each
+  // lane assembles 16-byte pieces of the transposed layout.
+  constexpr int RB = D * (int)sizeof(T);        // row bytes
+  constexpr int PPR = RB / 16;                  // 16-byte pieces per row
+  constexpr int NPL = ICE_PAGE_CAP * PPR / ICE_WAVE;   // pieces per lane
+  constexpr int EPC = 16 / (int)sizeof(T);      // elements per piece
+  __shared__ __attribute__((aligned(16))) char lds[4][ICE_PAGE_CAP * RB];
   const int h = blockIdx.y;
   void* hb = head_base(blob, L, h);
   const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
@@ -406,24 +427,44 @@ __global__ __launch_bounds__(256) void k_copy_vt(DevLayout L, const T* V, int64_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t* pg_tok = at<int32_t>(hb, L.off_pg_tok[0]);
   T* pv = reinterpret_cast<T*>(v_pages(L, hb, h));
-  const T* Vh = V + (int64_t)h * hstride;
-  for (int pg = blockIdx.x * 4 + wave; pg < n_pages; pg += gridDim.x * 4) {
-    const int my_tok = lane < ICE_PAGE_CAP ? pg_tok[(int64_t)pg * ICE_PAGE_CAP + lane] : -1;
-    T val[ICE_PAGE_CAP][DPL];
+  const char* Vh = reinterpret_cast<const char*>(V + (int64_t)h * hstride);
+  char* buf = lds[wave];
+  const T* bt = reinterpret_cast<const T*>(buf);
+  // the block's waves take consecutive pages in step, so the barriers are uniform
+  for (int pg0 = blockIdx.x * 4; pg0 < n_pages; pg0 += gridDim.x * 4) {
+    const int pg = pg0 + wave;
+    const bool live = pg < n_pages;
+    V4 x[NPL];
 #pragma unroll
-    for (int sl = 0; sl < ICE_PAGE_CAP; ++sl) {
-      const int tok = __shfl(my_tok, sl, 64);
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) val[sl][j] = tok >= 0 ? Vh[(int64_t)tok * D + DPL * lane + j] : T(0);
+    for (int u = 0; u < NPL; ++u) {
+      const int q = lane + ICE_WAVE * u;
+      const int tok = live ? pg_tok[(int64_t)pg * ICE_PAGE_CAP + q / PPR] : -1;
+      x[u] = V4{0, 0, 0, 0};
+      if (tok >= 0) x[u] = *reinterpret_cast<const V4*>(Vh + (int64_t)tok * RB + (q % PPR) * 16);
     }
 #pragma unroll
-    for (int g = 0; g < ICE_PAGE_CAP / 4; ++g) {
-      T* dst = pv + (((int64_t)pg * 4 + g) * D + DPL * lane) * 4;
-#pragma unroll
-      for (int j = 0; j < DPL; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[4 * j + i] = val[4 * g + i][j];
+    for (int u = 0; u < NPL; ++u) {
+      const int q = lane + ICE_WAVE * u;
+      *reinterpret_cast<V4*>(buf + (q / PPR) * RB + (q % PPR) * 16) = x[u];
     }
+    __syncthreads();
+    if (live) {
+      // output element E = (g * D + d) * 4 + i holds slot 4 g + i, dimension d
+#pragma unroll
+      for (int u = 0; u < NPL; ++u) {
+        const int o = lane + ICE_WAVE * u;
+        alignas(16) T out[EPC];
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) {
+          const int E = o * EPC + k;
+          const int i = E % 4, d = (E / 4) % D, g = E / (4 * D);
+          out[k] = bt[(4 * g + i) * D + d];
+        }
+        *reinterpret_cast<V4*>(pv + (int64_t)pg * ICE_PAGE_CAP * D + (int64_t)o * EPC) =
+            *reinterpret_cast<const V4*>(out);
+      }
+    }
+    __syncthreads();
   }
 }
 
