@@ -87,3 +87,23 @@ def test_pdci_argument_checks():
         ix.ice_build_pdci(K, K, dirs[:20], 5, 4, 4, 1)         # m*l above ICE_PDCI_MAX_KEYS
     with pytest.raises(L.IceError):
         ix.ice_build_pdci(K, K, dirs[:2], 1, 2, 0, 1)          # no visits
+
+
+@pytest.mark.parametrize("n", [0, 1, 17, 300])
+def test_pdci_edge_builds(n):
+    """Empty, single-token and tiny builds (often no promoted point, so no
+    parent search at all) give the oracle's layout."""
+    say(f"pdci edge build n={n}")
+    w, gen = synth.clustered_kv(1, max(n, 1), 64, 4, "f32", 40 + n, device="cpu")
+    K, V = w.K[:, :n].contiguous(), w.V[:, :n].contiguous()
+    dirs = synth.projection_dirs(4, 64, 41)
+    ix = IceIndex(1, 1, 64, "f32", max(n, 1), 3, 2, 40 + n, max_budget=64)
+    ix.ice_build_pdci(K.cuda(), V.cuda(), dirs.cuda(), 2, 2, 8, 2)
+    torch.cuda.synchronize()
+    g = gs.read_head(ix, 0)
+    ref = ic.build_head(gs.to64(K[0]), gs.to64(V[0]), 0, 40 + n, 3, 2, pdci=pd.Pdci(dirs.double().numpy(), 2, 2, 8, 2))
+    assert g.n == ref.n == n and np.array_equal(g.lev, ref.lev)
+    replay, t = gs.validate_parents(ref, g)
+    if t:
+        ref = gs.oracle_replay(gs.to64(K[0]), gs.to64(V[0]), 0, 40 + n, 3, 2, replay)
+    gs.compare_layout(ref, g, ix.capacity)
