@@ -107,3 +107,42 @@ def test_pdci_edge_builds(n):
     if t:
         ref = gs.oracle_replay(gs.to64(K[0]), gs.to64(V[0]), 0, 40 + n, 3, 2, replay)
     gs.compare_layout(ref, g, ix.capacity)
+
+
+def test_pdci_build_then_inserts():
+    """Inserts into a P-DCI-built index search their parents exactly, as
+    they do after an exact build (bf16, d=64)."""
+    H, N, d, seed = 2, 1500, 64, 42
+    say(f"pdci build then inserts H={H} N={N} d={d} bf16")
+    w, gen = synth.clustered_kv(H, N, d, 16, "bf16", seed, device="cpu")
+    dirs = synth.projection_dirs(4, d, seed + 1)
+    ix = IceIndex(H, 2, d, "bf16", N + 200, 3, 4, seed, max_budget=64)
+    ix.ice_build_pdci(w.K.cuda(), w.V.cuda(), dirs.cuda(), 2, 2, 32, 4)
+    torch.cuda.synchronize()
+    cfg = pd.Pdci(dirs.double().numpy(), 2, 2, 32, 4)
+    refs = {}
+    for h in range(H):
+        g = gs.read_head(ix, h)
+        K64, V64 = gs.to64(w.K[h]), gs.to64(w.V[h])
+        ref = ic.build_head(K64, V64, h, seed, 3, 4, pdci=cfg)
+        replay, t = gs.validate_parents(ref, g)
+        if t:
+            ref = gs.oracle_replay(K64, V64, h, seed, 3, 4, replay)
+        if gs.compare_layout(ref, g, ix.capacity):
+            gs.adopt_gpu_slots(ref, g)
+        refs[h] = ref
+    walk = synth.QueryWalk(w, 2, gen, seg=16)
+    ks, vs = zip(*[walk.step()[1:] for _ in range(200)])
+    k, v = torch.cat(ks, 1).contiguous(), torch.cat(vs, 1).contiguous()
+    say("insert n_new=200")
+    ix.ice_insert(k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    for h in range(H):
+        g = gs.read_head(ix, h)
+        gs.replay_inserts(refs[h], g, k[h], v[h], h, seed, 3, 4)
+        assert np.array_equal(g.lev, refs[h].lev)
+        gs.check_table_structure(g, ix.capacity)
+        if gs.compare_layout(refs[h], g, ix.capacity):
+            gs.adopt_gpu_slots(refs[h], g)
+    w2 = synth.Workload(K=torch.cat([w.K, k], 1), V=torch.cat([w.V, v], 1), mix=w.mix, dtype=w.dtype)
+    gs.check_decode(w2, ix, refs, walk.step()[0], 64, 4)

@@ -109,3 +109,7 @@ def test_resort_rejects_the_host_pool():
     say("resort with host pool is refused")
     with pytest.raises(L.IceError):
         IceIndex(1, 1, 64, "f32", 64, 3, 4, 0, max_budget=64, host_pool=True, resort=True)
+
+
+def test_resort_inserts_f32_d128():
+    _run(1, 2, 1200, 128, "f32", 10, 13, 3, 4, [64, 1, 90], 64, [(64, 4)])
