@@ -202,3 +202,93 @@ def test_qwen_shaped_long_generation():
         assert members == list(range(N + steps)), "every token in exactly one page"
     assert splits > 0
     say(f"qwen-shaped: {splits} page splits over {H} heads")
+
+
+def test_resort_split_long_generation():
+    """The re-sort split over a Qwen3-32B-shaped layer's long generation
+    (8 KV heads x 8 query heads, 8,192-token prompt, 4,096 steps inserting one
+    token per head), in the bench's configuration. Heads 0 and 5 are replayed
+    by the oracle (``resplit=True``) through all 4,096 inserts: layout exact
+    up to near-equal distances, pool rows bit-exact, then a decode check on
+    the final index; every head is checked for structure."""
+    from oracle import icecache as ic
+    H, G, N, d, C, steps = 8, 8, 8192, 128, 512, 4096
+    say(f"resort long generation H={H} G={G} N={N} + {steps} steps")
+    w, gen = synth.clustered_kv(H, N, d, C, "bf16", 7, device="cpu", rotate=True)
+    ix = IceIndex(H, G, d, "bf16", N + steps, seed=7, max_budget=256, device=DEV, resort=True)
+    ix.ice_build(w.K.cuda(), w.V.cuda())
+    torch.cuda.synchronize()
+    heads = [0, 5]
+    refs = check_build(w, ix, heads, 7, 3, 4)
+    walk = synth.QueryWalk(w, G, gen, seg=64)
+    ks, vs = [], []
+    for s in range(steps):
+        _, k, v = walk.step()
+        ix.ice_insert(k.cuda(), v.cuda())
+        ks.append(k)
+        vs.append(v)
+        if s % 1024 == 1023:
+            torch.cuda.synchronize()
+            say(f"step {s + 1} of {steps}")
+    torch.cuda.synchronize()
+    Kn, Vn = torch.cat(ks, 1), torch.cat(vs, 1)
+    for i, h in enumerate(heads):
+        g = gs.read_head(ix, h)
+        gs.replay_inserts(refs[h], g, Kn[h], Vn[h], h, 7, 3, 4, resplit=True)
+        assert np.array_equal(g.lev, refs[h].lev) and g.stats["splits"] == refs[h].splits
+        if gs.compare_layout(refs[h], g, ix.capacity):
+            gs.adopt_gpu_slots(refs[h], g)
+        say(f"head {h}: {steps} inserts replayed, {refs[h].splits} splits")
+    for h in range(H):
+        g = gs.read_head(ix, h)
+        assert g.n == N + steps and g.stats["overflow"] == 0
+        gs.check_table_structure(g, ix.capacity)
+    Kall, Vall = torch.cat([w.K, Kn], 1), torch.cat([w.V, Vn], 1)
+    for h in heads:
+        P = ix.stats(h)["n_pages"][0]
+        kp = ix.export(h, L.ICE_EXP_PAGE_K, 0, np_dtype=np.int16).reshape(-1, 16, d)[:P]
+        tok = gs.read_head(ix, h).tables[0]["tok"]
+        assert np.array_equal(kp[tok >= 0], gs.raw_rows(Kall[h])[tok[tok >= 0]])
+    out = run_decode(ix, walk.step()[0], 256, 16)
+    check_all_heads(ix, out)
+    compare_decode(ix, refs, out)
+
+
+def test_pdci_100k_sampled_children():
+    """P-DCI parents at the needle workload's size (8 KV heads x 100,000
+    tokens, d=128 bf16, 1024-centre mixtures), in the bench's P-DCI setting
+    m=4, l=2, 256 visits, 32 candidates: for 300 sampled level-0 points of
+    heads 0 and 6 the oracle's P-DCI parent (over the same candidates,
+    directions and budgets) equals the GPU's up to near-equal distances."""
+    from oracle import icecache as ic
+    from oracle import pdci as pd
+    H, N, d, seed = 8, 100000, 128, 11
+    m, l, visits, cands = 4, 2, 256, 32
+    say(f"pdci 100k H={H} N={N} m={m} l={l} visits={visits} cands={cands}")
+    w, gen = synth.clustered_kv(H, N, d, 1024, "bf16", seed, device="cpu", rotate=True)
+    dirs = synth.projection_dirs(m * l, d, seed + 1)
+    ix = IceIndex(H, 4, d, "bf16", N, 3, 4, seed, max_budget=64, device=DEV)
+    ix.ice_build_pdci(w.K.cuda(), w.V.cuda(), dirs.cuda(), m, l, visits, cands)
+    torch.cuda.synchronize()
+    cfg = pd.Pdci(dirs.double().numpy(), m, l, visits, cands)
+    rng = np.random.default_rng(5)
+    for h in (0, 6):
+        g = gs.read_head(ix, h)
+        K64 = gs.to64(w.K[h])
+        n2, M2, e = ic.lift(K64)
+        lev = ic.draw_levels(seed, h, 0, N, 3, 4)
+        assert np.array_equal(g.lev, lev)
+        X = ic.lifted(K64, e)
+        X32 = X.copy()
+        X32[:, -1] = X32[:, -1].astype(np.float32)
+        cand = np.nonzero(lev >= 1)[0]
+        kids = rng.choice(np.nonzero(lev == 0)[0], 300, replace=False)
+        j, D1, _ = pd.nearest_pdci(X[kids], X32[kids], X[cand], X32[cand], cfg)
+        gp = g.parent[0][kids]
+        differ = 0
+        for i, t in enumerate(kids):
+            if gp[i] != cand[j[i]]:
+                dg = float(((X[t] - X[gp[i]]) ** 2).sum())
+                assert abs(dg - D1[i]) <= gs.BAND * max(dg, D1[i]), f"head {h} token {t}: {dg:.9g} vs {D1[i]:.9g}"
+                differ += 1
+        say(f"head {h}: 300 sampled P-DCI parents match ({differ} near-ties)")
