@@ -725,6 +725,8 @@ def main():
     knew = [synth.new_tokens(w, gen, device=dev) for _ in range(n_ins)]
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the spin lets the host queue every insert before the first one starts
+    torch.cuda._sleep(int(5e7))
     e0.record()
     for k_, v_ in knew:
         ix.ice_insert(k_, v_)
