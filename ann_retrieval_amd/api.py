@@ -143,6 +143,19 @@ class IceIndex:
         check(self.lib.ice_build(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0), _ptr(self.ws),
                                  self.ws_bytes, _stream_ptr(self.device)), "ice_build")
 
+    def ice_build_timed(self, K: torch.Tensor, V: torch.Tensor) -> np.ndarray:
+        """ice_build with per-phase times (ms, ICE_BUILD_PHASES entries; see include/ice.h), measured by events
+        on the current stream; waits for the build to finish."""
+        self._check_kv(K, "K")
+        self._check_kv(V, "V")
+        if K.shape != V.shape or K.stride() != V.stride():
+            raise ValueError("K and V must have the same shape and strides")
+        ms = np.zeros(_lib.ICE_BUILD_PHASES, dtype=np.float32)
+        check(self.lib.ice_build_timed(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0), _ptr(self.ws),
+                                       self.ws_bytes, _stream_ptr(self.device), ms.ctypes.data_as(ctypes.c_void_p)),
+              "ice_build_timed")
+        return ms
+
     def ice_build_pdci(self, K: torch.Tensor, V: torch.Tensor, dirs: torch.Tensor, m: int, l: int, visits: int,
                        cands: int) -> None:
         """ice_build with parents found by P-DCI: dirs is a float32 [m*l, d+1] device tensor of projection

@@ -266,7 +266,8 @@ __device__ inline void attend_one(const DevLayout& L, const void* hb, int h, int
 }
 
 // A wave's partials (m, l and o of query qn; every lane group holds m and l,
-// lane group qt holds dims 16c + 4qt + j) into slot wv of the LDS partials.
+// lane group qt holds dims 16c + 4qt + j) into slot wv (< nw) of the LDS
+// partials.
 template <int D>
 __device__ inline void write_partial(const WaveAcc<D>& st, int wv, int G, float* part, int nw) {
   using M = MGeo<D>;
@@ -286,21 +287,24 @@ __device__ inline void write_partial(const WaveAcc<D>& st, int wv, int G, float*
       for (int j = 0; j < 4; ++j) part_o[(wv * G + qn) * D + 16 * c + 4 * qt + j] = st.acc[c][j];
 }
 
-// Merges the nw waves' partials (after a block barrier that follows every
-// write_partial) in one pass: every output element's thread forms its
-// query's common base, total weight and the waves' normalised factors itself
-// (the reads of one query's m and l are LDS broadcasts across a wave).
+// Merges the partials in slots 0 .. nused-1 of an area laid out for nw slots
+// (nused = nw: every wave's; after a block barrier that follows every
+// write_partial) in one pass, in slot order: every output element's thread
+// forms its query's common base, total weight and the slots' normalised
+// factors itself (the reads of one query's m and l are LDS broadcasts across
+// a wave).
 template <int D>
-__device__ inline void merge_partials(int G, const float* part, int nw, float* Oh, float* lseh) {
+__device__ inline void merge_partials(int G, const float* part, int nw, float* Oh, float* lseh, int nused = -1) {
   const float* part_m = part + 8 * D;
   const float* part_l = part_m + nw * ICE_MAX_GROUP;
   const float* part_o = part_l + nw * ICE_MAX_GROUP;
+  const int ns = nused < 0 ? nw : nused;
   for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
     const int q = t / D, dd = t % D;
     float Mx = -INFINITY;
-    for (int w = 0; w < nw; ++w) Mx = fmaxf(Mx, part_m[w * ICE_MAX_GROUP + q]);
+    for (int w = 0; w < ns; ++w) Mx = fmaxf(Mx, part_m[w * ICE_MAX_GROUP + q]);
     float Ls = 0.0f, a = 0.0f;
-    for (int w = 0; w < nw; ++w) {
+    for (int w = 0; w < ns; ++w) {
       const float mw = part_m[w * ICE_MAX_GROUP + q];
       const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - Mx);
       Ls = fmaf(part_l[w * ICE_MAX_GROUP + q], f, Ls);

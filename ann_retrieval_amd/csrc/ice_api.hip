@@ -27,6 +27,17 @@ struct ice_index {
   std::vector<uint8_t> dense;       // the flags, host copy
   std::vector<uint8_t> head_built;  // heads built since the handle was created
   bool built;             // every head built
+  // Level counts on the host. pos_ge[l][h]: the positions (< capacity) whose
+  // own promotion draw in head h reaches level l >= 1, ascending. runs[h]:
+  // the position ranges [t0, t1) of head h's tokens and the head whose draws
+  // gave them their levels (a head built by reuse takes its source's levels
+  // for the tokens it was built with); ltop[h]: its top level at build.
+  struct Run {
+    int32_t t0, t1, src;
+  };
+  std::vector<std::vector<int32_t>> pos_ge[ICE_MAX_LEVELS];
+  std::vector<std::vector<Run>> runs;
+  std::vector<int32_t> ltop;
 };
 
 namespace {
@@ -174,22 +185,19 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
   W->pdci_bytes = align256((int64_t)p->n_heads * ICE_PDCI_MAX_KEYS * n1 * 24);
 }
 
-int64_t attend_part_bytes(const DevLayout& L, int uni_stride) {
-  return align256((int64_t)L.H * attend_splits(uni_stride) * L.G * (L.d + 2) * 4);
-}
 bool host_mode(const DevLayout& L) { return L.vpool_head_bytes > 0; }
 int64_t page_bytes(const DevLayout& L) { return (int64_t)ICE_PAGE_CAP * L.d * L.elt; }
-// attention's workspace: split partials, then (host-pool mode) the V staging
-// area of uni_stride pages per head
+// attention's workspace: nothing in the device-pool mode; in host-pool mode
+// the V staging area of uni_stride pages per head
 int64_t attend_ws_bytes(const DevLayout& L, int uni_stride) {
   const int64_t stage = host_mode(L) ? (int64_t)L.H * uni_stride * page_bytes(L) : 0;
-  return attend_part_bytes(L, uni_stride) + align256(stage);
+  return align256(stage);
 }
 // the layout attention runs with: staged V in host-pool mode
 DevLayout attend_layout(const DevLayout& L, void* ws, int uni_stride) {
   DevLayout A = L;
   if (host_mode(L)) {
-    A.vstage = static_cast<const char*>(ws) + attend_part_bytes(L, uni_stride);
+    A.vstage = static_cast<const char*>(ws);
     A.vstage_pages = uni_stride;
   }
   return A;
@@ -204,6 +212,42 @@ int check_budget(const ice_index* idx, int32_t budget) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Tokens of head h at level >= l (l >= 1, at most its top level) once its
+// runs extend to position t_end with its own draws.
+int64_t level_count(const ice_index* idx, int h, int l, int32_t t_end) {
+  int64_t c = 0;
+  int32_t covered = 0;
+  auto in_range = [&](int src, int32_t a, int32_t b) {
+    const std::vector<int32_t>& v = idx->pos_ge[l][src];
+    return (int64_t)(std::lower_bound(v.begin(), v.end(), b) - std::lower_bound(v.begin(), v.end(), a));
+  };
+  for (const auto& r : idx->runs[h]) {
+    c += in_range(r.src, r.t0, r.t1);
+    covered = std::max(covered, r.t1);
+  }
+  if (t_end > covered) c += in_range(h, covered, t_end);
+  return c;
+}
+
+// Top level at build: the highest level holding a token of [0, n).
+int32_t top_from_draws(const ice_index* idx, int h, int32_t n) {
+  int32_t lt = 0;
+  for (int l = 1; l < idx->p.levels; ++l) {
+    const std::vector<int32_t>& v = idx->pos_ge[l][h];
+    if (!v.empty() && v.front() < n) lt = l;
+  }
+  return lt;
+}
+
+// Records heads h0..h0+n_heads-1 as built from their own draws with n tokens.
+void note_own_build(ice_index* idx, int h0, int n_heads, int32_t n) {
+  for (int h = h0; h < h0 + n_heads; ++h) {
+    idx->runs[h].clear();
+    if (n > 0) idx->runs[h].push_back({0, n, h});
+    idx->ltop[h] = top_from_draws(idx, h, n);
+  }
+}
 
 }  // namespace
 
@@ -265,6 +309,14 @@ int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_ind
   idx->dense.assign(p->n_heads, 0);
   idx->head_built.assign(p->n_heads, 0);
   idx->built = false;
+  for (int l = 1; l < p->levels; ++l) idx->pos_ge[l].assign(p->n_heads, {});
+  for (int h = 0; h < p->n_heads; ++h)
+    for (int t = 0; t < p->capacity; ++t) {
+      const int lv = draw_level(p->seed, h, t, p->levels, p->promote_log2);
+      for (int l = 1; l <= lv; ++l) idx->pos_ge[l][h].push_back(t);
+    }
+  idx->runs.assign(p->n_heads, {});
+  idx->ltop.assign(p->n_heads, 0);
   *out = idx;
   return ICE_OK;
 }
@@ -300,7 +352,8 @@ int32_t ice_n_tokens(const ice_index* idx) { return idx ? idx->n_tokens : -1; }
 namespace {
 
 int build_range(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, int32_t h0,
-                int32_t n_heads, void* ws, size_t ws_bytes, void* stream, const PdciArgs* pd) {
+                int32_t n_heads, void* ws, size_t ws_bytes, void* stream, const PdciArgs* pd,
+                hipEvent_t* ev = nullptr) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");
   const int H = idx->p.n_heads;
   if (h0 < 0 || n_heads < 1 || h0 > H - n_heads)
@@ -333,7 +386,7 @@ int build_range(ice_index* idx, const void* K, const void* V, int32_t n_tokens, 
   char* blob = static_cast<char*>(idx->blob) + (int64_t)h0 * L.head_bytes;
   char* wsr = static_cast<char*>(ws) + (int64_t)h0 * idx->W.head_bytes;
   hipError_t e = launch_build(L, idx->W, blob, K, V, n_tokens, head_stride, wsr, range_built,
-                              static_cast<hipStream_t>(stream), pd);
+                              static_cast<hipStream_t>(stream), pd, ev);
   if (e != hipSuccess) return hip_fail(e, "ice_build launch");
   if (!range_built)     // headers were cleared: no dense flags there any more
     for (int h = h0; h < h0 + n_heads; ++h) {
@@ -341,6 +394,7 @@ int build_range(ice_index* idx, const void* K, const void* V, int32_t n_tokens, 
       idx->dense[h] = 0;
     }
   for (int h = h0; h < h0 + n_heads; ++h) idx->head_built[h] = 1;
+  note_own_build(idx, h0, n_heads, n_tokens);
   idx->n_tokens = n_tokens;
   bool all = true;
   for (int h = 0; h < H; ++h) all &= idx->head_built[h] != 0;
@@ -425,7 +479,12 @@ int ice_build_reuse(ice_index* idx, const void* K, const void* V, int32_t n_toke
       idx->n_dense -= idx->dense[h];
       idx->dense[h] = 0;
     }
-  for (int h = h0; h < h0 + n_heads; ++h) idx->head_built[h] = 1;
+  for (int h = h0; h < h0 + n_heads; ++h) {
+    idx->head_built[h] = 1;
+    // the layout, levels included, is the source's
+    idx->runs[h] = idx->runs[src_h0 + (h - h0)];
+    idx->ltop[h] = idx->ltop[src_h0 + (h - h0)];
+  }
   bool all = true;
   for (int h = 0; h < H; ++h) all &= idx->head_built[h] != 0;
   idx->built = all;
@@ -436,6 +495,30 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
               size_t ws_bytes, void* stream) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");
   return ice_build_heads(idx, K, V, n_tokens, head_stride, 0, idx->p.n_heads, ws, ws_bytes, stream);
+}
+
+int ice_build_timed(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, void* ws,
+                    size_t ws_bytes, void* stream, float* phase_ms) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (!phase_ms) return fail(ICE_ERR_ARG, "phase_ms is null");
+  hipEvent_t ev[ICE_BUILD_PHASES + 1] = {};
+  int rc = ICE_OK;
+  hipError_t e = hipSuccess;
+  int made = 0;
+  for (; made <= ICE_BUILD_PHASES && e == hipSuccess; ++made) e = hipEventCreate(&ev[made]);
+  if (e != hipSuccess) {
+    --made;
+    rc = hip_fail(e, "ice_build_timed event");
+  } else {
+    rc = build_range(idx, K, V, n_tokens, head_stride, 0, idx->p.n_heads, ws, ws_bytes, stream, nullptr, ev);
+    if (rc == ICE_OK) {
+      e = hipEventSynchronize(ev[ICE_BUILD_PHASES]);
+      for (int i = 0; i < ICE_BUILD_PHASES && e == hipSuccess; ++i) e = hipEventElapsedTime(&phase_ms[i], ev[i], ev[i + 1]);
+      if (e != hipSuccess) rc = hip_fail(e, "ice_build_timed timing");
+    }
+  }
+  for (int i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+  return rc;
 }
 
 int ice_insert(ice_index* idx, const void* k_new, const void* v_new, int32_t n_new, void* ws, size_t ws_bytes,
@@ -451,9 +534,31 @@ int ice_insert(ice_index* idx, const void* k_new, const void* v_new, int32_t n_n
   if ((int64_t)idx->n_tokens + n_new > idx->p.capacity)
     return fail(ICE_ERR_CAPACITY, "insert of %d tokens exceeds capacity %d (holds %d)", n_new, idx->p.capacity,
                 idx->n_tokens);
+  // A head built from its own draws stays within the tables sized from those
+  // draws. A head built by reuse holds its source's levels for its first
+  // tokens and its own after them, which can outgrow the tables: its level
+  // counts after the insert are checked against their bounds first.
+  const int32_t t_end = idx->n_tokens + n_new;
+  for (int h = 0; h < idx->p.n_heads; ++h) {
+    bool own = true;
+    for (const auto& r : idx->runs[h]) own &= r.src == h;
+    if (own) continue;
+    for (int l = 1; l <= idx->ltop[h]; ++l) {
+      const int64_t c = level_count(idx, h, l, t_end);
+      if (c > idx->L.ncap[l])
+        return fail(ICE_ERR_CAPACITY,
+                    "head %d (built by reuse) would hold %lld tokens at level %d, its tables hold %d; nothing inserted",
+                    h, (long long)c, l, idx->L.ncap[l]);
+    }
+  }
   hipError_t e = launch_insert(idx->L, idx->blob, k_new, v_new, n_new, idx->n_tokens,
                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ice_insert launch");
+  for (int h = 0; h < idx->p.n_heads; ++h) {
+    auto& rv = idx->runs[h];
+    if (!rv.empty() && rv.back().src == h && rv.back().t1 == idx->n_tokens) rv.back().t1 = t_end;
+    else rv.push_back({idx->n_tokens, t_end, h});
+  }
   idx->n_tokens += n_new;
   return ICE_OK;
 }

@@ -94,9 +94,6 @@ struct WsLayout {
   int64_t off_cnt, off_fill, off_cbase, off_pbase;  // i32 [ncap[1]+1]
   int64_t off_btok, off_bkey, off_bown;             // bucketed points: i32 / f32 / i32 [cap]
   int64_t build_bytes;           // H * head_bytes
-  int64_t attend_bytes;          // partials of split attention
-  int32_t nsplit;                // attention splits per head for the max budget
-  int32_t max_pages;             // max union size G*k for the max budget
   // P-DCI parent search (ice_build_pdci): a region after the per-head
   // build workspace holding, per head and simple index, ncap[1] keys by
   // candidate, the sorted keys, the sorted candidates and their positions

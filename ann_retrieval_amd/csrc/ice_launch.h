@@ -12,9 +12,10 @@ hipError_t launch_build_reuse(const DevLayout& L, const WsLayout& W, void* blob,
                               const void* V, int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s);
 // keep: a rebuild, which keeps the headers' resident counts and dense flags
 // pd: parents by P-DCI instead of the exact search (nullptr: exact)
+// ev: nullable, ICE_BUILD_PHASES + 1 events recorded on s at the phase boundaries
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
                         int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s,
-                        const PdciArgs* pd = nullptr);
+                        const PdciArgs* pd = nullptr, hipEvent_t* ev = nullptr);
 // k_gemm.hip: nearest parent of every level-`level` point among the level-(level+1) points
 hipError_t launch_parent_gemm(const DevLayout& L, const WsLayout& W, void* blob, const void* K,
                               int64_t head_stride, void* ws, int level, hipStream_t s);
@@ -32,7 +33,6 @@ bool decode_fused(const DevLayout& L, int budget, int beam);
 hipError_t launch_decode(const DevLayout& L, const void* blob, const void* Q, int budget, int beam, int32_t* sel,
                          int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse, hipStream_t s);
 // k_attend.hip
-int attend_splits(int uni_stride);
 hipError_t launch_attend(const DevLayout& L, const void* blob, const void* Q, const int32_t* uni,
                          const int32_t* n_uni, int uni_stride, float scale, float* O, float* lse, void* ws,
                          hipStream_t s);

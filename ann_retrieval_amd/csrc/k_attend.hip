@@ -312,8 +312,6 @@ __global__ __launch_bounds__(256) void k_gather_v(DevLayout L, const void* blob,
 
 }  // namespace
 
-int attend_splits(int) { return 0; }
-
 hipError_t launch_gather_v(const DevLayout& L, const void* blob, const int32_t* uni, const int32_t* n_uni,
                            int uni_stride, hipStream_t s) {
   if (!L.vpool || !L.vstage) return hipErrorInvalidValue;

@@ -496,11 +496,15 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 
 template <int D, class T>
 hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const void* Kv, const void* Vv,
-                       int n, int64_t hstride, void* ws, bool keep, hipStream_t s, const PdciArgs* pd) {
+                       int n, int64_t hstride, void* ws, bool keep, hipStream_t s, const PdciArgs* pd,
+                       hipEvent_t* ev) {
   const T* K = static_cast<const T*>(Kv);
   const T* V = static_cast<const T*>(Vv);
   const unsigned H = (unsigned)L.H;
   hipError_t err;
+  // phase boundaries (ICE_BUILD_PHASES + 1 events when timed)
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+  if ((err = mark(0))) return err;
 #define ICE_CHECK()                                  \
   do {                                               \
     if ((err = hipGetLastError()) != hipSuccess) return err; \
@@ -528,19 +532,25 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
   }
   k_lift_compact<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
   ICE_CHECK();
+  if ((err = mark(1))) return err;
   const int last = L.L >= 2 ? L.L - 2 : 0;
   for (int level = 0; level <= last; ++level) {
     const int npts = L.ncap[level];
     if (L.L >= 2 && n > 0) {
       if (pd) {
+        if ((err = mark(2 + 4 * level))) return err;
         if ((err = launch_parent_pdci(L, W, *pd, blob, Kv, hstride, ws, level, s))) return err;
       } else {
         k_gather_opA<D, T><<<dim3(blocks_for((int64_t)L.ncap[level + 1] * W.kp, 256 * 8), H), 256, 0, s>>>(
             L, W, blob, K, hstride, ws, level);
         ICE_CHECK();
+        if ((err = mark(2 + 4 * level))) return err;
         if ((err = launch_parent_gemm(L, W, blob, Kv, hstride, ws, level, s))) return err;
       }
+    } else if ((err = mark(2 + 4 * level))) {
+      return err;
     }
+    if ((err = mark(3 + 4 * level))) return err;
     const int nown = (L.L >= 2 ? L.ncap[level + 1] : 0) + 1;
     if ((err = launch_fill_heads(ws, W.head_bytes, L.H, W.off_cnt, nown, 0, s))) return err;
     if (n > 0) {
@@ -554,6 +564,9 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
       ICE_CHECK();
       k_pack_place<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
       ICE_CHECK();
+    }
+    if ((err = mark(4 + 4 * level))) return err;
+    if (n > 0) {
       using G = RowGeo<D, T>;
       k_copy_pages<D, T><<<dim3(blocks_for((int64_t)L.pcap[level] * ICE_PAGE_CAP, 4 * G::RPP * 8), H), 256, 0,
                            s>>>(L, K, hstride, blob, level);
@@ -563,12 +576,17 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
         ICE_CHECK();
       }
     }
+    if ((err = mark(5 + 4 * level))) return err;
   }
+  for (int level = last + 1; level < ICE_MAX_LEVELS - 1; ++level)
+    for (int i = 2; i < 6; ++i)
+      if ((err = mark(i + 4 * level))) return err;
   if (L.L >= 2 && n > 0) {
     using G = RowGeo<D, T>;
     k_copy_top<D, T><<<dim3(blocks_for(L.topcap, 4 * G::RPP * 4), H), 256, 0, s>>>(L, K, hstride, blob);
     ICE_CHECK();
   }
+  if ((err = mark(ICE_BUILD_PHASES))) return err;
 #undef ICE_CHECK
   return hipSuccess;
 }
@@ -666,13 +684,14 @@ hipError_t launch_build_reuse(const DevLayout& L, const WsLayout& W, void* blob,
 }
 
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
-                        int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s, const PdciArgs* pd) {
+                        int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s, const PdciArgs* pd,
+                        hipEvent_t* ev) {
   if (L.dtype == ICE_BF16) {
-    if (L.d == 128) return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd);
-    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd);
+    if (L.d == 128) return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev);
+    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev);
   }
-  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd);
-  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd);
+  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev);
+  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev);
 }
 
 }  // namespace ice

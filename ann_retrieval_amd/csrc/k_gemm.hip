@@ -14,8 +14,9 @@
 // children the columns (B operand, kept in registers for the whole sweep: two
 // 32-child fragments per wave, whose MFMA chains interleave). Each lane then
 // owns one child column per fragment and 16 parent rows of every 32-row
-// block, so the argmax runs inside the lane's accumulators (4 VALU operations
-// per score) with one cross-lane step at the end. The
+// block, so the argmax runs inside the lane's accumulators (a v_max3 fold per
+// 32-row block, and a copy of the block's scores when it holds a new best)
+// with one cross-lane step at the end. The
 // e_i e_j term rides in one extra k-step: e is split into three bf16 parts
 // and six of the products are laid out as extra columns (the dropped terms
 // are below 2^-24 relative).
@@ -98,24 +99,45 @@ __device__ inline void write_parent(const DevLayout& L, const WsLayout& W, const
   if (a.second > -INFINITY && (a.best - a.second) < 1e-4f * (M2 - a.second)) atomicAdd(&v.hdr->near_ties, 1);
 }
 
-// Running best / runner-up of one lane over its rows of one child column,
-// branch-free: the runner-up is the median of (best, runner-up, s), the best
-// and its position move together on a strict comparison (rows arrive in
-// increasing order, so equal scores keep the lowest row). The position is
-// kept as (32-row block, accumulator j): j is a constant per score, and the
-// block is recorded once per block if any of its scores moved the best. The
-// lane's own row offset is added at the end.
+// Running best / runner-up of one lane over its rows of one child column, by
+// 32-row blocks (16 scores per lane and block). Per block: the block's max
+// by a v_max3 chain; if it beats the running best (strict, so equal scores
+// keep the earlier block, i.e. the lower rows), the block's 16 scores are
+// kept and the block recorded; `second` tracks the best of every other
+// block's max (v_med3 of the old best, itself and the block max). At the end
+// the kept block gives the winning row (its first score equal to the best:
+// rows increase with the accumulator index) and its own runner-up, so best,
+// row and runner-up equal a score-by-score scan of the lane's rows.
 struct LaneMax {
   float best = -INFINITY, second = -INFINITY;
-  int j = 0, blk = -1;
-  __device__ inline bool push(float s, int jj) {
-    const bool gt = s > best;
-    second = __builtin_amdgcn_fmed3f(best, second, s);
-    best = gt ? s : best;
-    j = gt ? jj : j;
-    return gt;
+  int blk = -1;
+  float kept[16];
+  __device__ inline void push_block(const float (&s)[16], int b) {
+    float bm = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+    for (int j = 3; j < 15; j += 2) bm = fmaxf(fmaxf(bm, s[j]), s[j + 1]);
+    bm = fmaxf(bm, s[15]);
+    const bool gt = bm > best;
+    second = __builtin_amdgcn_fmed3f(best, second, bm);
+    best = gt ? bm : best;
+    blk = gt ? b : blk;
+    if (gt) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) kept[j] = s[j];
+    }
   }
-  __device__ inline int row() const { return blk < 0 ? -1 : blk * 32 + 8 * (j >> 2) + (j & 3); }
+  // winning accumulator index j (first one equal to the best) and the
+  // runner-up over all the lane's scores
+  __device__ inline int finish(float& runner_up) const {
+    int jb = 15;
+#pragma unroll
+    for (int j = 14; j >= 0; --j) jb = kept[j] == best ? j : jb;
+    float r = second;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r = j == jb ? r : fmaxf(r, kept[j]);
+    runner_up = r;
+    return jb;
+  }
 };
 
 template <int D>
@@ -218,27 +240,21 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
         for (int f = 0; f < NF; ++f)
           acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bfr[f][ks], acc[f], 0, 0, 0);
       }
-      // accumulator j of a lane is row 8 (j/4) + 4 half + j%4 of the block
+      // accumulator j of a lane is row 8 (j/4) + 4 half + j%4 of the block;
+      // rows past the candidates (last stage only) score -inf
       const int rbase = p0 + rb * 32;
-      bool moved[NF];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) moved[f] = false;
-      if (full) {
+      for (int f = 0; f < NF; ++f) {
+        float sc[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < 16; ++j) sc[j] = acc[f][j];
+        if (!full) {
 #pragma unroll
-          for (int f = 0; f < NF; ++f) moved[f] |= am[f].push(acc[f][j], j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const bool ok = rbase + 8 * (j >> 2) + 4 * half + (j & 3) < v.n_cand;
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            if (ok) moved[f] |= am[f].push(acc[f][j], j);
+          for (int j = 0; j < 16; ++j)
+            sc[j] = rbase + 8 * (j >> 2) + 4 * half + (j & 3) < v.n_cand ? sc[j] : -INFINITY;
         }
+        am[f].push_block(sc, rbase / 32);
       }
-#pragma unroll
-      for (int f = 0; f < NF; ++f) am[f].blk = moved[f] ? rbase / 32 : am[f].blk;
     }
     stash(nxt, pf);
     __syncthreads();
@@ -258,9 +274,11 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     ArgMax a;
+    float ru;
+    const int j = am[f].finish(ru);
     a.best = am[f].best;
-    a.second = am[f].second;
-    a.idx = am[f].row() >= 0 ? am[f].row() + 4 * half : 0x7fffffff;
+    a.second = ru;
+    a.idx = am[f].blk >= 0 ? am[f].blk * 32 + 8 * (j >> 2) + (j & 3) + 4 * half : 0x7fffffff;
     a.merge_halves();
     if (lane < 32 && cvalid[f]) write_parent(L, W, v, blob, level, ctok[f], a);
   }

@@ -388,9 +388,15 @@ __global__ __launch_bounds__(kInsertWaves * 64) void k_insert(DevLayout L, void*
         else if (lam == l) ok &= place_token(L, hb, hdr, l, p, t, plc.page[l], plc.slot[l]);
       }
       if (Ltop >= 1 && lam == Ltop) {
-        plc.top_slot = hdr->n_top;
-        at<int32_t>(hb, L.off_top_tok)[hdr->n_top] = t;
-        hdr->n_top += 1;
+        // the top list is sized for every promoted position; the host rejects
+        // inserts that could outgrow it, and a full list is flagged, not written past
+        if (hdr->n_top < L.topcap) {
+          plc.top_slot = hdr->n_top;
+          at<int32_t>(hb, L.off_top_tok)[hdr->n_top] = t;
+          hdr->n_top += 1;
+        } else {
+          ok = false;
+        }
       }
       for (int l = 0; l < Ltop; ++l) {
         int32_t* par = at<int32_t>(hb, L.off_parent[l]);

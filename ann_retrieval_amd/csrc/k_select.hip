@@ -615,9 +615,10 @@ struct ClaimLds {
 // area) receives a copy of the union. Ends with a block barrier, after which
 // the selection's LDS area is free. With `cl` (the fused decode step) it
 // writes no union: each query head's waves leave as soon as its lead has
-// claimed the query head's pages not yet claimed by another (cl->pages,
-// cl->count; the claim bits must be zero on entry), and the caller writes the
-// union with write_union after a block barrier.
+// claimed the query head's pages that no lower query head selected
+// (cl->pages, cl->count; the claim bits must be zero and the counts -1 on
+// entry), and the caller writes the union with write_union after a block
+// barrier.
 template <int D, class T, bool BIG>
 __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int budget, int beam, int32_t* sel,
                            int32_t* uni, int32_t* n_uni, int32_t* trace, char* smem, int h, int32_t* uni_lds,
@@ -868,9 +869,24 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
     combine(tl, kpg, -1, -1);
   }
   if (cl) {
-    // the query head's selected pages that no other query head of the group
-    // has claimed yet, in selection order: these its waves attend
+    // the query head's selected pages that no lower query head of the group
+    // selected, in selection order: these its waves attend. The lead first
+    // waits for query head g-1 to publish; that one waited for g-2, and so
+    // on, so the claim bits then hold exactly the lower query heads' pages
+    // and the claims do not depend on which query head finished first (a
+    // bounded wait: past kSpinLimit polls it counts a timeout and goes on).
     if (lead) {
+      if (g > 0) {
+        int spins = 0;
+        while (__atomic_load_n(&cl->count[g - 1], __ATOMIC_RELAXED) < 0) {
+          if (++spins > kSpinLimit) {
+            if (lane == 0) atomicAdd(timeouts, 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
       const int p = lane < kpg ? sel_all[g * kpg + lane] : -1;
       const int pr = lane < kpg ? cl->sel_rows[g * kpg + lane] : 0;
       bool mine = false;
@@ -963,50 +979,61 @@ __global__ __launch_bounds__(1024) void k_decode(DevLayout L, const void* blob, 
   if (threadIdx.x == 0) *cl.done = *cl.next = 0;
   select_head<D, uint16_t, false>(L, blob, Q, budget, beam, sel, uni, n_uni, nullptr, smem, h, nullptr, &cl);
   // Attention: the claimed pages of all query heads, in query-head order,
-  // then the head's resident pages, are dealt out one at a time to whichever
-  // wave asks next, so waves whose query head finished its selection early
-  // take the pages of the later ones. A wave asks once its own selection has
-  // ended, and a claimed page waits for its query head to publish (a bounded
-  // wait: past kSpinLimit polls it counts a timeout and skips the page, so
-  // the kernel always ends).
+  // then the head's resident pages, form a list of items cut into at most nw
+  // chunks of consecutive items. The chunks are dealt out one at a time to
+  // whichever wave asks next, so waves whose query head finished its
+  // selection early take the chunks of the later ones. A wave attends its
+  // chunk's pages in list order into fresh sums and leaves them in the
+  // chunk's partial slot; the slots are merged in chunk order, so the result
+  // does not depend on which wave took which chunk (bitwise deterministic). A
+  // wave asks once its own selection has ended, and a claimed page waits for
+  // its query head to publish (a bounded wait: past kSpinLimit polls it
+  // counts a timeout and skips the page, so the kernel always ends).
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  (void)wv;
   const void* hb = head_base(blob, L, h);
   const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
   int* timeouts = const_cast<int*>(&hdr->sync_timeouts);
   const int n_pages = hdr->n_pages[0], n_res = hdr->n_resident;
   const int n_claim = G * kpg, n_items = n_claim + (n_res + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP;
-  mfma_attend::WaveAcc<D> st;
-  st.init();
+  const int cs = max(1, (n_items + nw - 1) / nw);        // items per chunk
+  const int n_chunks = (n_items + cs - 1) / cs;          // <= nw partial slots
   for (;;) {
-    int i = 0;
-    if (lane == 0) i = atomicAdd(cl.next, 1);
-    i = __builtin_amdgcn_readfirstlane(__shfl(i, 0, 64));
-    if (i >= n_items) break;
-    if (i >= n_claim) {     // a resident page: nothing to wait for
-      const int r = i - n_claim;
-      mfma_attend::attend_one<D>(L, hb, h, L.pcap[0] + L.res_pages, L.pcap[0] + r,
-                                 min(ICE_PAGE_CAP, n_res - ICE_PAGE_CAP * r), scale * mfma_attend::kLog2e, part, st);
-      continue;
-    }
-    const int gq = i / kpg;
-    int spins = 0;
-    bool ok = true;
-    while (__atomic_load_n(&cl.count[gq], __ATOMIC_RELAXED) < 0) {
-      if (++spins > kSpinLimit) {
-        if (lane == 0) atomicAdd(timeouts, 1);
-        ok = false;
-        break;
+    int c = 0;
+    if (lane == 0) c = atomicAdd(cl.next, 1);
+    c = __builtin_amdgcn_readfirstlane(__shfl(c, 0, 64));
+    if (c >= n_chunks) break;
+    mfma_attend::WaveAcc<D> st;
+    st.init();
+    const int i1 = min(n_items, (c + 1) * cs);
+    for (int i = c * cs; i < i1; ++i) {
+      if (i >= n_claim) {     // a resident page: nothing to wait for
+        const int r = i - n_claim;
+        mfma_attend::attend_one<D>(L, hb, h, L.pcap[0] + L.res_pages, L.pcap[0] + r,
+                                   min(ICE_PAGE_CAP, n_res - ICE_PAGE_CAP * r), scale * mfma_attend::kLog2e, part, st);
+        continue;
       }
-      __builtin_amdgcn_s_sleep(1);
+      const int gq = i / kpg;
+      int spins = 0;
+      bool ok = true;
+      while (__atomic_load_n(&cl.count[gq], __ATOMIC_RELAXED) < 0) {
+        if (++spins > kSpinLimit) {
+          if (lane == 0) atomicAdd(timeouts, 1);
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // the page id and rows: the same LDS words in every lane
+      const int pg = __builtin_amdgcn_readfirstlane(cl.pages[i]), n = __builtin_amdgcn_readfirstlane(cl.rows[i]);
+      if (ok && pg >= 0) mfma_attend::attend_one<D>(L, hb, h, n_pages, pg, n, scale * mfma_attend::kLog2e, part, st);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // the page id and rows: the same LDS words in every lane
-    const int pg = __builtin_amdgcn_readfirstlane(cl.pages[i]), n = __builtin_amdgcn_readfirstlane(cl.rows[i]);
-    if (ok && pg >= 0) mfma_attend::attend_one<D>(L, hb, h, n_pages, pg, n, scale * mfma_attend::kLog2e, part, st);
+    mfma_attend::write_partial<D>(st, c, G, part, nw);
   }
-  mfma_attend::write_partial<D>(st, wv, G, part, nw);
   __syncthreads();
-  mfma_attend::merge_partials<D>(G, part, nw, O + (int64_t)h * G * D, lse ? lse + (int64_t)h * G : nullptr);
+  mfma_attend::merge_partials<D>(G, part, nw, O + (int64_t)h * G * D, lse ? lse + (int64_t)h * G : nullptr,
+                                 n_chunks);
   // a union too long for one wave: written by the block from the selections
   // (the selection's LDS is untouched by the attention)
   if (G * kpg > 64) {

@@ -141,6 +141,29 @@ int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes
 int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
               void* ws, size_t ws_bytes, void* stream);
 
+/* ice_build, with the time of each build phase measured by events recorded
+ * on `stream` between the phases' kernels; waits for `stream` to reach the
+ * end of the build. phase_ms: host, ICE_BUILD_PHASES floats, in ms:
+ *   ICE_PHASE_LIFT                    header reset, key norms, promotion
+ *                                     levels, lift and level lists;
+ *   ICE_PHASE_OPERAND + 4 l           candidate-parent operand of level l;
+ *   ICE_PHASE_PARENT + 4 l            nearest-parent search of level l (the
+ *                                     distance GEMM with its argmax);
+ *   ICE_PHASE_PACK + 4 l              page pack of level l;
+ *   ICE_PHASE_COPY + 4 l              page-pool copies of level l;
+ *   ICE_PHASE_TOP                     top-list copy;
+ * for l = 0 .. ICE_MAX_LEVELS - 2 (levels that do not exist take 0 ms).
+ * Everything else is as in ice_build. */
+#define ICE_BUILD_PHASES  14
+#define ICE_PHASE_LIFT     0
+#define ICE_PHASE_OPERAND  1
+#define ICE_PHASE_PARENT   2
+#define ICE_PHASE_PACK     3
+#define ICE_PHASE_COPY     4
+#define ICE_PHASE_TOP     13
+int ice_build_timed(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
+                    void* ws, size_t ws_bytes, void* stream, float* phase_ms);
+
 /* ice_build with parents found by Prioritized DCI instead of the exact
  * search (the notes' key design 2: M-DCI sits on P-DCI; the article's
  * section 3 names it as the prior work; composite and simple indices as in
@@ -186,7 +209,11 @@ int ice_build_heads(ice_index* idx, const void* K, const void* V, int32_t n_toke
  * lift their own keys (M and e). Their selection then scores their own keys
  * inside the shared structure. n_tokens must equal the source heads' count;
  * the ranges must not overlap. No parent search runs, so it costs copies
- * only. Later inserts into these heads follow their own promotion draws. */
+ * only. Later inserts into these heads follow their own promotion draws; an
+ * insert that would give such a head more points at some level than its
+ * tables were sized for (they are sized from each head's own draws over the
+ * whole capacity) is refused with ICE_ERR_CAPACITY before anything is
+ * enqueued. */
 int ice_build_reuse(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
                     int32_t h0, int32_t n_heads, int32_t src_h0, void* ws, size_t ws_bytes, void* stream);
 
@@ -199,7 +226,8 @@ int ice_build_reuse(ice_index* idx, const void* K, const void* V, int32_t n_toke
  * its owner's last page, or to a newly split page if that one is full.
  * Tokens already placed keep their page and slot, except under
  * ICE_SPLIT_RESORT (see there). ICE_ERR_CAPACITY if the count would exceed
- * capacity (nothing is inserted). */
+ * capacity, or a head built by ice_build_reuse would outgrow its tables
+ * (nothing is inserted). */
 int ice_insert(ice_index* idx, const void* k_new, const void* v_new, int32_t n_new,
                void* ws, size_t ws_bytes, void* stream);
 
@@ -262,9 +290,10 @@ int ice_set_dense(ice_index* idx, const uint8_t* dense, void* stream);
  * fp32 sums in the attention. For bf16 keys with beam and budget/16 at most
  * 64 it runs as one kernel per step (each head selects, then attends its own
  * union, with no pass through memory in between); otherwise it enqueues the
- * two calls' kernels. The one-kernel step deals pages to its waves as they
- * become free, so its fp32 outputs may differ between runs in the last bits;
- * selections and unions are exact. */
+ * two calls' kernels. Either way two calls on the same index and queries
+ * give the same bits: the one-kernel step hands fixed chunks of the union to
+ * its waves as they become free and merges the chunks' partial sums in chunk
+ * order. */
 int ice_decode(const ice_index* idx, const void* Q, int32_t budget_tokens, int32_t beam,
                int32_t* sel, int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse,
                void* ws, size_t ws_bytes, void* stream);

@@ -269,6 +269,9 @@ class HeadIndex:
     clamps: int = 0
     splits: int = 0
     insert_ties: int = 0
+    # spare-capacity buffers behind the per-token arrays, so that a long run
+    # of inserts appends in amortised constant time (storage only)
+    _spare: dict = dataclasses.field(default_factory=dict, repr=False, compare=False)
 
     @property
     def n(self) -> int:
@@ -280,6 +283,19 @@ class HeadIndex:
 
     def X(self) -> np.ndarray:
         return lifted(self.K, self.e)
+
+    def _append(self, name: str, arr: np.ndarray, x) -> np.ndarray:
+        """``arr`` with ``x`` appended along axis 0, as a view of a buffer
+        with room to spare (the values are exactly those of np.append)."""
+        buf, view = self._spare.get(name, (None, None))
+        n = arr.shape[0]
+        if view is not arr or buf.shape[0] <= n:
+            buf = np.empty((max(2 * n, 64),) + arr.shape[1:], dtype=arr.dtype)
+            buf[:n] = arr
+        buf[n] = x
+        out = buf[:n + 1]
+        self._spare[name] = (buf, out)
+        return out
 
 
 def pack(lev: np.ndarray, L_top: int, parent: list, dist: list, page_cap: int):
@@ -455,7 +471,7 @@ def insert(idx: HeadIndex, k, v, lev_override: int | None = None, parent_overrid
     if lam < idx.L_top:
         cand = np.nonzero(idx.lev >= lam + 1)[0]
         if parent_override is None:
-            j, D1, D2 = nearest(x[None, :], idx.X()[cand])
+            j, D1, D2 = nearest(x[None, :], lifted(idx.K[cand], idx.e[cand]))
             p = int(cand[j[0]])
             if is_near_tie(D1, D2)[0]:
                 idx.insert_ties += 1
@@ -464,18 +480,18 @@ def insert(idx: HeadIndex, k, v, lev_override: int | None = None, parent_overrid
             p = int(parent_override)
             if idx.lev[p] < lam + 1:
                 raise ValueError("given parent is not a point of the next level")
-            dp = float(_sq_dist(x, idx.X()[p:p + 1])[0])
+            dp = float(_sq_dist(x, lifted(idx.K[p:p + 1], idx.e[p:p + 1]))[0])
     # grow token arrays
-    idx.K = np.vstack([idx.K, k[None, :]])
-    idx.V = np.vstack([idx.V, v[None, :]])
-    idx.n2 = np.append(idx.n2, float(np.dot(k, k)))
-    idx.e = np.append(idx.e, e_t)
-    idx.lev = np.append(idx.lev, lam)
+    idx.K = idx._append("K", idx.K, k)
+    idx.V = idx._append("V", idx.V, v)
+    idx.n2 = idx._append("n2", idx.n2, float(np.dot(k, k)))
+    idx.e = idx._append("e", idx.e, e_t)
+    idx.lev = idx._append("lev", idx.lev, lam)
     idx.clamps += int(clamped)
     for l in range(idx.L_top):
-        par = np.append(idx.parent[l], -1)
-        dst = np.append(idx.dist[l], np.nan)
-        sec = np.append(idx.second[l], np.inf)
+        par = idx._append(f"parent{l}", idx.parent[l], -1)
+        dst = idx._append(f"dist{l}", idx.dist[l], np.nan)
+        sec = idx._append(f"second{l}", idx.second[l], np.inf)
         if l < lam:
             par[t], dst[t] = t, 0.0
         elif l == lam:

@@ -179,3 +179,19 @@ def test_host_pool_sizes_and_checks(lib):
         assert lib.ice_build(hh, fake, fake, 10, 10 * d, fake, ws_bytes, None) == L.ICE_ERR_STATE
     finally:
         lib.ice_destroy(hh)
+
+
+def test_reuse_can_outgrow_tables_sized_from_own_draws():
+    """The sizing fact behind the reuse insert check: a head that takes its
+    source's levels for its first 2048 tokens and its own draws after them
+    can hold more level-1 points than any head's own draws over the whole
+    capacity (the tables are sized from those). Seed 1, 2 heads, 2 levels,
+    p = 1/16, capacity 4096: the reused head passes the 261-point bound at
+    token 3992, which the GPU test of reuse inserts relies on."""
+    cap, nb = 4096, 2048
+    l0 = ic.draw_levels(1, 0, 0, cap, 2, 4)
+    l1 = ic.draw_levels(1, 1, 0, cap, 2, 4)
+    ncap = max(int((l0 >= 1).sum()), int((l1 >= 1).sum()))
+    run = int((l0[:nb] >= 1).sum()) + np.cumsum(l1[nb:] >= 1)
+    assert ncap == 261
+    assert nb + int(np.nonzero(run > ncap)[0][0]) == 3992

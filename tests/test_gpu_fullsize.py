@@ -114,13 +114,21 @@ def test_llama_layer_decode_with_inserts():
     say("llama layer: inserts replayed, layouts equal")
 
 
+# Smallest beam at which query head 0 of every KV head finds a needle page at
+# every depth of the needle workload (budget 64, seed 0). At beam = k = 4 it
+# finds one in 21 of the 40 (depth, head) cases; the needle's level-1 owner
+# often hangs under a top-level point that q ranks below the first few.
+NEEDLE_BEAM = 64
+
+
 @pytest.mark.parametrize("depth", [0.1, 0.3, 0.5, 0.7, 0.9])
 def test_needle_100k(depth):
     """Needle workload: 8 KV heads x 4 query heads, 100,000 tokens, d=128
     bf16, 1024-component background, a 16-token span with cosine 0.9 to query
     head 0's query, budget 64. Head 0 is checked against the oracle at depth
-    0.5; at every depth the coverage of the needle by query head 0's pages is
-    reported, with the smallest beam that reaches it."""
+    0.5 (beam 4) and at beam NEEDLE_BEAM; at every depth, query head 0 of every
+    KV head selects a page holding needle tokens at beam NEEDLE_BEAM, and the
+    coverage at beam 4 is reported."""
     H, G, N, d = 8, 4, 100000, 128
     say(f"needle depth={depth} H={H} N={N}")
     w, Q, start = synth.needle_workload(H, G, N, d, 1024, depth, seed=0, device=DEV)
@@ -129,33 +137,34 @@ def test_needle_100k(depth):
     torch.cuda.synchronize()
     out = run_decode(ix, Q, 64, 4)
     check_all_heads(ix, out)
+    wide = run_decode(ix, Q, 64, NEEDLE_BEAM)
+    check_all_heads(ix, wide)
     if depth == 0.5:
         refs = check_build(w, ix, [0], 0, 3, 4)
         compare_decode(ix, refs, out)
+        compare_decode(ix, refs, wide)
     needle = set(range(start, start + 16))
     covered = []
     for h in range(H):
         tok = ix.export(h, L.ICE_EXP_PAGE_TOK, 0).reshape(-1, 16)
-        hit = {int(t) for p in out["sel"][h, 0] if p >= 0 for t in tok[p] if t in needle}
-        first_beam = None
-        for beam in (4, 8, 16, 32, 64, 128, 256):
-            sel = ix.ice_select(Q, 64, beam)[0].cpu().numpy()
-            if any(t in needle for p in sel[h, 0] if p >= 0 for t in tok[p]):
-                first_beam = beam
-                break
-        covered.append((len(hit), first_beam))
-    say(f"needle depth={depth}: tokens covered per head (beam 4) and smallest beam reaching it: {covered}")
+        hit4 = {int(t) for p in out["sel"][h, 0] if p >= 0 for t in tok[p] if t in needle}
+        hitw = {int(t) for p in wide["sel"][h, 0] if p >= 0 for t in tok[p] if t in needle}
+        covered.append((len(hit4), len(hitw)))
+        assert hitw, f"depth {depth} head {h}: no needle page at beam {NEEDLE_BEAM}"
+    say(f"needle depth={depth}: needle tokens covered per head at beam 4 / beam {NEEDLE_BEAM}: {covered}")
 
 
 def test_qwen_shaped_long_generation():
     """Qwen3-32B-shaped long generation: 512 heads (64 layers x 8 KV heads),
-    8 query heads each, 8,192-token prompt, 4,096 steps of select + attend at
-    budget 256 then one insert per head, queries and new keys walking between
-    mixture centres so pages split. Heads 0 and 300 are replayed by the oracle
-    through step 1,023 with decode checks at steps 0, 512 and 1,023; every head
-    is checked for structure and counts after all 4,096 steps."""
+    8 query heads each, 8,192-token prompt, 4,096 steps of the fused decode
+    step (ice_decode: select + attend, unions of up to 128 pages) at budget
+    256, then one insert per head, queries and new keys walking between
+    mixture centres so pages split. Heads 0 and 300 are replayed by the
+    oracle through all 4,096 inserts, with decode checks (against ice_select +
+    ice_attend and against the oracle) at steps 0, 1,024, 2,048, 3,072 and
+    4,095; every head is checked for structure and counts at the end."""
     H, G, N, d, C = 512, 8, 8192, 128, 512
-    steps, replayed, checks = 4096, 1024, (0, 512, 1023)
+    steps, checks = 4096, (0, 1024, 2048, 3072, 4095)
     say(f"qwen-shaped H={H} G={G} N={N} + {steps} steps")
     w, gen = synth.clustered_kv(H, N, d, C, "bf16", 0, device=DEV)
     ix = IceIndex(H, G, d, "bf16", N + steps, seed=0, max_budget=256, device=DEV)
@@ -165,31 +174,36 @@ def test_qwen_shaped_long_generation():
     refs = check_build(w, ix, heads, 0, 3, 4)
     walk = synth.QueryWalk(w, G, gen, device=DEV)
     outs, ks, vs = {}, [], []
+    long_union = False
     for s in range(steps):
         Q, k, v = walk.step()
         if s in checks:
-            outs[s] = run_decode(ix, Q, 256, 16)
+            # the oracle follows later, once it has replayed the inserts before step s
+            outs[s] = gs.decode_against_select_attend(ix, {}, Q, 256, 16, f"step {s}")
             check_all_heads(ix, outs[s])
+            long_union |= int(outs[s]["nuni"].max()) > 64
         else:
-            _, uni, nuni = ix.ice_select(Q, 256, 16)
-            ix.ice_attend(Q, uni, nuni)
+            ix.ice_decode(Q, 256, 16)
         ix.ice_insert(k, v)
-        if s < replayed:
-            ks.append(k[heads].cpu())
-            vs.append(v[heads].cpu())
+        ks.append(k[heads].cpu())
+        vs.append(v[heads].cpu())
         if s % 1024 == 1023:
             torch.cuda.synchronize()
             say(f"step {s + 1} of {steps}")
     torch.cuda.synchronize()
+    assert long_union, "the workload must reach the fused step's long-union path"
     Kn, Vn = torch.cat(ks, 1), torch.cat(vs, 1)
     for i, h in enumerate(heads):
         g = gs.read_head(ix, h)
         ref = refs[h]
-        for s in range(replayed):
+        for s in range(steps):
             if s in checks:
                 compare_decode(ix, {h: ref}, outs[s])
             gs.replay_inserts(ref, g, Kn[i, s:s + 1], Vn[i, s:s + 1], h, 0, 3, 4)
-        say(f"head {h}: {replayed} inserts replayed, {ref.splits} splits")
+        gs.check_table_structure(g, ix.capacity)
+        gs.compare_layout(ref, g, ix.capacity)
+        assert g.stats["splits"] == ref.splits and g.stats["clamps"] == ref.clamps
+        say(f"head {h}: {steps} inserts replayed, {ref.splits} splits")
     splits = 0
     for h in range(H):
         st = ix.stats(h)
@@ -197,7 +211,6 @@ def test_qwen_shaped_long_generation():
         splits += st["splits"]
     for h in heads:
         g = gs.read_head(ix, h)
-        gs.check_table_structure(g, ix.capacity)
         members = sorted(t for p in g.tables[0]["pages"] for t in p)
         assert members == list(range(N + steps)), "every token in exactly one page"
     assert splits > 0

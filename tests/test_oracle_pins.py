@@ -317,6 +317,110 @@ def test_insert_into_empty_index_and_clamp():
 
 
 # --------------------------------------------------------------------------
+# replay entry points: a given parent instead of the search's own choice
+# --------------------------------------------------------------------------
+# The GPU parity tests hand the oracle the GPU's parent wherever the two best
+# parents are near-tied (build_head(parents=...), insert(parent_override=...)).
+# These pins fix what those two paths compute: a hand-worked case where the
+# given parent is the runner-up, and the identity with the free search when
+# the given parents are the search's own.
+
+def _replay_case():
+    c = _golden("replay_case.json")
+    K = np.array(c["keys"], dtype=np.float64)
+    return c, K
+
+
+def _num(x):
+    return np.inf if x == "inf" else float(x)
+
+
+def check_replay_golden():
+    c, K = _replay_case()
+    lev = np.array(c["levels"])
+    cap = c["page_cap"]
+    ok = True
+    free = ic.build_head(K, K, 0, 0, lev=lev, page_cap=cap)
+    f = c["free"]
+    ok &= free.parent[0].tolist() == f["parent0"]
+    ok &= np.allclose(free.dist[0], f["dist0"], rtol=0, atol=1e-9)
+    ok &= np.allclose(free.second[0], [_num(x) for x in f["second0"]], rtol=0, atol=1e-9)
+    ok &= free.pages == f["pages"] and {str(k): v for k, v in free.owner_pages.items()} == f["owner_pages"]
+    fb = c["forced_build"]
+    forced = ic.build_head(K, K, 0, 0, lev=lev, page_cap=cap, parents=[np.array(fb["parents0"])])
+    ok &= forced.parent[0].tolist() == fb["parent0"]
+    ok &= np.allclose(forced.dist[0], fb["dist0"], rtol=0, atol=1e-9)
+    ok &= forced.pages == fb["pages"] and {str(k): v for k, v in forced.owner_pages.items()} == fb["owner_pages"]
+    ins = c["insert"]
+    for mode, override in (("free", None), ("forced", ins["forced"]["parent"])):
+        idx = ic.build_head(K, K, 0, 0, lev=lev, page_cap=cap)
+        lam, p = ic.insert(idx, np.array(ins["key"], np.float64), np.zeros(2), lev_override=ins["level"],
+                           parent_override=override)
+        w = ins[mode]
+        ok &= lam == ins["level"] and p == w["parent"] and abs(idx.dist[0][5] - w["dist"]) <= 1e-9
+        ok &= idx.pages == w["pages"] and {str(k): v for k, v in idx.owner_pages.items()} == w["owner_pages"]
+        ok &= idx.splits == w["splits"]
+    return bool(ok)
+
+
+def test_replay_hand_case_runner_up():
+    assert check_replay_golden()
+
+
+def test_replay_build_with_own_parents_is_the_free_build():
+    for n, d, c, seed, levels in [(1500, 8, 16, 21, 3), (700, 4, 40, 22, 4), (300, 16, 5, 23, 2)]:
+        K, V, _ = _clustered(n, d, c, seed)
+        free = ic.build_head(K, V, 3, seed, levels)
+        given = [free.parent[l].copy() for l in range(free.L_top)]
+        rep = ic.build_head(K, V, 3, seed, levels, parents=given)
+        assert rep.pages == free.pages and rep.page_owner == free.page_owner
+        assert rep.owner_pages == free.owner_pages and rep.children == free.children and rep.top == free.top
+        for l in range(free.L_top):
+            assert np.array_equal(rep.parent[l], free.parent[l])
+            # the replay recomputes D as a direct sum of squares, as the free search does
+            m = free.parent[l] >= 0
+            assert np.array_equal(rep.dist[l][m], free.dist[l][m])
+
+
+def test_replay_insert_with_own_choice_is_the_free_insert():
+    K, V, cent = _clustered(1500, 8, 16, 24)
+    a = ic.build_head(K, V, 2, 24)
+    b = ic.build_head(K, V, 2, 24)
+    r = _rng(25)
+    for step in range(400):
+        k = cent[r.integers(0, len(cent))] + 0.3 * r.standard_normal(8)
+        v = r.standard_normal(8)
+        lam, p = ic.insert(a, k, v)
+        lam_b, p_b = ic.insert(b, k, v, parent_override=p)
+        assert (lam, p) == (lam_b, p_b)
+    assert a.pages == b.pages and a.owner_pages == b.owner_pages and a.top == b.top
+    assert a.children == b.children and a.splits == b.splits and a.splits > 0
+    for l in range(a.L_top):
+        assert np.array_equal(a.parent[l], b.parent[l])
+        m = a.parent[l] >= 0
+        assert np.array_equal(a.dist[l][m], b.dist[l][m])
+
+
+def test_planted_replay_ignoring_the_given_parent_is_caught(monkeypatch):
+    # a replay that silently keeps the search's own parent fails the hand case
+    real = ic.build_head
+
+    def ignoring(K, V, head, seed, levels=3, promote_log2=4, page_cap=16, lev=None, parents=None, pdci=None):
+        return real(K, V, head, seed, levels, promote_log2, page_cap, lev=lev, parents=None, pdci=pdci)
+    monkeypatch.setattr(ic, "build_head", ignoring)
+    assert not check_replay_golden()
+
+
+def test_planted_insert_ignoring_the_override_is_caught(monkeypatch):
+    real = ic.insert
+
+    def ignoring(idx, k, v, lev_override=None, parent_override=None, resplit=False):
+        return real(idx, k, v, lev_override=lev_override, parent_override=None, resplit=resplit)
+    monkeypatch.setattr(ic, "insert", ignoring)
+    assert not check_replay_golden()
+
+
+# --------------------------------------------------------------------------
 # insert with the re-sort split
 # --------------------------------------------------------------------------
 
