@@ -21,6 +21,7 @@ ICE_F32, ICE_BF16 = 0, 1
 ICE_HOST_POOL, ICE_SPLIT_RESORT, ICE_RESPLIT_MAX = 1, 2, 1024
 ICE_PDCI_MAX_KEYS, ICE_PDCI_MAX_L = 16, 4
 ICE_PAGE_CAP, ICE_MAX_LEVELS, ICE_MAX_GROUP, ICE_MAX_BEAM, ICE_MAX_RESIDENT = 16, 4, 16, 256, 4096
+ICE_NOALLOC_SCRATCH_BYTES = 64 << 20
 ICE_BUILD_PHASES, ICE_PHASE_LIFT, ICE_PHASE_OPERAND, ICE_PHASE_PARENT, ICE_PHASE_PACK, ICE_PHASE_COPY, ICE_PHASE_TOP = \
     14, 0, 1, 2, 3, 4, 13
 (ICE_EXP_LEVEL, ICE_EXP_LIFT, ICE_EXP_PARENT, ICE_EXP_PAGE_TOK, ICE_EXP_PAGE_CNT, ICE_EXP_PAGE_NEXT,
@@ -48,6 +49,7 @@ _SIGNATURES = {
     "ice_host_pool_bytes": (c_size, [ctypes.POINTER(IceParams)]),
     "ice_attach_host_pool": (ctypes.c_int, [c_void_p, c_void_p, c_size]),
     "ice_build": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p, c_size, c_void_p]),
+    "ice_build_noalloc": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p]),
     "ice_build_timed": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p, c_size, c_void_p,
                                        c_void_p]),
     "ice_build_pdci": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i64, c_void_p, c_i32, c_i32, c_i32, c_i32,

@@ -143,6 +143,16 @@ class IceIndex:
         check(self.lib.ice_build(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0), _ptr(self.ws),
                                  self.ws_bytes, _stream_ptr(self.device)), "ice_build")
 
+    def ice_build_noalloc(self, K: torch.Tensor, V: torch.Tensor) -> None:
+        """ice_build with the library's fixed device scratch instead of this object's workspace (allocates
+        nothing; see include/ice.h)."""
+        self._check_kv(K, "K")
+        self._check_kv(V, "V")
+        if K.shape != V.shape or K.stride() != V.stride():
+            raise ValueError("K and V must have the same shape and strides")
+        check(self.lib.ice_build_noalloc(self.handle, _ptr(K), _ptr(V), K.shape[1], K.stride(0),
+                                         _stream_ptr(self.device)), "ice_build_noalloc")
+
     def ice_build_timed(self, K: torch.Tensor, V: torch.Tensor) -> np.ndarray:
         """ice_build with per-phase times (ms, ICE_BUILD_PHASES entries; see include/ice.h), measured by events
         on the current stream; waits for the build to finish."""

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <cstddef>
 #include <string>
@@ -14,6 +15,12 @@
 #include "ice_launch.h"
 
 using namespace ice;
+
+// Build scratch of ice_build_noalloc: a fixed array in every device's global
+// memory, loaded with the library and held until the process ends. In host
+// code `scratch` only names the symbol; its device address is looked up once
+// per device (hipGetSymbolAddress) and used in its place.
+static __device__ __align__(256) char scratch[ICE_NOALLOC_SCRATCH_BYTES];
 
 struct ice_index {
   ice_params p;
@@ -495,6 +502,49 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
               size_t ws_bytes, void* stream) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");
   return ice_build_heads(idx, K, V, n_tokens, head_stride, 0, idx->p.n_heads, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with it current) and kept for the process.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "ice_build_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ICE_ERR_ARG, "ice_build_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e, "ice_build_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return ICE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ice_build_noalloc(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
+                      void* stream) {
+  if (!idx) return fail(ICE_ERR_ARG, "index is null");
+  if (idx->W.build_bytes > (int64_t)ICE_NOALLOC_SCRATCH_BYTES)
+    return fail(ICE_ERR_CAPACITY, "ice_build_noalloc: the build needs %lld bytes of scratch, the library holds %lld",
+                (long long)idx->W.build_bytes, (long long)ICE_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  const int rc = scratch_address(&ptr);
+  if (rc != ICE_OK) return rc;
+  return ice_build_heads(idx, K, V, n_tokens, head_stride, 0, idx->p.n_heads, ptr, (size_t)ICE_NOALLOC_SCRATCH_BYTES,
+                         stream);
 }
 
 int ice_build_timed(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, void* ws,

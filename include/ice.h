@@ -141,6 +141,24 @@ int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes
 int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
               void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ice_build
+ * without a workspace argument. Its scratch is a fixed array of
+ * ICE_NOALLOC_SCRATCH_BYTES in each device's global memory, part of the
+ * loaded library and held until the process ends; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine). The device
+ * is the current one; its array's address is looked up on the first call on
+ * that device. ICE_ERR_CAPACITY (nothing enqueued) when the index's build
+ * needs more scratch than that, i.e. ice_workspace_bytes' build part: enough
+ * for one 32k-token layer of 8 KV heads (d = 128 bf16), not for all layers of
+ * a model at once. Every call on one device shares that device's array, so
+ * calls that overlap on one device (other streams, other indexes, other host
+ * threads) race; enqueue them on one stream. The build leaves nothing in the
+ * array that a later call relies on. Otherwise as ice_build. */
+#define ICE_NOALLOC_SCRATCH_BYTES 67108864  /* 64 MiB */
+int ice_build_noalloc(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
+                      void* stream);
+
 /* ice_build, with the time of each build phase measured by events recorded
  * on `stream` between the phases' kernels; waits for `stream` to reach the
  * end of the build. phase_ms: host, ICE_BUILD_PHASES floats, in ms:
