@@ -43,6 +43,9 @@ WORKLOADS = {
     "llama-layer": (8, 4, 32768, 128, "bf16", 512, False,
                     "one 32k-token layer, 8 KV heads x 4 query heads, d=128 bf16, 512-component mixtures"),
     "tiny": (1, 1, 2048, 64, "f32", 32, False, "1 head, 2048 tokens, d=64 fp32, 32-component mixture"),
+    "qwen-gen": (512, 8, 8192, 128, "bf16", 512, False,
+                 "8192-token prompt then generation, 64 layers x 8 KV heads x 8 query heads (Qwen3-32B shape), "
+                 "d=128 bf16, 512-component mixtures, queries and new keys walking between centres"),
 }
 
 
@@ -53,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ctx36k", choices=sorted(WORKLOADS))
     ap.add_argument("--budget", type=int, default=256)
-    ap.add_argument("--budgets", default="", help="extra budgets to time beside --budget, e.g. 64,128")
+    ap.add_argument("--budgets", default="64,128", help="extra budgets to time beside --budget")
     ap.add_argument("--builds", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle's timed sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -61,10 +64,16 @@ def parse():
     ap.add_argument("--no-pipeline", action="store_true", help="skip the per-layer build pipeline measurement")
     ap.add_argument("--resident", type=int, default=68,
                     help="resident (sink + window) tokens per head for the resident-token leg; 0 skips it")
-    ap.add_argument("--drift-steps", type=int, default=4096,
-                    help="generated steps of the split-reading recall comparison (0 skips it)")
-    ap.add_argument("--pdci-tokens", type=int, default=100000,
-                    help="context of the P-DCI against exact-parent comparison (0 skips it)")
+    ap.add_argument("--drift-steps", type=int, default=0,
+                    help="generated steps of the split-reading recall comparison (0 skips it; 4096 is the "
+                         "Qwen3-32B-shaped generation)")
+    ap.add_argument("--pdci-tokens", type=int, default=0,
+                    help="context of the P-DCI against exact-parent comparison (0 skips it; 100000 is the needle "
+                         "workload's context)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (Qwen3-32B-shaped generation, Llama layer, tiny, needle)")
+    ap.add_argument("--no-recall", action="store_true", help="skip the selection-recall table")
+    ap.add_argument("--recall-heads", type=int, default=64, help="heads in the selection-recall table")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="print a markdown summary of rocprofv3 output instead of benchmarking: one "
@@ -572,6 +581,262 @@ def cpu_baseline(w, Qs, budget, beam, heads, seed):
     return t_build, t_dec, threads
 
 
+def cpu_model():
+    """The host CPU's model string (Linux), else the platform's name."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def ev_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def decode_timing(ix, Qs, budget, steps, warmup, d, elt, G, separate=True):
+    """Whole decode steps (one ice_decode each) between two events, queued by
+    the host behind a short spin so the events bracket GPU work; then (if
+    `separate`) the same steps as ice_select alone and ice_attend alone; and
+    the algorithmic bytes of the run's own selections."""
+    import torch
+    beam = budget // 16
+    for s in range(warmup):
+        ix.ice_decode(Qs[s], budget, beam)
+        if separate:
+            _, uni, nuni = ix.ice_select(Qs[s], budget, beam)
+            ix.ice_attend(Qs[s], uni, nuni)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0, g1 = ev_pair()
+    torch.cuda._sleep(int(5e7))
+    g0.record()
+    for s in range(steps):
+        ix.ice_decode(Qs[warmup + s], budget, beam)
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = g0.elapsed_time(g1) / steps
+    r = dict(ms_per_step=ms_step, steps_per_s=1000.0 / ms_step, wall_s=wall)
+    nb = min(steps, 4)
+    byt = dict(select=0.0, attend=0.0, decode=0.0)
+    for s in range(nb):
+        _, uni, nuni, tr = ix.ice_select(Qs[warmup + s], budget, beam, trace=True)
+        bb = algorithmic_bytes(ix, tr.cpu().numpy(), uni.cpu().numpy(), nuni.cpu().numpy(), d, elt, G)
+        for k2 in byt:
+            byt[k2] += bb[k2] / nb
+    r.update(decode_bytes=byt["decode"], decode_gbs=byt["decode"] / ms_step / 1e6)
+    if separate:
+        unis = []
+        for s in range(steps):
+            _, uni, nuni = ix.ice_select(Qs[warmup + s], budget, beam)
+            unis.append((uni, nuni))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda._sleep(int(5e7))
+        e[0].record()
+        for s in range(steps):
+            ix.ice_select(Qs[warmup + s], budget, beam)
+        e[1].record()
+        torch.cuda._sleep(int(5e7))
+        e[2].record()
+        for s in range(steps):
+            ix.ice_attend(Qs[warmup + s], *unis[s])
+        e[3].record()
+        torch.cuda.synchronize()
+        sel_ms = e[0].elapsed_time(e[1]) / steps
+        att_ms = e[2].elapsed_time(e[3]) / steps
+        r.update(select_ms=sel_ms, attend_ms=att_ms, select_bytes=byt["select"], attend_bytes=byt["attend"],
+                 select_gbs=byt["select"] / sel_ms / 1e6, attend_gbs=byt["attend"] / att_ms / 1e6)
+    return r
+
+
+def build_timing(ix, w, builds):
+    """Median over `builds` timed builds (after one untimed) of the whole build
+    and of each phase (ice_build_timed: events on the build's stream)."""
+    import torch
+    ix.ice_build(w.K, w.V)
+    torch.cuda.synchronize()
+    runs = [ix.ice_build_timed(w.K, w.V) for _ in range(builds)]
+    ph = np.median(np.stack(runs), axis=0)
+    tot = float(np.median([x.sum() for x in runs]))
+    return tot, ph
+
+
+def parent_flops(ix, H, level, d):
+    """Algorithmic flops of the level-`level` parent search over all heads: two
+    per multiply-add of a d-dimensional key product, for every point of the
+    level that is not itself at the next level, against every point of the
+    next level."""
+    from ann_retrieval_amd import _lib as L
+    tot = 0
+    for h in range(H):
+        n = ix.stats(h)["n_tokens"]
+        lev = ix.export(h, L.ICE_EXP_LEVEL, np_dtype=np.int8)[:n]
+        n_l, n_up = int((lev >= level).sum()), int((lev >= level + 1).sum())
+        tot += 2 * (n_l - n_up) * n_up * d
+    return tot
+
+
+def recall_leg(ix, w, Qs, budgets, n_heads, G):
+    """Selection quality at each budget T (k = T/16 pages per query head), over
+    the first `n_heads` heads and a few decode queries: the share of each query
+    head's exact top-T keys by q.k that lie in its selected pages, for beams
+    k, 2k and 4k; for the best k semantic pages found by brute force (every
+    page scored by its best key, the limit of an unbounded beam); and for the
+    best k sequential 16-token pages (the layout the pages argue against)."""
+    import torch
+    from ann_retrieval_amd import _lib as L
+    dev = w.K.device
+    Kf = w.K[:n_heads].float()                                   # [h, N, d]
+    N = Kf.shape[1]
+    tok = [torch.from_numpy(ix.export(h, L.ICE_EXP_PAGE_TOK, 0).reshape(-1, 16)[:ix.stats(h)["n_pages"][0]]).to(dev)
+           .long() for h in range(n_heads)]
+    out = {}
+    for T in budgets:
+        k = T // 16
+        hits = {f"beam_{m}k": 0 for m in (1, 2, 4)}
+        hits.update(semantic_all_pages=0, sequential_pages=0)
+        total = 0
+        for Q in Qs:
+            S = torch.bmm(Q[:n_heads].float(), Kf.transpose(1, 2))   # [h, G, N]
+            top = torch.topk(S, T, dim=-1).indices                    # [h, G, T]
+            sels = {m: ix.ice_select(Q, T, min(m * k, L.ICE_MAX_BEAM))[0][:n_heads].long() for m in (1, 2, 4)}
+            seq_pad = torch.full((n_heads, G, (N + 15) // 16 * 16 - N), -float("inf"), device=dev)
+            seq_best = torch.cat([S, seq_pad], -1).reshape(n_heads, G, -1, 16).amax(-1)
+            seq_sel = torch.topk(seq_best, k, dim=-1).indices          # sequential page p = tokens 16p .. 16p+15
+            for h in range(n_heads):
+                tb = tok[h]
+                sc = torch.where(tb[None] >= 0, S[h][:, tb.clamp(min=0)], torch.tensor(-float("inf"), device=dev))
+                best = torch.topk(sc.amax(-1), min(k, tb.shape[0]), dim=-1).indices      # [G, k]
+                for g in range(G):
+                    want = top[h, g]
+                    for m in (1, 2, 4):
+                        pg = sels[m][h, g]
+                        st = tb[pg[pg >= 0]].reshape(-1)
+                        hits[f"beam_{m}k"] += int(torch.isin(want, st[st >= 0]).sum())
+                    st = tb[best[g]].reshape(-1)
+                    hits["semantic_all_pages"] += int(torch.isin(want, st[st >= 0]).sum())
+                    sq = (seq_sel[h, g][:, None] * 16 + torch.arange(16, device=dev)[None]).reshape(-1)
+                    hits["sequential_pages"] += int(torch.isin(want, sq[sq < N]).sum())
+                    total += T
+        out[str(T)] = {key: round(v / total, 4) for key, v in hits.items()}
+        print(f"[bench] recall T={T}: " + ", ".join(f"{key} {v:.3f}" for key, v in out[str(T)].items()),
+              file=sys.stderr, flush=True)
+    return {"heads": n_heads, "queries": len(Qs) * n_heads * G,
+            "definition": "share of each query head's exact top-T keys by q.k inside its k = T/16 pages", **out}
+
+
+def needle_leg(a):
+    """The needle workload (8 KV heads x 4 query heads, 100,000 tokens, d=128
+    bf16, 1024-component background, a 16-token span with cosine 0.9 to query
+    head 0's final query, budget 64) at five depths: for query head 0 of every
+    KV head, the needle tokens inside its selected pages at beam 4 (= k) and at
+    beam 64, the smallest beam whose pages hold a needle token, and the
+    attention weight query head 0 gives the needle tokens in its head's union
+    at beam 4."""
+    import torch
+    from ann_retrieval_amd import _lib as L
+    from ann_retrieval_amd import synth
+    from ann_retrieval_amd.api import IceIndex
+    H, G, N, d, T = 8, 4, 100000, 128, 64
+    out = {"workload": f"{N}-token context, {H} KV heads x {G} query heads, d=128 bf16, budget {T}", "depths": {}}
+    for depth in (0.1, 0.3, 0.5, 0.7, 0.9):
+        w, Q, start = synth.needle_workload(H, G, N, d, 1024, depth, seed=a.seed, device="cuda")
+        ix = IceIndex(H, G, d, "bf16", N, seed=a.seed, max_budget=T)
+        ix.ice_build(w.K, w.V)
+        _, uni, nuni, O, lse = ix.ice_decode(Q, T, 4)
+        sels = {b: ix.ice_select(Q, T, b)[0].cpu().numpy() for b in (4, 8, 16, 32, 64, 128, 256)}
+        torch.cuda.synchronize()
+        uni, nuni = uni.cpu().numpy(), nuni.cpu().numpy()
+        rows = []
+        for h in range(H):
+            tb = ix.export(h, L.ICE_EXP_PAGE_TOK, 0).reshape(-1, 16)
+            cov = {b: int(sum(1 for p in sels[b][h, 0] if p >= 0 for t in tb[p] if start <= t < start + 16))
+                   for b in sels}
+            first = next((b for b in sorted(sels) if cov[b] > 0), None)
+            toks = np.array([t for p in uni[h, :nuni[h]] for t in tb[p] if t >= 0])
+            lg = (w.K[h, toks].float() @ Q[h, 0].float()) / math.sqrt(d)
+            wt = torch.softmax(lg, 0).cpu().numpy()
+            mass = float(wt[(toks >= start) & (toks < start + 16)].sum())
+            rows.append({"covered_beam4": cov[4], "covered_beam64": cov[64], "smallest_beam": first,
+                         "attention_mass_beam4": round(mass, 4)})
+        hits4 = sum(r["covered_beam4"] > 0 for r in rows)
+        hits64 = sum(r["covered_beam64"] > 0 for r in rows)
+        out["depths"][str(depth)] = {"heads_hit_beam4": hits4, "heads_hit_beam64": hits64, "per_head": rows}
+        print(f"[bench] needle depth {depth}: query head 0 finds it in {hits4}/{H} heads at beam 4, {hits64}/{H} "
+              f"at beam 64; smallest beams {[r['smallest_beam'] for r in rows]}", file=sys.stderr, flush=True)
+        del ix, w
+        torch.cuda.empty_cache()
+    return out
+
+
+def workload_leg(name, a, steps, warmup, with_inserts):
+    """Build, decode steps (ice_decode at the workload's budgets) and one-token
+    inserts of one workload; for the long-generation shape the queries and
+    new keys walk between mixture centres (pages split)."""
+    import torch
+    from ann_retrieval_amd import synth
+    from ann_retrieval_amd.api import IceIndex
+    H, G, N, d, dtype, C, rotate, desc = WORKLOADS[name]
+    budgets = BUDGETS[name]
+    dev = torch.device("cuda", 0)
+    w, gen = synth.clustered_kv(H, N, d, C, dtype, a.seed, device=dev, rotate=rotate)
+    elt = 2 if dtype == "bf16" else 4
+    n_ins = steps + warmup if with_inserts else 0
+    ix = IceIndex(H, G, d, dtype, N + n_ins, seed=a.seed, max_budget=max(budgets), device=dev)
+    build_ms, ph = build_timing(ix, w, 3)
+    head_meta(ix, H, N + n_ins)
+    if name == "qwen-gen":
+        walk = synth.QueryWalk(w, G, gen, device=dev)
+        seq = [walk.step() for _ in range(warmup + steps)]
+        Qs = [x[0] for x in seq]
+        ins = [(x[1], x[2]) for x in seq]
+    else:
+        Qs = [synth.decode_queries(w, G, gen, device=dev) for _ in range(warmup + steps)]
+        ins = [synth.new_tokens(w, gen, device=dev) for _ in range(n_ins)]
+    res = {"workload": desc, "heads": H, "group": G, "context": N, "build_ms": build_ms,
+           "index_keys_per_s": H * N / (build_ms / 1000.0), "per_budget": {}}
+    for T in budgets:
+        r = decode_timing(ix, Qs, T, steps, warmup, d, elt, G, separate=False)
+        res["per_budget"][str(T)] = {k: round(v, 6) for k, v in r.items()}
+        print(f"[bench] {name} T={T}: {r['ms_per_step'] * 1000:.1f} us/step ({r['decode_gbs']:.0f} GB/s)",
+              file=sys.stderr, flush=True)
+    if with_inserts:
+        T = max(budgets)
+        # inserts alone, then whole steps of decode + insert, both queued behind a spin
+        e0, e1 = ev_pair()
+        torch.cuda._sleep(int(5e7))
+        e0.record()
+        for k_, v_ in ins[:warmup]:
+            ix.ice_insert(k_, v_)
+        e1.record()
+        torch.cuda.synchronize()
+        ins_ms = e0.elapsed_time(e1) / max(warmup, 1)
+        c0, c1 = ev_pair()
+        torch.cuda._sleep(int(5e7))
+        c0.record()
+        for s in range(steps):
+            ix.ice_decode(Qs[warmup + s], T, T // 16)
+            ix.ice_insert(*ins[warmup + s])
+        c1.record()
+        torch.cuda.synchronize()
+        comb_ms = c0.elapsed_time(c1) / steps
+        splits = sum(ix.stats(h)["splits"] for h in range(H))
+        res.update(insert_ms_per_step=ins_ms, decode_plus_insert_ms_per_step=comb_ms, splits=splits)
+        print(f"[bench] {name}: insert {ins_ms * 1000:.1f} us/step; decode + insert {comb_ms * 1000:.1f} us/step; "
+              f"{splits} page splits", file=sys.stderr, flush=True)
+    del ix, w
+    torch.cuda.empty_cache()
+    return res
+
+
+BUDGETS = {"qwen-gen": [256], "llama-layer": [64, 128, 256], "tiny": [64]}
+
+
 def main():
     a = parse()
     if a.summarize:
@@ -586,9 +851,7 @@ def main():
     from ann_retrieval_amd.api import IceIndex
 
     H, G, N, d, dtype, C, rotate, desc = WORKLOADS[a.workload]
-    budgets = [int(b) for b in a.budgets.split(",") if b]
-    if a.budget not in budgets:
-        budgets.append(a.budget)
+    budgets = sorted({int(b) for b in a.budgets.split(",") if b} | {a.budget})
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     print(f"[bench] workload={a.workload} H={H} G={G} N={N} d={d} {dtype}", file=sys.stderr, flush=True)
@@ -598,20 +861,14 @@ def main():
     ix = IceIndex(H, G, d, dtype, N + n_ins, seed=a.seed, max_budget=max(budgets), device=dev,
                   resident=max(a.resident, 0))
 
-    # ---- index build: median of a few full builds
-    bt = []
-    for i in range(a.builds + 1):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        ix.ice_build(w.K, w.V)
-        e1.record()
-        torch.cuda.synchronize()
-        if i:
-            bt.append(e0.elapsed_time(e1))
-    build_ms = float(np.median(bt))
-    print(f"[bench] build {build_ms:.2f} ms", file=sys.stderr, flush=True)
+    # ---- index build: median of a few builds, each phase timed by events on the build's stream
+    build_ms, phases = build_timing(ix, w, a.builds)
+    print(f"[bench] build {build_ms:.2f} ms; phases (ms) {np.round(phases, 3).tolist()}", file=sys.stderr, flush=True)
     head_meta(ix, H, N + n_ins)
+    from ann_retrieval_amd import _lib as L
+    gemm_ms = float(phases[L.ICE_PHASE_PARENT])
+    gemm_flop = parent_flops(ix, H, 0, d)
+    gemm_tflops = gemm_flop / (gemm_ms / 1000.0) / 1e12
 
     if a.copy_mib:
         # two plain copies of a known size: the runtime's device-to-device copy
@@ -624,67 +881,19 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- decode steps
+    # ---- decode steps at each budget
     Qs = [synth.decode_queries(w, G, gen, device=dev) for _ in range(a.warmup + a.steps)]
     results = {}
     for budget in budgets:
-        k = budget // 16
-        beam = k
-        for s in range(a.warmup):
-            ix.ice_decode(Qs[s], budget, beam)
-            _, uni, nuni = ix.ice_select(Qs[s], budget, beam)
-            ix.ice_attend(Qs[s], uni, nuni)
-        torch.cuda.synchronize()
-        # whole steps: one ice_decode per step (the fused select + attend); a
-        # short spin on the stream first lets the host queue the timed steps
-        # ahead of the GPU, so the events bracket GPU work, not launch gaps
-        t0 = time.perf_counter()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(int(5e7))
-        g0.record()
-        for s in range(a.steps):
-            ix.ice_decode(Qs[a.warmup + s], budget, beam)
-        g1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms_step = g0.elapsed_time(g1) / a.steps
-        # the separate calls, each kernel on its own: the same launches back to
-        # back between two events
-        unis = []
-        for s in range(a.steps):
-            _, uni, nuni = ix.ice_select(Qs[a.warmup + s], budget, beam)
-            unis.append((uni, nuni))
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        torch.cuda._sleep(int(5e7))
-        e[0].record()
-        for s in range(a.steps):
-            ix.ice_select(Qs[a.warmup + s], budget, beam)
-        e[1].record()
-        torch.cuda._sleep(int(5e7))
-        e[2].record()
-        for s in range(a.steps):
-            ix.ice_attend(Qs[a.warmup + s], *unis[s])
-        e[3].record()
-        torch.cuda.synchronize()
-        sel_ms = e[0].elapsed_time(e[1]) / a.steps
-        att_ms = e[2].elapsed_time(e[3]) / a.steps
-        # algorithmic bytes from the same selections (replayed with a trace)
-        nb = min(a.steps, 4)
-        byt = dict(select=0.0, attend=0.0, decode=0.0)
-        for s in range(nb):
-            q = Qs[a.warmup + s]
-            _, uni, nuni, tr = ix.ice_select(q, budget, beam, trace=True)
-            bb = algorithmic_bytes(ix, tr.cpu().numpy(), uni.cpu().numpy(), nuni.cpu().numpy(), d, elt, G)
-            for k2 in byt:
-                byt[k2] += bb[k2] / nb
-        sb, ab, db = byt["select"], byt["attend"], byt["decode"]
-        results[budget] = dict(ms_per_step=ms_step, steps_per_s=1000.0 / ms_step, wall_s=wall,
-                               decode_bytes=db, decode_gbs=db / ms_step / 1e6,
-                               select_ms=sel_ms, attend_ms=att_ms, select_bytes=sb, attend_bytes=ab,
-                               select_gbs=sb / sel_ms / 1e6, attend_gbs=ab / att_ms / 1e6)
-        print(f"[bench] T={budget}: {ms_step*1000:.1f} us/step fused ({db/ms_step/1e6:.0f} GB/s); separately "
-              f"select {sel_ms*1000:.1f} us ({sb/sel_ms/1e6:.0f} GB/s) attend {att_ms*1000:.1f} us "
-              f"({ab/att_ms/1e6:.0f} GB/s)", file=sys.stderr, flush=True)
+        r = decode_timing(ix, Qs, budget, a.steps, a.warmup, d, elt, G)
+        results[budget] = r
+        print(f"[bench] T={budget}: {r['ms_per_step']*1000:.1f} us/step fused ({r['decode_gbs']:.0f} GB/s); "
+              f"separately select {r['select_ms']*1000:.1f} us ({r['select_gbs']:.0f} GB/s) attend "
+              f"{r['attend_ms']*1000:.1f} us ({r['attend_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+
+    recall = None
+    if not a.no_recall:
+        recall = recall_leg(ix, w, Qs[a.warmup:a.warmup + 2], budgets, min(a.recall_heads, H), G)
 
     host_pool = None
     if not a.no_host_pool:
@@ -702,7 +911,7 @@ def main():
     resident = None
     if a.resident > 0:
         Kr, Vr = synth.resident_tokens(w, a.resident, gen, device=dev)
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0, r1 = ev_pair()
         torch.cuda.synchronize()
         r0.record()
         ix.set_resident(Kr, Vr)
@@ -729,7 +938,7 @@ def main():
     # ---- insert: one token per head per step
     knew = [synth.new_tokens(w, gen, device=dev) for _ in range(n_ins)]
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev_pair()
     # the spin lets the host queue every insert before the first one starts
     torch.cuda._sleep(int(5e7))
     e0.record()
@@ -738,6 +947,40 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     insert_ms = e0.elapsed_time(e1) / n_ins
+
+    # ---- the oracle on the host cores, on a bounded sample of the same workload
+    cpu = None
+    if not a.no_cpu:
+        heads = list(range(min(a.cpu_heads, H)))
+        n_cpu_steps = min(a.steps, 50)
+        t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(n_cpu_steps)], a.budget,
+                                               a.budget // 16, heads, a.seed)
+        per_head_step = t_dec / len(heads)
+        cpu = {
+            "value": 1.0 / (per_head_step * H), "unit": "decode steps/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 oracle on {len(heads)} of {H} heads ({N} tokens each): its own index build, then "
+                       f"select+attend for {G} query heads over {n_cpu_steps} steps at T={a.budget}; per-head time "
+                       f"scaled to {H} heads"),
+            "index_keys_per_s": len(heads) * N / t_build,
+            "cpu": cpu_model(),
+        }
+    del ix
+    torch.cuda.empty_cache()
+
+    # ---- the other workloads: Qwen3-32B-shaped long generation, one Llama
+    # layer, the tiny case, the needle
+    configs = needle = None
+    if not a.no_configs:
+        configs = {"qwen-gen": workload_leg("qwen-gen", a, a.steps, a.warmup, True),
+                   "llama-layer": workload_leg("llama-layer", a, a.steps, a.warmup, True),
+                   "tiny": workload_leg("tiny", a, a.steps, a.warmup, False)}
+        q = configs["qwen-gen"]["per_budget"]["256"]
+        q_ach = q["decode_bytes"] / q["ms_per_step"] / 1e6
+        configs["qwen-gen"]["roofline"] = {"bound": "hbm", "kernel": "k_decode", "achieved": q_ach,
+                                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": q_ach / HBM_PEAK_GBS,
+                                           "traffic": recorded_traffic("k_decode", "qwen-gen"),
+                                           "bytes_per_launch": q["decode_bytes"], "launch_ms": q["ms_per_step"]}
+        needle = needle_leg(a)
 
     head = results[a.budget]
     # the step is one kernel (the fused decode); its launches run back to back
@@ -764,12 +1007,26 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": recorded_traffic("k_decode", a.workload) if a.budget == 256 else None,
                      "bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
+        "roofline_build": {"bound": "mfma", "kernel": "k_parent_bf16", "level": 0, "achieved": gemm_tflops,
+                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tflops / BF16_PEAK_TFLOPS,
+                           "flop_per_launch": gemm_flop, "launch_ms": gemm_ms},
         "index_keys_per_s": H * N / (build_ms / 1000.0),
         "build_ms": build_ms,
+        "build_phases_ms": {"lift": float(phases[L.ICE_PHASE_LIFT]),
+                            **{f"{nm}_l{lv}": float(phases[base + 4 * lv]) for lv in range(2)
+                               for nm, base in (("operand", L.ICE_PHASE_OPERAND), ("parent", L.ICE_PHASE_PARENT),
+                                                ("pack", L.ICE_PHASE_PACK), ("copy", L.ICE_PHASE_COPY))},
+                            "top": float(phases[L.ICE_PHASE_TOP])},
         "insert_ms_per_step": insert_ms,
         "per_budget": {str(b): {k2: (round(v, 6) if isinstance(v, float) else v) for k2, v in r.items()}
                        for b, r in results.items()},
     }
+    if recall is not None:
+        out["recall"] = recall
+    if configs is not None:
+        out["configs"] = configs
+    if needle is not None:
+        out["needle"] = needle
     if host_pool is not None:
         out["host_pool"] = host_pool
     if resident is not None:
@@ -782,20 +1039,8 @@ def main():
         out["split_drift"] = split_drift(a)
     if a.pdci_tokens > 0:
         out["pdci"] = pdci_leg(a)
-    if not a.no_cpu:
-        heads = list(range(min(a.cpu_heads, H)))
-        n_cpu_steps = min(a.steps, 50)
-        t_build, t_dec, threads = cpu_baseline(w, [Qs[a.warmup + s] for s in range(n_cpu_steps)], a.budget,
-                                               a.budget // 16, heads, a.seed)
-        per_head_step = t_dec / len(heads)
-        out["cpu_baseline"] = {
-            "value": 1.0 / (per_head_step * H), "unit": "decode steps/s", "cores": threads, "kind": "oracle",
-            "sample": (f"fp64 oracle on {len(heads)} of {H} heads ({N} tokens each): its own index build, then "
-                       f"select+attend for {G} query heads over {n_cpu_steps} steps at T={a.budget}; per-head time scaled to "
-                       f"{H} heads"),
-            "index_keys_per_s": len(heads) * N / t_build,
-            "cpu": platform.processor() or platform.machine(),
-        }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -170,7 +170,9 @@ int ice_build_noalloc(ice_index* idx, const void* K, const void* V, int32_t n_to
  *   ICE_PHASE_PACK + 4 l              page pack of level l;
  *   ICE_PHASE_COPY + 4 l              page-pool copies of level l;
  *   ICE_PHASE_TOP                     top-list copy;
- * for l = 0 .. ICE_MAX_LEVELS - 2 (levels that do not exist take 0 ms).
+ * for l = 0 .. ICE_MAX_LEVELS - 2 (a phase with no kernel, such as the
+ * parent search of a level that does not exist, reports the few
+ * microseconds between two events).
  * Everything else is as in ice_build. */
 #define ICE_BUILD_PHASES  14
 #define ICE_PHASE_LIFT     0

@@ -254,5 +254,7 @@ def test_build_timed_equals_build():
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
     assert ms.shape == (L.ICE_BUILD_PHASES,) and np.all(ms >= 0)
     assert ms[L.ICE_PHASE_PARENT] > 0 and ms[L.ICE_PHASE_PARENT + 4] > 0
-    assert np.all(ms[L.ICE_PHASE_OPERAND + 8:L.ICE_PHASE_TOP] == 0)     # no level-2 parents with 3 levels
+    # no level-2 parents with 3 levels: those phases hold no kernel (two
+    # events back to back, a few microseconds apart)
+    assert np.all(ms[L.ICE_PHASE_OPERAND + 8:L.ICE_PHASE_TOP] < 0.05)
     say(f"build phases (ms): {np.round(ms, 4).tolist()}")
