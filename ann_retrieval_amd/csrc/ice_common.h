@@ -75,9 +75,10 @@ __host__ __device__ inline const char* v_pages(const DevLayout& L, const void* h
   return L.vpool ? L.vpool + (int64_t)h * L.vpool_head_bytes : static_cast<const char*>(hb) + L.off_pgV;
 }
 
-// Rows of the parent GEMM's candidate operand readable past the last
-// candidate: two 64-row stages.
-constexpr int kGemmPadRows = 128;
+// Candidate rows per stage of the parent GEMM, and the operand rows readable
+// past the last candidate: two stages.
+constexpr int kGemmTile = 64;
+constexpr int kGemmPadRows = 2 * kGemmTile;
 
 // Build workspace, also laid out per head.
 struct WsLayout {

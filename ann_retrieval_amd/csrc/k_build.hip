@@ -47,11 +47,14 @@ __global__ void k_fill_heads(void* base, int64_t head_bytes, int64_t off, int64_
 
 // |k|^2 in fp64 (exact products for bf16 and fp32 inputs), the promotion
 // level (unless `draw` is false: a layout taken from another head keeps its
-// levels), and the per-head maximum M^2. One block covers 64 tokens of a head.
+// levels), and the per-head maximum M^2. One block covers kNormTokens tokens
+// of a head, every wave a quarter of them with all its row loads in flight.
+constexpr int kNormTokens = 256;
 template <int D, class T>
 __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, void* blob, const T* K,
                                                     int64_t hstride, int n, void* ws, bool draw) {
   using G = RowGeo<D, T>;
+  constexpr int PW = kNormTokens / 4;     // tokens per wave
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const T* Kh = K + (int64_t)h * hstride;
@@ -59,9 +62,9 @@ __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, voi
   double* n2 = at<double>(static_cast<char*>(ws) + (int64_t)h * W.head_bytes, W.off_n2);
   int8_t* lev = at<int8_t>(hb, L.off_lev);
   double mx = 0.0;
-  const int base = blockIdx.x * 64 + wave * 16;
+  const int base = blockIdx.x * kNormTokens + wave * PW;
 #pragma unroll
-  for (int r0 = 0; r0 < 16; r0 += G::RPP) {
+  for (int r0 = 0; r0 < PW; r0 += G::RPP) {
     const int t = base + r0 + lane / G::LPR;
     double acc = 0.0;
     if (t < n) {
@@ -172,7 +175,9 @@ __global__ __launch_bounds__(kScanThreads) void k_lift_compact(DevLayout L, WsLa
 // Operand rows of the candidate parents (points of level `level`+1):
 // bf16: [key (D) | e0 e1 e0 e2 e0 e1 | 0 ...] with e = e0+e1+e2 split in
 // bf16 parts, so that one extra MFMA step adds e_child * e_parent to the
-// key inner product; fp32: [key | e | 0 0 0].
+// key inner product; then kGemmPadRows padding rows [0 ... 0 | -3.4e38 in
+// the step's last column], which the children's 1 in that column turns
+// into scores below any candidate's. fp32: [key | e | 0 0 0].
 template <int D, class T>
 __global__ void k_gather_opA(DevLayout L, WsLayout W, const void* blob, const T* K, int64_t hstride, void* ws,
                              int level) {
@@ -186,9 +191,13 @@ __global__ void k_gather_opA(DevLayout L, WsLayout W, const void* blob, const T*
   T* opA = at<T>(wh, W.off_opA);
   const T* Kh = K + (int64_t)h * hstride;
   const int kp = W.kp;
-  const int64_t total = (int64_t)n_cand * kp;
+  const int64_t total = (int64_t)(n_cand + (sizeof(T) == 2 ? kGemmPadRows : 0)) * kp;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int r = (int)(i / kp), c = (int)(i % kp);
+    if (r >= n_cand) {       // bf16 padding row
+      opA[i] = c == kp - 1 ? T(0xFF7F) : T(0);
+      continue;
+    }
     const int tok = pts[r];
     T out;
     if (c < D) {
@@ -236,42 +245,16 @@ __device__ inline PackView pack_view(const DevLayout& L, const WsLayout& W, cons
   return v;
 }
 
-__global__ void k_pack_count(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
-  const int h = blockIdx.y;
-  void* hb = head_base(blob, L, h);
-  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
-  const PackView v = pack_view(L, W, hb, wh, level);
-  if (v.skip) return;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= v.n_pts) return;
-  const int t = v.pts ? v.pts[i] : i;
-  int o = 0;
-  if (!v.root) {
-    int32_t* parent = at<int32_t>(hb, L.off_parent[level]);
-    const int8_t* lev = at<int8_t>(hb, L.off_lev);
-    int ow;
-    if (lev[t] >= level + 1) {
-      ow = t;
-      parent[t] = t;
-      at<float>(wh, W.off_s1)[t] = INFINITY;   // the owner leads its own run
-    } else {
-      ow = parent[t];
-    }
-    o = at<int32_t>(wh, W.off_rank[level + 1])[ow];
-  }
-  at<int32_t>(wh, W.off_oloc)[i] = o;
-  atomicAdd(at<int32_t>(wh, W.off_cnt) + o, 1);
-}
-
-__global__ __launch_bounds__(kScanThreads) void k_pack_scan(DevLayout L, WsLayout W, void* blob, void* ws,
-                                                           int level) {
-  const int h = blockIdx.x;
-  void* hb = head_base(blob, L, h);
-  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
-  const PackView v = pack_view(L, W, hb, wh, level);
-  if (v.skip) return;
+// Owner table and page metadata from the owners' member counts cnt[o]
+// (global or LDS): a block-wide scan over the owners in chunks of the block
+// gives each owner its first bucket position cbase and first page pbase
+// (written to the workspace, and to base_lds when given); every owner slot
+// gets its first / tail page, run and count, every page its owner, next
+// page and count, and the empty token slots -1. Called by the whole block.
+__device__ void write_owner_table(const DevLayout& L, const WsLayout& W, void* hb, char* wh, const PackView& v,
+                                  int level, const int32_t* cnt, int32_t* base_lds) {
   __shared__ int lds[16];
-  const int32_t* cnt = at<int32_t>(wh, W.off_cnt);
+  int32_t* cnt_g = at<int32_t>(wh, W.off_cnt);
   int32_t* cbase = at<int32_t>(wh, W.off_cbase);
   int32_t* pbase = at<int32_t>(wh, W.off_pbase);
   int32_t* fill = at<int32_t>(wh, W.off_fill);
@@ -285,17 +268,19 @@ __global__ __launch_bounds__(kScanThreads) void k_pack_scan(DevLayout L, WsLayou
   int32_t* orun = at<int32_t>(hb, L.off_orun[level]);
   int32_t* ocnt = at<int32_t>(hb, L.off_ocnt[level]);
   int runc = 0, runp = 0;
-  for (int base = 0; base < v.n_own; base += kScanThreads) {
-    const int o = base + threadIdx.x;
+  for (int b0 = 0; b0 < v.n_own; b0 += kScanThreads) {
+    const int o = b0 + threadIdx.x;
     const int c = o < v.n_own ? cnt[o] : 0;
     const int np = (c + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP;
     int totc, totp;
     const int cb = runc + block_scan_excl(c, lds, totc);
     const int pb = runp + block_scan_excl(np, lds, totp);
     if (o < v.n_own) {
+      if (cnt != cnt_g) cnt_g[o] = c;
       cbase[o] = cb;
       pbase[o] = pb;
       fill[o] = 0;
+      if (base_lds) base_lds[o] = cb;
       const int tok = v.root ? ICE_ROOT : owners[o];
       const int slot = v.root ? L.cap : tok;
       first[slot] = np ? pb : -1;
@@ -308,13 +293,150 @@ __global__ __launch_bounds__(kScanThreads) void k_pack_scan(DevLayout L, WsLayou
         pg_owner[p] = tok;
         pg_next[p] = j + 1 < np ? p + 1 : -1;
         pg_cnt[p] = pc;
-        for (int s = pc; s < ICE_PAGE_CAP; ++s) pg_tok[(int64_t)p * ICE_PAGE_CAP + s] = -1;
+        for (int s2 = pc; s2 < ICE_PAGE_CAP; ++s2) pg_tok[(int64_t)p * ICE_PAGE_CAP + s2] = -1;
       }
     }
     runc += totc;
     runp += totp;
   }
   if (threadIdx.x == 0) at<Hdr>(hb, L.off_hdr)->n_pages[level] = runp;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_pack_scan(DevLayout L, WsLayout W, void* blob, void* ws,
+                                                           int level) {
+  const int h = blockIdx.x;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const PackView v = pack_view(L, W, hb, wh, level);
+  if (v.skip) return;
+  write_owner_table(L, W, hb, wh, v, level, at<int32_t>(wh, W.off_cnt), nullptr);
+}
+
+// Owner slot of point i of the level (its owner's position in the next
+// level's point list; 0 in root mode). An owner is its own parent.
+__device__ inline int point_owner(const DevLayout& L, const WsLayout& W, void* hb, char* wh, const PackView& v,
+                                  int level, int i, int& t) {
+  t = v.pts ? v.pts[i] : i;
+  if (v.root) return 0;
+  int32_t* parent = at<int32_t>(hb, L.off_parent[level]);
+  const int8_t* lev = at<int8_t>(hb, L.off_lev);
+  int ow;
+  if (lev[t] >= level + 1) {
+    ow = t;
+    parent[t] = t;
+    at<float>(wh, W.off_s1)[t] = INFINITY;   // the owner leads its own run
+  } else {
+    ow = parent[t];
+  }
+  return at<int32_t>(wh, W.off_rank[level + 1])[ow];
+}
+
+// Owners per head the one-block pack keeps in LDS (two int32 arrays).
+constexpr int kPackLdsOwners = 8192;
+
+// The pack's grouping of one head in one block, for heads whose owners fit
+// the LDS: every point's owner and the owners' counts (LDS atomics), the
+// owner table (write_owner_table), then every point into a slot of its
+// owner's bucket (LDS atomics; root mode keeps token order). k_pack_place
+// then orders each bucket.
+__global__ __launch_bounds__(kScanThreads) void k_pack_group(DevLayout L, WsLayout W, void* blob, void* ws,
+                                                            int level) {
+  const int h = blockIdx.x;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const PackView v = pack_view(L, W, hb, wh, level);
+  if (v.skip || v.n_own > kPackLdsOwners) return;
+  __shared__ int32_t cnt[kPackLdsOwners], base[kPackLdsOwners];
+  for (int o = threadIdx.x; o < v.n_own; o += kScanThreads) cnt[o] = 0;
+  __syncthreads();
+  int32_t* oloc = at<int32_t>(wh, W.off_oloc);
+  int32_t* parent = at<int32_t>(hb, L.off_parent[level]);
+  const int8_t* lev = at<int8_t>(hb, L.off_lev);
+  const int32_t* rank = v.root ? nullptr : at<int32_t>(wh, W.off_rank[level + 1]);
+  float* s1w = at<float>(wh, W.off_s1);
+  // U points per thread at a time, their loads in flight together
+  constexpr int U = 8;
+  for (int i0 = threadIdx.x; i0 < v.n_pts; i0 += kScanThreads * U) {
+    int t[U], ow[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScanThreads;
+      t[u] = i < v.n_pts ? (v.pts ? v.pts[i] : i) : -1;
+    }
+    if (!v.root) {
+      int8_t lv[U];
+      int par[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        lv[u] = t[u] >= 0 ? lev[t[u]] : 0;
+        par[u] = t[u] >= 0 ? parent[t[u]] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool own = t[u] >= 0 && lv[u] >= level + 1;   // an owner is its own parent
+        if (own) {
+          parent[t[u]] = t[u];
+          s1w[t[u]] = INFINITY;                              // the owner leads its own run
+        }
+        ow[u] = own ? t[u] : par[u];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) ow[u] = t[u] >= 0 ? rank[ow[u]] : 0;
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) ow[u] = 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t[u] < 0) continue;
+      oloc[i0 + u * kScanThreads] = ow[u];
+      atomicAdd(&cnt[ow[u]], 1);
+    }
+  }
+  __syncthreads();
+  write_owner_table(L, W, hb, wh, v, level, cnt, base);
+  __syncthreads();
+  for (int o = threadIdx.x; o < v.n_own; o += kScanThreads) cnt[o] = 0;   // bucket fill counters
+  __syncthreads();
+  int32_t* btok = at<int32_t>(wh, W.off_btok);
+  float* bkey = at<float>(wh, W.off_bkey);
+  int32_t* bown = at<int32_t>(wh, W.off_bown);
+  const float* s1 = at<float>(wh, W.off_s1);
+  for (int i0 = threadIdx.x; i0 < v.n_pts; i0 += kScanThreads * U) {
+    int t[U], o[U];
+    float key[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kScanThreads;
+      t[u] = i < v.n_pts ? (v.pts ? v.pts[i] : i) : -1;
+      o[u] = i < v.n_pts ? oloc[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) key[u] = t[u] >= 0 && !v.root ? s1[t[u]] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t[u] < 0) continue;
+      const int i = i0 + u * kScanThreads;
+      const int pos = v.root ? i : base[o[u]] + atomicAdd(&cnt[o[u]], 1);
+      btok[pos] = t[u];
+      bkey[pos] = key[u];
+      bown[pos] = o[u];
+    }
+  }
+}
+
+__global__ void k_pack_count(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const PackView v = pack_view(L, W, hb, wh, level);
+  if (v.skip) return;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= v.n_pts) return;
+  int t;
+  const int o = point_owner(L, W, hb, wh, v, level, i, t);
+  at<int32_t>(wh, W.off_oloc)[i] = o;
+  atomicAdd(at<int32_t>(wh, W.off_cnt) + o, 1);
 }
 
 __global__ void k_pack_scatter(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
@@ -352,10 +474,14 @@ __global__ void k_pack_place(DevLayout L, WsLayout W, void* blob, void* ws, int 
   const float key = bkey[pos];
   const int t = btok[pos];
   int r = 0;
-  for (int j = b; j < b + c; ++j) {
-    const float kj = bkey[j];
-    const int tj = btok[j];
-    r += (kj > key) || (kj == key && tj < t);
+  if (v.root) {
+    r = t;      // the virtual root's bucket holds every token, in token order
+  } else {
+    for (int j = b; j < b + c; ++j) {
+      const float kj = bkey[j];
+      const int tj = btok[j];
+      r += (kj > key) || (kj == key && tj < t);
+    }
   }
   const int page = at<int32_t>(wh, W.off_pbase)[o] + r / ICE_PAGE_CAP;
   at<int32_t>(hb, L.off_pg_tok[level])[(int64_t)page * ICE_PAGE_CAP + r % ICE_PAGE_CAP] = t;
@@ -527,7 +653,7 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
     if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_ocnt[l], L.cap + 1, 0, s))) return err;
   }
   if (n > 0) {
-    k_norm_level<D, T><<<dim3(blocks_for(n, 64), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws, true);
+    k_norm_level<D, T><<<dim3(blocks_for(n, kNormTokens), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws, true);
     ICE_CHECK();
   }
   k_lift_compact<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
@@ -552,16 +678,24 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
     }
     if ((err = mark(3 + 4 * level))) return err;
     const int nown = (L.L >= 2 ? L.ncap[level + 1] : 0) + 1;
-    if ((err = launch_fill_heads(ws, W.head_bytes, L.H, W.off_cnt, nown, 0, s))) return err;
-    if (n > 0) {
-      k_pack_count<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
+    if (nown <= kPackLdsOwners) {
+      // every head's owners fit one block's LDS: count, scan and bucket in one kernel
+      k_pack_group<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, level);
       ICE_CHECK();
+    } else {
+      if ((err = launch_fill_heads(ws, W.head_bytes, L.H, W.off_cnt, nown, 0, s))) return err;
+      if (n > 0) {
+        k_pack_count<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
+        ICE_CHECK();
+      }
+      k_pack_scan<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, level);
+      ICE_CHECK();
+      if (n > 0) {
+        k_pack_scatter<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
+        ICE_CHECK();
+      }
     }
-    k_pack_scan<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, level);
-    ICE_CHECK();
     if (n > 0) {
-      k_pack_scatter<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
-      ICE_CHECK();
       k_pack_place<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
       ICE_CHECK();
     }
@@ -650,7 +784,7 @@ hipError_t build_reuse_typed(const DevLayout& L, const WsLayout& W, void* blob, 
   if ((err = hipGetLastError())) return err;
   // the head's own lift
   if (n > 0) {
-    k_norm_level<D, T><<<dim3(blocks_for(n, 64), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws, false);
+    k_norm_level<D, T><<<dim3(blocks_for(n, kNormTokens), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws, false);
     if ((err = hipGetLastError())) return err;
   }
   k_lift_compact<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);

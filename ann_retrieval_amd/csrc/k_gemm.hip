@@ -30,8 +30,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChildBf16 = 256;  // children per block: 4 waves x 64 (bf16), 4 waves x 32 (fp32)
 constexpr int kChildF32 = 128;
+constexpr uint16_t kBf16One = 0x3F80;
 
 struct GemmView {
+  int h;
   bool skip;
   int n_child, n_cand;
   const int32_t* exact;
@@ -40,9 +42,22 @@ struct GemmView {
   Hdr* hdr;
 };
 
-__device__ inline GemmView gemm_view(const DevLayout& L, const WsLayout& W, void* blob, void* ws, int level) {
+// Block (child block cb, head h) of the parent search from the 1-D launch
+// index. Consecutive launch indices go to the 8 XCDs in turn; the mapping
+// hands each XCD a contiguous range of (head, child block) pairs, so the
+// blocks that share a head's candidate operand share one L2. nbx: child
+// blocks per head; the last total % 8 indices keep their own position.
+struct GemmBlock {
+  int cb, h;
+};
+__device__ inline GemmBlock gemm_block(int nbx, int H) {
+  const int b = blockIdx.x, total = nbx * H, q = total / 8;
+  const int logical = b < 8 * q ? (b % 8) * q + b / 8 : b;
+  return GemmBlock{logical % nbx, logical / nbx};
+}
+
+__device__ inline GemmView gemm_view(const DevLayout& L, const WsLayout& W, void* blob, void* ws, int level, int h) {
   GemmView v;
-  const int h = blockIdx.y;
   void* hb = head_base(blob, L, h);
   v.hdr = at<Hdr>(hb, L.off_hdr);
   v.wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
@@ -52,6 +67,7 @@ __device__ inline GemmView gemm_view(const DevLayout& L, const WsLayout& W, void
   v.n_cand = cnts[level + 1];
   v.exact = at<int32_t>(v.wh, W.off_exact[level]);
   v.pts = at<int32_t>(v.wh, W.off_pts[level + 1]);
+  v.h = h;
   return v;
 }
 
@@ -86,7 +102,7 @@ struct ArgMax {
 
 __device__ inline void write_parent(const DevLayout& L, const WsLayout& W, const GemmView& v, void* blob,
                                     int level, int ctok, const ArgMax& a) {
-  const int h = blockIdx.y;
+  const int h = v.h;
   void* hb = head_base(blob, L, h);
   // a.idx is unset only if every score was NaN (non-finite input): fall back
   // to the first candidate rather than index out of range
@@ -121,10 +137,10 @@ struct LaneMax {
     second = __builtin_amdgcn_fmed3f(best, second, bm);
     best = gt ? bm : best;
     blk = gt ? b : blk;
-    if (gt) {
+    // selects, not a branch: the block's MFMAs and the previous block's
+    // epilogue stay in one basic block, so the scheduler can interleave them
 #pragma unroll
-      for (int j = 0; j < 16; ++j) kept[j] = s[j];
-    }
+    for (int j = 0; j < 16; ++j) kept[j] = gt ? s[j] : kept[j];
   }
   // winning accumulator index j (first one equal to the best) and the
   // runner-up over all the lane's scores
@@ -140,25 +156,35 @@ struct LaneMax {
   }
 };
 
+// 16 bytes per lane from global memory into LDS without registers
+// (global_load_lds_dwordx4): lane i writes bytes 16 i .. 16 i + 15 of the
+// wave-uniform LDS address `lds_run`.
+__device__ inline void load_to_lds16(const void* src, void* lds_run) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_run, 16, 0, 0);
+}
+// Waits until this wave's vector-memory loads are complete.
+__device__ inline void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int D>
 __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, void* blob, const uint16_t* K,
-                                                     int64_t hstride, void* ws, int level) {
+                                                     int64_t hstride, void* ws, int level, int nbx) {
   constexpr int KP = D + 16;            // operand row length (elements)
   constexpr int KS = KP / 16;           // k-steps of 16
   constexpr int ROWB = KP * 2;          // operand row bytes
   constexpr int LDSB = ROWB + 16;       // padded LDS row stride
-  constexpr int TILE = 64;              // candidate rows per stage (two 32-row MFMA blocks)
-  constexpr int CHUNKS = TILE * ROWB / 16;
-  constexpr int PF = (CHUNKS + 255) / 256;   // 16-byte loads per thread per stage
+  constexpr int TILE = kGemmTile;       // candidate rows per stage
+  constexpr int NB = TILE / 32;         // 32-row MFMA blocks per stage (even)
+  static_assert(NB % 2 == 0, "blocks alternate between two accumulator sets");
   constexpr int NF = 2;                 // 32-child fragments per wave
   __shared__ __attribute__((aligned(16))) char tile[2][TILE * LDSB];
 
-  const GemmView v = gemm_view(L, W, blob, ws, level);
+  const GemmBlock gb = gemm_block(nbx, L.H);
+  const GemmView v = gemm_view(L, W, blob, ws, level, gb.h);
   if (v.skip) return;
-  const int c0 = blockIdx.x * kChildBf16;
+  const int c0 = gb.cb * kChildBf16;
   if (c0 >= v.n_child) return;
-  const int h = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = gb.h;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float* e = at<float>(head_base(blob, L, h), L.off_e);
   const uint16_t* Kh = K + (int64_t)h * hstride;
   const char* opA = reinterpret_cast<const char*>(at<uint16_t>(v.wh, W.off_opA));
@@ -192,85 +218,105 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
       x.y = (uint32_t)a1 | ((uint32_t)a0 << 16);
       x.z = (uint32_t)a2 | ((uint32_t)a1 << 16);
     }
+    // column 15 of the step is 1: it carries the padding rows' sentinel
+    if (half == 1) x.w = (uint32_t)kBf16One << 16;
     bfr[f][KS - 1] = __builtin_bit_cast(bf16x8, x);
   }
 
-  // Candidate stages: global -> registers (issued a stage ahead) -> LDS.
-  // Thread chunk i of a stage is fixed, so its global and LDS offsets are
-  // computed once; chunk indices past the stage repeat its last chunk (the
-  // same value to the same LDS address). The loads carry no bounds checks:
-  // the operand has kGemmPadRows readable rows past the last candidate, whose
-  // scores are never pushed.
+  // Candidate stages go from global memory straight into LDS
+  // (global_load_lds_dwordx4: lane i of an instruction fills 16-byte slot i
+  // of a 1 KiB run, no registers held), two stages ahead of their use. A
+  // stage is TILE rows of 18 slots each plus one pad slot (the padded row
+  // stride LDSB), TILE * 19 slots in runs of 64, split over the 4 waves; a pad
+  // slot loads its row's first 16 bytes, never read. The loads carry no
+  // bounds checks: the operand has kGemmPadRows readable rows past the last
+  // candidate, and those rows score far below any candidate (their sentinel
+  // column), so the argmax needs no row mask.
   static_assert(2 * TILE <= kGemmPadRows, "stage loads past the candidates");
-  uint32_t goff[PF], soff[PF];
+  static_assert(LDSB == ROWB + 16, "one pad slot per row");
+  constexpr int SLOTS_ROW = LDSB / 16;               // 19
+  constexpr int RUNS = TILE * SLOTS_ROW / 64;        // runs of 64 slots per stage
+  static_assert(TILE * SLOTS_ROW % 64 == 0, "whole runs");
+  constexpr int RPW = (RUNS + 3) / 4;                // runs per wave (the last wave takes fewer)
+  uint32_t goff[RPW];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int c = min(threadIdx.x + 256 * i, CHUNKS - 1);
-    const int r = c / (ROWB / 16), q = c % (ROWB / 16);
-    goff[i] = (uint32_t)(r * ROWB + q * 16);
-    soff[i] = (uint32_t)(r * LDSB + q * 16);
+  for (int m = 0; m < RPW; ++m) {
+    const int sl = (wave + 4 * m) * 64 + lane;
+    const int r = min(sl / SLOTS_ROW, TILE - 1), q = sl % SLOTS_ROW;
+    goff[m] = (uint32_t)(r * ROWB + (q < SLOTS_ROW - 1 ? q * 16 : 0));
   }
-  auto fetch = [&](int p0, V4 (&pf)[PF]) {
-    const char* base = opA + (int64_t)p0 * ROWB;
+  auto load_stage = [&](int t, char* buf) {
+    const char* base = opA + (int64_t)t * TILE * ROWB;
 #pragma unroll
-    for (int i = 0; i < PF; ++i) pf[i] = *reinterpret_cast<const V4*>(base + goff[i]);
+    for (int m = 0; m < RPW; ++m)
+      if (wave + 4 * m < RUNS)
+        load_to_lds16(base + goff[m], buf + (wave + 4 * m) * 1024);
   };
-  auto stash = [&](char* buf, const V4 (&pf)[PF]) {
-#pragma unroll
-    for (int i = 0; i < PF; ++i) *reinterpret_cast<V4*>(buf + soff[i]) = pf[i];
-  };
+  // this wave's stage loads have landed (their LDS writes are done)
+  auto loads_done = [&]() { wait_vm_loads(); };
 
   LaneMax am[NF];
-  // one stage: the MFMAs and argmax of the rows in `cur`, with the next
-  // stage's loads in flight, then the next stage into `nxt`
-  auto stage = [&](int t, const char* cur, char* nxt) {
-    const int p0 = t * TILE;
-    V4 pf[PF];
-    fetch(p0 + TILE, pf);
-    const bool full = p0 + TILE <= v.n_cand;
+  // MFMAs of 32-row block rb of the stage in `cur`
+  auto mfma_block = [&](const char* cur, int rb, f32x16 (&acc)[NF]) {
 #pragma unroll
-    for (int rb = 0; rb < TILE / 32; ++rb) {
-      f32x16 acc[NF];
+    for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
 #pragma unroll
-      for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
+    for (int ks = 0; ks < KS; ++ks) {
+      const V4 a = *reinterpret_cast<const V4*>(cur + (rb * 32 + (lane & 31)) * LDSB + ks * 32 + half * 16);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const V4 a = *reinterpret_cast<const V4*>(cur + (rb * 32 + (lane & 31)) * LDSB + ks * 32 + half * 16);
+      for (int f = 0; f < NF; ++f)
+        acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bfr[f][ks], acc[f], 0, 0, 0);
+    }
+  };
+  // argmax of 32-row block `blk` (accumulator j of a lane is row 8 (j/4) +
+  // 4 half + j%4 of the block)
+  auto epilogue = [&](const f32x16 (&acc)[NF], int blk) {
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
-          acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bfr[f][ks], acc[f], 0, 0, 0);
-      }
-      // accumulator j of a lane is row 8 (j/4) + 4 half + j%4 of the block;
-      // rows past the candidates (last stage only) score -inf
-      const int rbase = p0 + rb * 32;
+    for (int f = 0; f < NF; ++f) {
+      float sc[16];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        float sc[16];
+      for (int j = 0; j < 16; ++j) sc[j] = acc[f][j];
+      am[f].push_block(sc, blk);
+    }
+  };
+  // Software pipeline over 32-row blocks: a block's MFMAs are issued before
+  // the previous block's argmax, so the matrix cores work while the vector
+  // ALUs fold the previous scores. Stage t (NB blocks) sits in `cur`, stage
+  // t + 1 in `nxt`; once every wave is past stage t (one barrier), stage
+  // t + 2 is loaded into `cur`. The last stage runs the same straight-line
+  // code: it multiplies a stage of padding rows whose scores are dropped.
+  const int n_tiles = (v.n_cand + TILE - 1) / TILE;
+  f32x16 accA[NF], accB[NF];
+  load_stage(0, tile[0]);
+  loads_done();
+  __syncthreads();
+  load_stage(min(1, n_tiles), tile[1]);
+  mfma_block(tile[0], 0, accA);
+  // blocks rb of the stage alternate between the accumulator sets A (even)
+  // and B (odd)
+  auto stage = [&](int t, char* cur, char* nxt) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sc[j] = acc[f][j];
-        if (!full) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            sc[j] = rbase + 8 * (j >> 2) + 4 * half + (j & 3) < v.n_cand ? sc[j] : -INFINITY;
-        }
-        am[f].push_block(sc, rbase / 32);
+    for (int rb = 1; rb < NB; ++rb) {
+      if (rb & 1) {
+        mfma_block(cur, rb, accB);                 // block (t, rb)
+        epilogue(accA, NB * t + rb - 1);           // block (t, rb - 1)
+      } else {
+        mfma_block(cur, rb, accA);
+        epilogue(accB, NB * t + rb - 1);
       }
     }
-    stash(nxt, pf);
+    loads_done();                                  // stage t + 1 is in nxt
     __syncthreads();
+    load_stage(min(t + 2, n_tiles), cur);          // at most one stage past the candidates' last stage
+    mfma_block(nxt, 0, accA);                      // block (t + 1, 0)
+    epilogue(accB, NB * t + NB - 1);               // block (t, NB - 1)
   };
-  const int n_tiles = (v.n_cand + TILE - 1) / TILE;
-  {
-    V4 pf[PF];
-    fetch(0, pf);
-    stash(tile[0], pf);
-  }
-  __syncthreads();
   // stages in pairs, so each one's LDS buffers are fixed addresses
   for (int t = 0; t < n_tiles; t += 2) {
     stage(t, tile[0], tile[1]);
     if (t + 1 < n_tiles) stage(t + 1, tile[1], tile[0]);
   }
+  loads_done();   // no load may still write the LDS when the block ends
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     ArgMax a;
@@ -287,18 +333,19 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
 // fp32 inputs: v_mfma_f32_32x32x2f32, operand rows [key | e | 0 0 0].
 template <int D>
 __global__ __launch_bounds__(256) void k_parent_f32(DevLayout L, WsLayout W, void* blob, const float* K,
-                                                    int64_t hstride, void* ws, int level) {
+                                                    int64_t hstride, void* ws, int level, int nbx) {
   constexpr int KP = D + 4;
   constexpr int KS = (D + 2) / 2;       // k-steps of 2 over [key | e | 0]
   constexpr int LDSW = KP + 1;          // padded LDS row stride (floats)
   constexpr int TILE = 32;
   __shared__ float tile[TILE * LDSW];
 
-  const GemmView v = gemm_view(L, W, blob, ws, level);
+  const GemmBlock gb = gemm_block(nbx, L.H);
+  const GemmView v = gemm_view(L, W, blob, ws, level, gb.h);
   if (v.skip) return;
-  const int c0 = blockIdx.x * kChildF32;
+  const int c0 = gb.cb * kChildF32;
   if (c0 >= v.n_child) return;
-  const int h = blockIdx.y;
+  const int h = gb.h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* e = at<float>(head_base(blob, L, h), L.off_e);
   const float* Kh = K + (int64_t)h * hstride;
@@ -346,16 +393,17 @@ hipError_t launch_parent_gemm(const DevLayout& L, const WsLayout& W, void* blob,
                               int64_t head_stride, void* ws, int level, hipStream_t s) {
   const int n_child_max = L.ncap[level];
   const int per = L.dtype == ICE_BF16 ? kChildBf16 : kChildF32;
-  const dim3 grid((unsigned)((n_child_max + per - 1) / per), (unsigned)L.H);
-  if (grid.x == 0) return hipSuccess;
+  const int nbx = (n_child_max + per - 1) / per;
+  if (nbx == 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)nbx * L.H));
   if (L.dtype == ICE_BF16) {
     const uint16_t* Kb = static_cast<const uint16_t*>(K);
-    if (L.d == 128) k_parent_bf16<128><<<grid, 256, 0, s>>>(L, W, blob, Kb, head_stride, ws, level);
-    else k_parent_bf16<64><<<grid, 256, 0, s>>>(L, W, blob, Kb, head_stride, ws, level);
+    if (L.d == 128) k_parent_bf16<128><<<grid, 256, 0, s>>>(L, W, blob, Kb, head_stride, ws, level, nbx);
+    else k_parent_bf16<64><<<grid, 256, 0, s>>>(L, W, blob, Kb, head_stride, ws, level, nbx);
   } else {
     const float* Kf = static_cast<const float*>(K);
-    if (L.d == 128) k_parent_f32<128><<<grid, 256, 0, s>>>(L, W, blob, Kf, head_stride, ws, level);
-    else k_parent_f32<64><<<grid, 256, 0, s>>>(L, W, blob, Kf, head_stride, ws, level);
+    if (L.d == 128) k_parent_f32<128><<<grid, 256, 0, s>>>(L, W, blob, Kf, head_stride, ws, level, nbx);
+    else k_parent_f32<64><<<grid, 256, 0, s>>>(L, W, blob, Kf, head_stride, ws, level, nbx);
   }
   return hipGetLastError();
 }
