@@ -36,7 +36,36 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxWaves = 16;
 
+// Waves per query head: 16 waves per block, which fill a CU's registers (128
+// VGPRs per wave), so each head's block runs on a CU of its own. With more
+// heads than CUs such blocks run in rounds; launch_waves then halves the
+// waves per query head when two blocks' LDS fits one CU, so that two heads
+// share each CU and every head runs at once. The kernels take their wave
+// count from the block size.
 __host__ __device__ inline int waves_per_query(int G) { return G <= 4 ? 4 : 16 / G; }
+constexpr int kCuLds = 160 * 1024;
+
+// the device's compute units (current device, looked up once per device)
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Waves of a selection block: waves_per_query(G) per query head, or half as
+// many when the heads outnumber the CUs and lds(nw) bytes fit twice in a CU.
+template <class LdsOf>
+int launch_waves(const DevLayout& L, LdsOf lds) {
+  const int w = waves_per_query(L.G);
+  if (L.H > cu_count() && w >= 2 && 2 * lds((w / 2) * L.G) <= kCuLds) return (w / 2) * L.G;
+  return w * L.G;
+}
 // LDS slots of the union's sort: the next power of two
 __host__ __device__ inline int union_pad(int n) {
   int p = 64;
@@ -625,7 +654,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
                            const ClaimLds* cl = nullptr) {
   using QG = Quarter<D, T>;
   using Top = std::conditional_t<BIG, LdsTop, RegTop>;
-  const int G = L.G, W = waves_per_query(G);
+  const int G = L.G, W = (int)(blockDim.x >> 6) / G;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = wv / W, j = wv % W;      // query head, wave within the query
   const bool lead = j == g % W;          // merges the query's lists (leads sit on different SIMDs)
@@ -702,7 +731,7 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
       if (lead) {
         const uint64_t* ql0 = comb + (g * W) * 64;
         uint64_t r = ql0[lane];
-        if (W > 1 && W * cap <= 64) {
+        if ((W == 2 || W == 4) && W * cap <= 64) {
           r = merge_lists(ql0, W, lane);
         } else {
           for (int jj = 1; jj < W; ++jj) r = wave_merge(r, ql0[jj * 64 + 63 - lane]);
@@ -1050,7 +1079,8 @@ void launch_typed(const DevLayout& L, const void* blob, const void* Qv, int budg
   const int lcap = beam > kpg ? beam : kpg;
   const bool big = lcap > 64;
   const SelLds S = sel_lds(L.G, lcap, kpg, big);
-  const dim3 grid((unsigned)L.H), block(64 * waves_per_query(L.G) * L.G);
+  const int nw = launch_waves(L, [&](int) { return S.total; });
+  const dim3 grid((unsigned)L.H), block(64 * nw);
   const T* Q = static_cast<const T*>(Qv);
   if (big) k_select<D, T, true><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, uni, n_uni, trace);
   else k_select<D, T, false><<<grid, block, (size_t)S.total, s>>>(L, blob, Q, budget, beam, sel, uni, n_uni, trace);
@@ -1060,7 +1090,7 @@ template <int D>
 void launch_decode_typed(const DevLayout& L, const void* blob, const void* Qv, int budget, int beam, int32_t* sel,
                          int32_t* uni, int32_t* n_uni, float scale, float* O, float* lse, hipStream_t s) {
   const int kpg = budget / ICE_PAGE_CAP;
-  const int nw = waves_per_query(L.G) * L.G;
+  const int nw = launch_waves(L, [&](int n) { return dec_lds(L.G, beam, kpg, n, D, L.pcap[0]).total; });
   const DecLds DL = dec_lds(L.G, beam, kpg, nw, D, L.pcap[0]);
   k_decode<D><<<dim3((unsigned)L.H), dim3(64 * nw), (size_t)DL.total, s>>>(
       L, blob, static_cast<const uint16_t*>(Qv), budget, beam, sel, uni, n_uni, scale, O, lse);
@@ -1071,7 +1101,7 @@ void launch_decode_typed(const DevLayout& L, const void* blob, const void* Qv, i
 bool decode_fused(const DevLayout& L, int budget, int beam) {
   const int kpg = budget / ICE_PAGE_CAP;
   if (L.dtype != ICE_BF16 || (beam > kpg ? beam : kpg) > 64) return false;
-  const int nw = waves_per_query(L.G) * L.G;
+  const int nw = launch_waves(L, [&](int n) { return dec_lds(L.G, beam, kpg, n, L.d, L.pcap[0]).total; });
   return dec_lds(L.G, beam, kpg, nw, L.d, L.pcap[0]).total <= kDecodeMaxLds;
 }
 

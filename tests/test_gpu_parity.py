@@ -85,6 +85,7 @@ def test_max_group_beam_budget():
     dict(dtype="bf16", G=8, budget=256, beam=16, d=128),      # union longer than a wave (G*k = 128)
     dict(dtype="bf16", G=16, budget=128, beam=8, d=64),       # union longer than a wave (G*k = 128)
     dict(dtype="bf16", G=16, budget=64, beam=4, d=64),
+    dict(dtype="bf16", G=5, budget=128, beam=8, d=128),       # 3 waves per query head
     dict(dtype="bf16", G=2, budget=256, beam=100, d=128),     # long lists: the two-kernel path
     dict(dtype="bf16", G=16, budget=128, beam=8, d=128),      # LDS too small for one kernel: two kernels
     dict(dtype="f32", G=4, budget=128, beam=8, d=128),        # fp32: the two-kernel path
@@ -111,6 +112,19 @@ def test_decode_long_union_qwen_group():
         Q = synth.decode_queries(w, 8, gen).cuda()
         out = decode_against_select_attend(ix, refs, Q, 256, 16, "qwen group")
         assert int(out["nuni"].max()) > 64, "the case must reach the long-union path"
+
+
+@pytest.mark.parametrize("G,budget,beam", [(8, 256, 16), (4, 128, 8), (6, 64, 4)])
+def test_decode_two_blocks_per_cu(G, budget, beam):
+    """More heads than compute units: the selection blocks take half the waves
+    per query head so that two share a CU. Selections, unions and attention
+    against select + attend and the oracle, first and last heads."""
+    H = torch.cuda.get_device_properties(0).multi_processor_count + 8
+    w, gen, ix = build_case(H, 700, 128, "bf16", 12, 17, G=G, budget=budget)
+    refs = check_build(w, ix, [0, H - 1], 17, 3, 4)
+    for _ in range(2):
+        Q = synth.decode_queries(w, G, gen).cuda()
+        decode_against_select_attend(ix, refs, Q, budget, beam, f"paired G={G}")
 
 
 def test_identical_keys():
