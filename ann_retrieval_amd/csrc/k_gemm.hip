@@ -158,12 +158,28 @@ struct LaneMax {
 
 // 16 bytes per lane from global memory into LDS without registers
 // (global_load_lds_dwordx4): lane i writes bytes 16 i .. 16 i + 15 of the
-// wave-uniform LDS address `lds_run`.
+// wave-uniform LDS address `lds_run` (through m0, which this kernel uses for
+// nothing else). Written as inline assembly: the compiler then does not treat
+// the copy as an LDS store that every later LDS read must wait for, which
+// would wait for the stages still in flight; the kernel waits for its own
+// stages (vmcnt, then a barrier) before reading them.
 __device__ inline void load_to_lds16(const void* src, void* lds_run) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_run, 16, 0, 0);
+  const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_run;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane((int)m)) : "memory", "m0");
 }
 // Waits until this wave's vector-memory loads are complete.
 __device__ inline void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ inline void wait_vm_loads_le() {
+  if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, void* blob, const uint16_t* K,
@@ -176,7 +192,7 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
   constexpr int NB = TILE / 32;         // 32-row MFMA blocks per stage (even)
   static_assert(NB % 2 == 0, "blocks alternate between two accumulator sets");
   constexpr int NF = 2;                 // 32-child fragments per wave
-  __shared__ __attribute__((aligned(16))) char tile[2][TILE * LDSB];
+  __shared__ __attribute__((aligned(16))) char tile[3][TILE * LDSB];
 
   const GemmBlock gb = gemm_block(nbx, L.H);
   const GemmView v = gemm_view(L, W, blob, ws, level, gb.h);
@@ -237,35 +253,45 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
   constexpr int SLOTS_ROW = LDSB / 16;               // 19
   constexpr int RUNS = TILE * SLOTS_ROW / 64;        // runs of 64 slots per stage
   static_assert(TILE * SLOTS_ROW % 64 == 0, "whole runs");
-  constexpr int RPW = (RUNS + 3) / 4;                // runs per wave (the last wave takes fewer)
+  constexpr int RPW = (RUNS + 3) / 4;                // runs per wave
+  // wave w takes runs w, w + 4, ...; where that passes the last run, the
+  // wave loads its previous run again (the same bytes to the same place), so
+  // every wave issues RPW loads per stage and no load is conditional
   uint32_t goff[RPW];
+  int lrun[RPW];
 #pragma unroll
   for (int m = 0; m < RPW; ++m) {
-    const int sl = (wave + 4 * m) * 64 + lane;
+    lrun[m] = wave + 4 * m < RUNS ? wave + 4 * m : wave + 4 * (m - 1);
+    const int sl = lrun[m] * 64 + lane;
     const int r = min(sl / SLOTS_ROW, TILE - 1), q = sl % SLOTS_ROW;
     goff[m] = (uint32_t)(r * ROWB + (q < SLOTS_ROW - 1 ? q * 16 : 0));
   }
   auto load_stage = [&](int t, char* buf) {
     const char* base = opA + (int64_t)t * TILE * ROWB;
 #pragma unroll
-    for (int m = 0; m < RPW; ++m)
-      if (wave + 4 * m < RUNS)
-        load_to_lds16(base + goff[m], buf + (wave + 4 * m) * 1024);
+    for (int m = 0; m < RPW; ++m) load_to_lds16(base + goff[m], buf + lrun[m] * 1024);
   };
   // this wave's stage loads have landed (their LDS writes are done)
   auto loads_done = [&]() { wait_vm_loads(); };
+  // the older of this wave's two stages in flight has landed: at most the
+  // newer stage's RPW loads are outstanding (loads complete in issue order)
+  static_assert(RPW >= 1 && RPW <= 5, "wait counts below");
+  auto older_stage_done = [&]() { wait_vm_loads_le<RPW>(); };
 
   LaneMax am[NF];
   // MFMAs of 32-row block rb of the stage in `cur`
   auto mfma_block = [&](const char* cur, int rb, f32x16 (&acc)[NF]) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
+    V4 a[KS];   // the block's A pieces, all read before its first MFMA
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a[ks] = *reinterpret_cast<const V4*>(cur + (rb * 32 + (lane & 31)) * LDSB + ks * 32 + half * 16);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const V4 a = *reinterpret_cast<const V4*>(cur + (rb * 32 + (lane & 31)) * LDSB + ks * 32 + half * 16);
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), bfr[f][ks], acc[f], 0, 0, 0);
+        acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ks]), bfr[f][ks], acc[f], 0, 0, 0);
     }
   };
   // argmax of 32-row block `blk` (accumulator j of a lane is row 8 (j/4) +
@@ -281,16 +307,19 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
   };
   // Software pipeline over 32-row blocks: a block's MFMAs are issued before
   // the previous block's argmax, so the matrix cores work while the vector
-  // ALUs fold the previous scores. Stage t (NB blocks) sits in `cur`, stage
-  // t + 1 in `nxt`; once every wave is past stage t (one barrier), stage
-  // t + 2 is loaded into `cur`. The last stage runs the same straight-line
-  // code: it multiplies a stage of padding rows whose scores are dropped.
+  // ALUs fold the previous scores. Three stage buffers: stage t (NB blocks)
+  // sits in `cur`, stage t + 1 in `nxt`, stage t + 2 is on its way into the
+  // third; once every wave is past stage t (one barrier), stage t + 3 is
+  // loaded into `cur`, so each stage has two stages' time to land. The last
+  // stage runs the same straight-line code: it multiplies a stage of padding
+  // rows whose scores are dropped.
   const int n_tiles = (v.n_cand + TILE - 1) / TILE;
   f32x16 accA[NF], accB[NF];
   load_stage(0, tile[0]);
-  loads_done();
-  __syncthreads();
   load_stage(min(1, n_tiles), tile[1]);
+  older_stage_done();                              // stage 0 is in tile[0]
+  __syncthreads();
+  load_stage(min(2, n_tiles), tile[2]);
   mfma_block(tile[0], 0, accA);
   // blocks rb of the stage alternate between the accumulator sets A (even)
   // and B (odd)
@@ -305,16 +334,17 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
         epilogue(accB, NB * t + rb - 1);
       }
     }
-    loads_done();                                  // stage t + 1 is in nxt
+    older_stage_done();                            // stage t + 1 is in nxt
     __syncthreads();
-    load_stage(min(t + 2, n_tiles), cur);          // at most one stage past the candidates' last stage
+    load_stage(min(t + 3, n_tiles), cur);          // at most one stage past the candidates' last stage
     mfma_block(nxt, 0, accA);                      // block (t + 1, 0)
     epilogue(accB, NB * t + NB - 1);               // block (t, NB - 1)
   };
-  // stages in pairs, so each one's LDS buffers are fixed addresses
-  for (int t = 0; t < n_tiles; t += 2) {
+  // stages in threes, so each one's LDS buffers are fixed addresses
+  for (int t = 0; t < n_tiles; t += 3) {
     stage(t, tile[0], tile[1]);
-    if (t + 1 < n_tiles) stage(t + 1, tile[1], tile[0]);
+    if (t + 1 < n_tiles) stage(t + 1, tile[1], tile[2]);
+    if (t + 2 < n_tiles) stage(t + 2, tile[2], tile[0]);
   }
   loads_done();   // no load may still write the LDS when the block ends
 #pragma unroll
