@@ -567,7 +567,7 @@ int ice_build_timed(ice_index* idx, const void* K, const void* V, int32_t n_toke
       if (e != hipSuccess) rc = hip_fail(e, "ice_build_timed timing");
     }
   }
-  for (int i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+  for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
   return rc;
 }
 

@@ -190,30 +190,42 @@ __global__ void k_gather_opA(DevLayout L, WsLayout W, const void* blob, const T*
   const float* e = at<float>(hb, L.off_e);
   T* opA = at<T>(wh, W.off_opA);
   const T* Kh = K + (int64_t)h * hstride;
-  const int kp = W.kp;
-  const int64_t total = (int64_t)(n_cand + (sizeof(T) == 2 ? kGemmPadRows : 0)) * kp;
+  // one 16-byte piece of a row per thread
+  constexpr int EPP = 16 / (int)sizeof(T);     // elements per piece
+  const int ppr = W.kp / EPP;                  // pieces per row
+  const int64_t total = (int64_t)(n_cand + (sizeof(T) == 2 ? kGemmPadRows : 0)) * ppr;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(i / kp), c = (int)(i % kp);
-    if (r >= n_cand) {       // bf16 padding row
-      opA[i] = c == kp - 1 ? T(0xFF7F) : T(0);
-      continue;
-    }
-    const int tok = pts[r];
-    T out;
-    if (c < D) {
-      out = Kh[(int64_t)tok * D + c];
-    } else if constexpr (sizeof(T) == 4) {
-      out = (c == D) ? e[tok] : 0.0f;
+    const int r = (int)(i / ppr), q = (int)(i % ppr);
+    union {
+      V4 v;
+      T x[EPP];
+    } out;
+    out.v = V4{0, 0, 0, 0};
+    if (r >= n_cand) {                                     // bf16 padding row
+      if (q == ppr - 1) out.x[EPP - 1] = T(0xFF7F);
     } else {
-      const float ev = e[tok];
-      const uint16_t p0 = f32_to_bf16(ev);
-      const float r1 = ev - bf16_to_f32(p0);
-      const uint16_t p1 = f32_to_bf16(r1);
-      const uint16_t p2 = f32_to_bf16(r1 - bf16_to_f32(p1));
-      const int j = c - D;
-      out = j == 0 || j == 2 || j == 4 ? p0 : j == 1 || j == 5 ? p1 : j == 3 ? p2 : (uint16_t)0;
+      const int tok = pts[r];
+      if (q < D / EPP) {
+        out.v = *reinterpret_cast<const V4*>(Kh + (int64_t)tok * D + q * EPP);
+      } else if (q == D / EPP) {
+        if constexpr (sizeof(T) == 4) {
+          out.x[0] = e[tok];
+        } else {
+          const float ev = e[tok];
+          const uint16_t p0 = f32_to_bf16(ev);
+          const float r1 = ev - bf16_to_f32(p0);
+          const uint16_t p1 = f32_to_bf16(r1);
+          const uint16_t p2 = f32_to_bf16(r1 - bf16_to_f32(p1));
+          out.x[0] = p0;
+          out.x[1] = p1;
+          out.x[2] = p0;
+          out.x[3] = p2;
+          out.x[4] = p0;
+          out.x[5] = p1;
+        }
+      }
     }
-    opA[i] = out;
+    *reinterpret_cast<V4*>(opA + i * EPP) = out.v;
   }
 }
 
