@@ -184,9 +184,7 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
   W->off_fill = w.take((n1 + 1) * 4);
   W->off_cbase = w.take((n1 + 1) * 4);
   W->off_pbase = w.take((n1 + 1) * 4);
-  W->off_btok = w.take(cap * 4);
-  W->off_bkey = w.take(cap * 4);
-  W->off_bown = w.take(cap * 4);
+  W->off_brec = w.take(cap * 16);
   W->head_bytes = w.off;
   W->build_bytes = W->head_bytes * p->n_heads;
   W->pdci_bytes = align256((int64_t)p->n_heads * ICE_PDCI_MAX_KEYS * n1 * 24);

@@ -93,7 +93,7 @@ struct WsLayout {
   int64_t off_s1, off_s2;        // f32 [cap]: best / runner-up parent score per token
   int64_t off_oloc;              // i32 [cap]: owner slot of each point
   int64_t off_cnt, off_fill, off_cbase, off_pbase;  // i32 [ncap[1]+1]
-  int64_t off_btok, off_bkey, off_bown;             // bucketed points: i32 / f32 / i32 [cap]
+  int64_t off_brec;              // bucketed points: (score bits, token, owner, 0) int4 [cap]
   int64_t build_bytes;           // H * head_bytes
   // P-DCI parent search (ice_build_pdci): a region after the per-head
   // build workspace holding, per head and simple index, ncap[1] keys by

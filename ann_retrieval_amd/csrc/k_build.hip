@@ -348,9 +348,9 @@ constexpr int kPackLdsOwners = 8192;
 
 // The pack's grouping of one head in one block, for heads whose owners fit
 // the LDS: every point's owner and the owners' counts (LDS atomics), the
-// owner table (write_owner_table), then every point into a slot of its
-// owner's bucket (LDS atomics; root mode keeps token order). k_pack_place
-// then orders each bucket.
+// owner table (write_owner_table), then every point's (score, token) into a
+// slot of its owner's bucket (LDS atomics). k_pack_rank then orders each
+// bucket; the virtual root (root mode) needs no bucket.
 __global__ __launch_bounds__(kScanThreads) void k_pack_group(DevLayout L, WsLayout W, void* blob, void* ws,
                                                             int level) {
   const int h = blockIdx.x;
@@ -408,11 +408,10 @@ __global__ __launch_bounds__(kScanThreads) void k_pack_group(DevLayout L, WsLayo
   __syncthreads();
   write_owner_table(L, W, hb, wh, v, level, cnt, base);
   __syncthreads();
+  if (v.root) return;   // the virtual root's slots are its tokens in order (k_pack_place_root)
   for (int o = threadIdx.x; o < v.n_own; o += kScanThreads) cnt[o] = 0;   // bucket fill counters
   __syncthreads();
-  int32_t* btok = at<int32_t>(wh, W.off_btok);
-  float* bkey = at<float>(wh, W.off_bkey);
-  int32_t* bown = at<int32_t>(wh, W.off_bown);
+  int4* brec = at<int4>(wh, W.off_brec);
   const float* s1 = at<float>(wh, W.off_s1);
   for (int i0 = threadIdx.x; i0 < v.n_pts; i0 += kScanThreads * U) {
     int t[U], o[U];
@@ -424,15 +423,12 @@ __global__ __launch_bounds__(kScanThreads) void k_pack_group(DevLayout L, WsLayo
       o[u] = i < v.n_pts ? oloc[i] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) key[u] = t[u] >= 0 && !v.root ? s1[t[u]] : 0.0f;
+    for (int u = 0; u < U; ++u) key[u] = t[u] >= 0 ? s1[t[u]] : 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t[u] < 0) continue;
-      const int i = i0 + u * kScanThreads;
-      const int pos = v.root ? i : base[o[u]] + atomicAdd(&cnt[o[u]], 1);
-      btok[pos] = t[u];
-      bkey[pos] = key[u];
-      bown[pos] = o[u];
+      const int pos = base[o[u]] + atomicAdd(&cnt[o[u]], 1);
+      brec[pos] = make_int4(__float_as_int(key[u]), t[u], o[u], 0);   // one 16-byte store per point
     }
   }
 }
@@ -456,47 +452,78 @@ __global__ void k_pack_scatter(DevLayout L, WsLayout W, void* blob, void* ws, in
   void* hb = head_base(blob, L, h);
   char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
   const PackView v = pack_view(L, W, hb, wh, level);
-  if (v.skip) return;
+  if (v.skip || v.root) return;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= v.n_pts) return;
   const int t = v.pts ? v.pts[i] : i;
   const int o = at<int32_t>(wh, W.off_oloc)[i];
   const int pos = at<int32_t>(wh, W.off_cbase)[o] + atomicAdd(at<int32_t>(wh, W.off_fill) + o, 1);
-  at<int32_t>(wh, W.off_btok)[pos] = t;
-  at<float>(wh, W.off_bkey)[pos] = v.root ? 0.0f : at<float>(wh, W.off_s1)[t];
-  at<int32_t>(wh, W.off_bown)[pos] = o;
+  at<int4>(wh, W.off_brec)[pos] = make_int4(__float_as_int(at<float>(wh, W.off_s1)[t]), t, o, 0);
 }
 
-// Final slot of every bucketed point = its rank inside the owner's bucket by
-// (score desc, token asc). Consecutive positions share a bucket, so the lanes
-// of a wave mostly loop over the same bucket.
-__global__ void k_pack_place(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
+// Final slot of every bucketed point: its rank in its owner's bucket by
+// (score desc, token asc). A block takes 256 consecutive bucket positions;
+// the buckets they fall in form one contiguous window of the bucket array,
+// which the block stages in LDS when it fits (else each point scans its
+// bucket in global memory). The owner's pages are consecutive, so rank r is
+// slot r counted from its first page.
+constexpr int kRankWin = 2048;   // LDS window (entries of 8 bytes)
+__global__ __launch_bounds__(256) void k_pack_rank(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
   const int h = blockIdx.y;
   void* hb = head_base(blob, L, h);
   char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
   const PackView v = pack_view(L, W, hb, wh, level);
-  if (v.skip) return;
-  const int pos = blockIdx.x * blockDim.x + threadIdx.x;
-  if (pos >= v.n_pts) return;
-  const int32_t* btok = at<int32_t>(wh, W.off_btok);
-  const float* bkey = at<float>(wh, W.off_bkey);
-  const int o = at<int32_t>(wh, W.off_bown)[pos];
-  const int b = at<int32_t>(wh, W.off_cbase)[o];
-  const int c = at<int32_t>(wh, W.off_cnt)[o];
-  const float key = bkey[pos];
-  const int t = btok[pos];
+  if (v.skip || v.root) return;
+  const int p0 = blockIdx.x * 256;
+  if (p0 >= v.n_pts) return;
+  const int pos = p0 + (int)threadIdx.x;
+  const bool live = pos < v.n_pts;
+  const int4* brec = at<int4>(wh, W.off_brec);
+  const int4 me = live ? brec[pos] : make_int4(0, 0, 0, 0);
+  const int b = live ? at<int32_t>(wh, W.off_cbase)[me.z] : 0;
+  const int c = live ? at<int32_t>(wh, W.off_cnt)[me.z] : 0;
+  __shared__ int lohi[2];
+  __shared__ int2 win[kRankWin];
+  if (threadIdx.x == 0) lohi[0] = b;
+  if (pos == min(p0 + 255, v.n_pts - 1)) lohi[1] = b + c;
+  __syncthreads();
+  const int lo = lohi[0], hi = lohi[1];
+  const bool staged = hi - lo <= kRankWin;
+  if (staged)
+    for (int k = threadIdx.x; k < hi - lo; k += 256) {
+      const int4 x = brec[lo + k];
+      win[k] = make_int2(x.x, x.y);
+    }
+  __syncthreads();
+  if (!live) return;
+  const float key = __int_as_float(me.x);
   int r = 0;
-  if (v.root) {
-    r = t;      // the virtual root's bucket holds every token, in token order
+  if (staged) {
+    for (int j = b - lo; j < b - lo + c; ++j) {
+      const int2 x = win[j];
+      r += (__int_as_float(x.x) > key) || (__int_as_float(x.x) == key && x.y < me.y);
+    }
   } else {
     for (int j = b; j < b + c; ++j) {
-      const float kj = bkey[j];
-      const int tj = btok[j];
-      r += (kj > key) || (kj == key && tj < t);
+      const int4 x = brec[j];
+      r += (__int_as_float(x.x) > key) || (__int_as_float(x.x) == key && x.y < me.y);
     }
   }
-  const int page = at<int32_t>(wh, W.off_pbase)[o] + r / ICE_PAGE_CAP;
-  at<int32_t>(hb, L.off_pg_tok[level])[(int64_t)page * ICE_PAGE_CAP + r % ICE_PAGE_CAP] = t;
+  at<int32_t>(hb, L.off_pg_tok[level])[(int64_t)at<int32_t>(wh, W.off_pbase)[me.z] * ICE_PAGE_CAP + r] = me.y;
+}
+
+// The virtual root's bucket holds every token in token order: token t takes
+// slot t of the root's pages.
+__global__ void k_pack_place_root(DevLayout L, WsLayout W, void* blob, void* ws, int level) {
+  const int h = blockIdx.y;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const PackView v = pack_view(L, W, hb, wh, level);
+  if (v.skip || !v.root) return;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= v.n_pts) return;
+  const int t = v.pts ? v.pts[i] : i;
+  at<int32_t>(hb, L.off_pg_tok[level])[(int64_t)at<int32_t>(wh, W.off_pbase)[0] * ICE_PAGE_CAP + t] = t;
 }
 
 // Rows of the page table into its key (and, at level 0, value) pool; empty
@@ -708,8 +735,14 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
       }
     }
     if (n > 0) {
-      k_pack_place<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
-      ICE_CHECK();
+      if (L.L >= 2) {
+        k_pack_rank<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
+        ICE_CHECK();
+      }
+      if (level == 0) {
+        k_pack_place_root<<<dim3(blocks_for(npts, 256), H), 256, 0, s>>>(L, W, blob, ws, level);
+        ICE_CHECK();
+      }
     }
     if ((err = mark(4 + 4 * level))) return err;
     if (n > 0) {

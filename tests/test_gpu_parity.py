@@ -56,6 +56,9 @@ def test_bf16_ragged_multi_tile():
     dict(N=1000, d=64, dtype="bf16"),
     dict(N=700, d=128, dtype="f32"),
     dict(N=3000, d=128, dtype="bf16", levels=4, plog2=2),
+    # 2-4 owners per head: buckets of 1,500-4,500 members, past the pack's
+    # LDS window of 2,048 (their ranks scan the bucket in global memory)
+    dict(N=6000, d=64, dtype="bf16", levels=2, plog2=11),
     dict(N=257, d=64, dtype="f32", G=16),
 ], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_edge_builds(case):
