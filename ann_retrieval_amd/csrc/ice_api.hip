@@ -173,6 +173,7 @@ void make_layout(const ice_params* p, DevLayout* L, WsLayout* W) {
   for (int l = 1; l < p->levels; ++l) W->off_pts[l] = w.take((int64_t)L->ncap[l] * 4);
   for (int l = 0; l < p->levels; ++l) W->off_exact[l] = w.take((int64_t)L->ncap[l] * 4);
   W->off_cnts = w.take(2 * ICE_MAX_LEVELS * 4);
+  W->off_blkcnt = w.take((cap + kLiftBlock - 1) / kLiftBlock * 2 * ICE_MAX_LEVELS * 4);
   const int64_t n1 = p->levels >= 2 ? L->ncap[1] : 0;
   // candidate operand rows, plus kGemmPadRows rows the parent GEMM may read
   // past the last candidate (its stage loads carry no bounds checks)

@@ -79,6 +79,9 @@ __host__ __device__ inline const char* v_pages(const DevLayout& L, const void* h
 // past the last candidate: two stages.
 constexpr int kGemmTile = 64;
 constexpr int kGemmPadRows = 2 * kGemmTile;
+// tokens per block of the lift: the per-block level counts are kept per
+// kLiftBlock tokens
+constexpr int kLiftBlock = 256;
 
 // Build workspace, also laid out per head.
 struct WsLayout {
@@ -89,6 +92,8 @@ struct WsLayout {
   int64_t off_pts[ICE_MAX_LEVELS];    // i32 [ncap[l]], l >= 1: points with level >= l, ascending
   int64_t off_exact[ICE_MAX_LEVELS];  // i32 [ncap[l]]: points with level == l, ascending
   int64_t off_cnts;              // i32 [2*ICE_MAX_LEVELS]: n_ge[l], n_eq[l]
+  int64_t off_blkcnt;            // i32 [ceil(cap / kLiftBlock)][2*ICE_MAX_LEVELS]: a token block's n_ge, n_eq,
+                                 // then (scanned) the counts before it
   int64_t off_opA;               // elt [ncap[1]][kp]: candidate-parent operand rows
   int64_t off_s1, off_s2;        // f32 [cap]: best / runner-up parent score per token
   int64_t off_oloc;              // i32 [cap]: owner slot of each point

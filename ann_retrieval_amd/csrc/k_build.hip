@@ -45,15 +45,46 @@ __global__ void k_fill_heads(void* base, int64_t head_bytes, int64_t off, int64_
     p[i] = value;
 }
 
+// Several fills of every head region in one launch: range z of `f` is
+// n[z] int32 words at byte offset off[z], set to val[z].
+constexpr int kMaxFills = 2 + 5 * (ICE_MAX_LEVELS - 1);   // header (two ranges) + five per table
+struct FillSet {
+  int count = 0;
+  int64_t off[kMaxFills], n[kMaxFills];
+  int32_t val[kMaxFills];
+  void add(int64_t o, int64_t words, int32_t v) {
+    off[count] = o;
+    n[count] = words;
+    val[count] = v;
+    ++count;
+  }
+};
+__global__ void k_fill_set(void* base, int64_t head_bytes, FillSet f) {
+  const int z = blockIdx.z;
+  int32_t* p = at<int32_t>(static_cast<char*>(base) + (int64_t)blockIdx.y * head_bytes, f.off[z]);
+  const int32_t value = f.val[z];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < f.n[z]; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+// Flag f of a token at level lv (lv = -1: no token) in the level lists:
+// f < ICE_MAX_LEVELS: lv >= f; else lv == f - ICE_MAX_LEVELS (levels < NL).
+__device__ inline bool level_flag(int f, int lv, int NL) {
+  return f < ICE_MAX_LEVELS ? f < NL && lv >= f : f - ICE_MAX_LEVELS < NL && lv == f - ICE_MAX_LEVELS;
+}
+constexpr int kLevelFlags = 2 * ICE_MAX_LEVELS;
+
 // |k|^2 in fp64 (exact products for bf16 and fp32 inputs), the promotion
 // level (unless `draw` is false: a layout taken from another head keeps its
-// levels), and the per-head maximum M^2. One block covers kNormTokens tokens
-// of a head, every wave a quarter of them with all its row loads in flight.
-constexpr int kNormTokens = 256;
+// levels), the per-head maximum M^2, and the block's count of every level
+// flag. One block covers kNormTokens tokens of a head, every wave a quarter
+// of them with all its row loads in flight.
+constexpr int kNormTokens = kLiftBlock;
 template <int D, class T>
 __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, void* blob, const T* K,
                                                     int64_t hstride, int n, void* ws, bool draw) {
   using G = RowGeo<D, T>;
+  static_assert(kNormTokens == 256, "four waves, one token per thread in the level counts");
   constexpr int PW = kNormTokens / 4;     // tokens per wave
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -78,8 +109,27 @@ __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, voi
     acc = group_sum_d<G::LPR>(acc);
     if (t < n && (lane % G::LPR) == 0) {
       n2[t] = acc;
-      if (draw) lev[t] = (int8_t)draw_level(L.seed, L.h0 + h, t, L.L, L.plog2);
       mx = fmax(mx, acc);
+    }
+  }
+  // level of token blockIdx.x * kNormTokens + threadIdx.x, and the block's
+  // count of each level flag
+  __shared__ int fc[4][kLevelFlags];
+  {
+    const int t = blockIdx.x * kNormTokens + (int)threadIdx.x;
+    int lv = -1;
+    if (t < n) {
+      if (draw) {
+        lv = draw_level(L.seed, L.h0 + h, t, L.L, L.plog2);
+        lev[t] = (int8_t)lv;
+      } else {
+        lv = lev[t];
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < kLevelFlags; ++f) {
+      const uint64_t m = __ballot(level_flag(f, lv, L.L));
+      if (lane == 0) fc[wave][f] = __popcll(m);
     }
   }
   __shared__ double red[4];
@@ -87,6 +137,9 @@ __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, voi
   for (int m = 1; m < 64; m <<= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
   if (lane == 0) red[wave] = mx;
   __syncthreads();
+  if (threadIdx.x < kLevelFlags)
+    at<int32_t>(static_cast<char*>(ws) + (int64_t)h * W.head_bytes, W.off_blkcnt)[blockIdx.x * kLevelFlags + threadIdx.x] =
+        fc[0][threadIdx.x] + fc[1][threadIdx.x] + fc[2][threadIdx.x] + fc[3][threadIdx.x];
   if (threadIdx.x == 0) {
     const double b = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
     // Non-negative doubles order like their bit patterns.
@@ -96,79 +149,84 @@ __global__ __launch_bounds__(256) void k_norm_level(DevLayout L, WsLayout W, voi
   }
 }
 
-// Lift coordinate e = sqrt(max(0, M^2 - |k|^2)) and the stable level lists:
-// pts[l] (level >= l, ascending), rank[l], exact[l] (level == l). One block
-// of 1024 threads per head walks the tokens in order.
-__global__ __launch_bounds__(kScanThreads) void k_lift_compact(DevLayout L, WsLayout W, void* blob, void* ws,
-                                                              int n) {
-  const int h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// The stable level lists from the per-block flag counts, in two steps.
+// k_lift_scan (one block per head): each flag's counts become the counts of
+// the blocks before (an exclusive scan over the token blocks); the totals
+// give the level sizes, the top level and the header's counts.
+__global__ __launch_bounds__(kScanThreads) void k_lift_scan(DevLayout L, WsLayout W, void* blob, void* ws, int n) {
+  const int h = blockIdx.x, tid = threadIdx.x;
   void* hb = head_base(blob, L, h);
   char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
   Hdr* hdr = at<Hdr>(hb, L.off_hdr);
-  const double M2 = hdr->M2;
-  const double* n2 = at<double>(wh, W.off_n2);
-  const int8_t* lev = at<int8_t>(hb, L.off_lev);
-  float* e = at<float>(hb, L.off_e);
-  constexpr int NFMAX = 2 * ICE_MAX_LEVELS;
-  __shared__ int wsum[16][NFMAX];
-  __shared__ int run[NFMAX];
-  const int NL = L.L;
-  if (tid < NFMAX) run[tid] = 0;
-  __syncthreads();
-  for (int base = 0; base < n; base += kScanThreads) {
-    const int t = base + tid;
-    const bool valid = t < n;
-    const int lv = valid ? lev[t] : -1;
-    if (valid) e[t] = (float)sqrt(fmax(0.0, M2 - n2[t]));
-    uint64_t masks[NFMAX];
-#pragma unroll
-    for (int f = 0; f < NFMAX; ++f) {
-      bool fl = false;
-      if (f < NL) fl = lv >= f;
-      else if (f >= ICE_MAX_LEVELS && f - ICE_MAX_LEVELS < NL) fl = lv == f - ICE_MAX_LEVELS;
-      masks[f] = __ballot(fl);
-      if (lane == 0) wsum[wave][f] = __popcll(masks[f]);
+  int32_t* bc = at<int32_t>(wh, W.off_blkcnt);
+  const int nblk = (n + kNormTokens - 1) / kNormTokens;
+  __shared__ int lds[16];
+  __shared__ int tot[kLevelFlags];
+  for (int f = 0; f < kLevelFlags; ++f) {
+    int run = 0;
+    for (int b0 = 0; b0 < nblk; b0 += kScanThreads) {
+      const int b = b0 + tid;
+      const int c = b < nblk ? bc[b * kLevelFlags + f] : 0;
+      int total;
+      const int ex = block_scan_excl(c, lds, total);
+      if (b < nblk) bc[b * kLevelFlags + f] = run + ex;
+      run += total;
     }
-    __syncthreads();
-#pragma unroll
-    for (int f = 0; f < NFMAX; ++f) {
-      int off = run[f];
-      for (int w = 0; w < wave; ++w) off += wsum[w][f];
-      const int pos = off + __popcll(masks[f] & ((1ull << lane) - 1ull));
-      const bool fl = (masks[f] >> lane) & 1ull;
-      if (f >= 1 && f < NL) {
-        if (fl) at<int32_t>(wh, W.off_pts[f])[pos] = t;
-        if (valid) at<int32_t>(wh, W.off_rank[f])[t] = fl ? pos : -1;
-      } else if (f >= ICE_MAX_LEVELS && fl) {
-        at<int32_t>(wh, W.off_exact[f - ICE_MAX_LEVELS])[pos] = t;
-      }
-    }
-    __syncthreads();
-    if (tid < NFMAX) {
-      int s = 0;
-      for (int w = 0; w < 16; ++w) s += wsum[w][tid];
-      run[tid] += s;
-    }
-    __syncthreads();
+    if (tid == 0) tot[f] = run;
   }
-  int Ltop = 0;
-  for (int l = 1; l < NL; ++l)
-    if (run[l] > 0) Ltop = l;
+  __syncthreads();
   if (tid == 0) {
+    const int NL = L.L;
+    int Ltop = 0;
+    for (int l = 1; l < NL; ++l)
+      if (tot[l] > 0) Ltop = l;
     int32_t* cnts = at<int32_t>(wh, W.off_cnts);
     for (int l = 0; l < ICE_MAX_LEVELS; ++l) {
-      cnts[l] = l < NL ? run[l] : 0;
-      cnts[ICE_MAX_LEVELS + l] = l < NL ? run[ICE_MAX_LEVELS + l] : 0;
+      cnts[l] = l < NL ? tot[l] : 0;
+      cnts[ICE_MAX_LEVELS + l] = l < NL ? tot[ICE_MAX_LEVELS + l] : 0;
     }
     hdr->n_tokens = n;
     hdr->top_level = Ltop;
-    hdr->n_top = Ltop >= 1 ? run[Ltop] : 0;
+    hdr->n_top = Ltop >= 1 ? tot[Ltop] : 0;
   }
-  if (Ltop >= 1) {
-    const int32_t* pts = at<int32_t>(wh, W.off_pts[Ltop]);
-    int32_t* top = at<int32_t>(hb, L.off_top_tok);
-    for (int i = tid; i < run[Ltop]; i += kScanThreads) top[i] = pts[i];
+}
+
+// k_lift_scatter (one block per kNormTokens tokens): the lift coordinate
+// e = sqrt(max(0, M^2 - |k|^2)) of each token, and its place in every level
+// list it belongs to: pts[l] (level >= l, ascending) with rank[l], exact[l]
+// (level == l), and the top list (the top level's points, ascending).
+__global__ __launch_bounds__(kNormTokens) void k_lift_scatter(DevLayout L, WsLayout W, void* blob, void* ws, int n) {
+  const int h = blockIdx.y, blk = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  void* hb = head_base(blob, L, h);
+  char* wh = static_cast<char*>(ws) + (int64_t)h * W.head_bytes;
+  const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
+  const int NL = L.L, Ltop = hdr->top_level;
+  const int t = blk * kNormTokens + tid;
+  const bool valid = t < n;
+  const int lv = valid ? at<int8_t>(hb, L.off_lev)[t] : -1;
+  if (valid) at<float>(hb, L.off_e)[t] = (float)sqrt(fmax(0.0, hdr->M2 - at<double>(wh, W.off_n2)[t]));
+  __shared__ int wc[kNormTokens / 64][kLevelFlags];
+  uint64_t masks[kLevelFlags];
+#pragma unroll
+  for (int f = 0; f < kLevelFlags; ++f) {
+    masks[f] = __ballot(level_flag(f, lv, NL));
+    if (lane == 0) wc[wave][f] = __popcll(masks[f]);
+  }
+  __syncthreads();
+  const int32_t* before = at<int32_t>(wh, W.off_blkcnt) + blk * kLevelFlags;
+#pragma unroll
+  for (int f = 0; f < kLevelFlags; ++f) {
+    int pos = before[f] + __popcll(masks[f] & ((1ull << lane) - 1ull));
+    for (int w = 0; w < wave; ++w) pos += wc[w][f];
+    const bool fl = (masks[f] >> lane) & 1ull;
+    if (f >= 1 && f < NL) {
+      if (fl) at<int32_t>(wh, W.off_pts[f])[pos] = t;
+      if (valid) at<int32_t>(wh, W.off_rank[f])[t] = fl ? pos : -1;
+      if (fl && f == Ltop) at<int32_t>(hb, L.off_top_tok)[pos] = t;
+    } else if (f >= ICE_MAX_LEVELS && fl) {
+      at<int32_t>(wh, W.off_exact[f - ICE_MAX_LEVELS])[pos] = t;
+    }
   }
 }
 
@@ -676,27 +734,36 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
   } while (0)
   // fresh header, parent links and owner heads; `keep` (a rebuild) keeps
   // the header's resident count and dense flag
-  if (!keep) {
-    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_hdr, sizeof(Hdr) / 4, 0, s))) return err;
-  } else {
-    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_hdr, offsetof(Hdr, n_resident) / 4, 0, s))) return err;
-    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_hdr + offsetof(Hdr, M2),
-                                 (sizeof(Hdr) - offsetof(Hdr, M2)) / 4, 0, s)))
-      return err;
-  }
-  for (int l = 0; l < L.ntab; ++l) {
-    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_parent[l], L.cap, -1, s))) return err;
-    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_first[l], L.cap + 1, -1, s))) return err;
-    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_tail[l], L.cap + 1, -1, s))) return err;
-    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_orun[l], L.cap + 1, 0, s))) return err;
-    if ((err = launch_fill_heads(blob, L.head_bytes, L.H, L.off_ocnt[l], L.cap + 1, 0, s))) return err;
-  }
-  if (n > 0) {
-    k_norm_level<D, T><<<dim3(blocks_for(n, kNormTokens), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws, true);
+  {
+    FillSet f;
+    if (!keep) {
+      f.add(L.off_hdr, sizeof(Hdr) / 4, 0);
+    } else {
+      f.add(L.off_hdr, offsetof(Hdr, n_resident) / 4, 0);
+      f.add(L.off_hdr + offsetof(Hdr, M2), (sizeof(Hdr) - offsetof(Hdr, M2)) / 4, 0);
+    }
+    for (int l = 0; l < L.ntab; ++l) {
+      f.add(L.off_parent[l], L.cap, -1);
+      f.add(L.off_first[l], L.cap + 1, -1);
+      f.add(L.off_tail[l], L.cap + 1, -1);
+      f.add(L.off_orun[l], L.cap + 1, 0);
+      f.add(L.off_ocnt[l], L.cap + 1, 0);
+    }
+    k_fill_set<<<dim3(blocks_for(L.cap + 1, 256 * 4), (unsigned)H, (unsigned)f.count), 256, 0, s>>>(blob, L.head_bytes,
+                                                                                                   f);
     ICE_CHECK();
   }
-  k_lift_compact<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
+  if (n > 0) {
+    k_norm_level<D, T><<<dim3(blocks_for(n, kNormTokens), H), kNormTokens, 0, s>>>(L, W, blob, K, hstride, n, ws,
+                                                                                   true);
+    ICE_CHECK();
+  }
+  k_lift_scan<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
   ICE_CHECK();
+  if (n > 0) {
+    k_lift_scatter<<<dim3(blocks_for(n, kNormTokens), H), kNormTokens, 0, s>>>(L, W, blob, ws, n);
+    ICE_CHECK();
+  }
   if ((err = mark(1))) return err;
   const int last = L.L >= 2 ? L.L - 2 : 0;
   for (int level = 0; level <= last; ++level) {
@@ -829,11 +896,16 @@ hipError_t build_reuse_typed(const DevLayout& L, const WsLayout& W, void* blob, 
   if ((err = hipGetLastError())) return err;
   // the head's own lift
   if (n > 0) {
-    k_norm_level<D, T><<<dim3(blocks_for(n, kNormTokens), H), 256, 0, s>>>(L, W, blob, K, hstride, n, ws, false);
+    k_norm_level<D, T><<<dim3(blocks_for(n, kNormTokens), H), kNormTokens, 0, s>>>(L, W, blob, K, hstride, n, ws,
+                                                                                   false);
     if ((err = hipGetLastError())) return err;
   }
-  k_lift_compact<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
+  k_lift_scan<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
   if ((err = hipGetLastError())) return err;
+  if (n > 0) {
+    k_lift_scatter<<<dim3(blocks_for(n, kNormTokens), H), kNormTokens, 0, s>>>(L, W, blob, ws, n);
+    if ((err = hipGetLastError())) return err;
+  }
   if (n == 0) return hipSuccess;
   // its own rows into the pages
   using G = RowGeo<D, T>;
