@@ -869,6 +869,13 @@ def main():
     gemm_ms = float(phases[L.ICE_PHASE_PARENT])
     gemm_flop = parent_flops(ix, H, 0, d)
     gemm_tflops = gemm_flop / (gemm_ms / 1000.0) / 1e12
+    # the same keys with one level (no promotion, no parent search: the
+    # virtual root owns every token in token order)
+    ix1 = IceIndex(H, G, d, dtype, N + n_ins, levels=1, seed=a.seed, max_budget=max(budgets), device=dev)
+    build1_ms, _ = build_timing(ix1, w, a.builds)
+    del ix1
+    torch.cuda.synchronize()
+    print(f"[bench] build with one level {build1_ms:.2f} ms", file=sys.stderr, flush=True)
 
     if a.copy_mib:
         # two plain copies of a known size: the runtime's device-to-device copy
@@ -1012,6 +1019,7 @@ def main():
                            "flop_per_launch": gemm_flop, "launch_ms": gemm_ms},
         "index_keys_per_s": H * N / (build_ms / 1000.0),
         "build_ms": build_ms,
+        "build_levels1_ms": build1_ms,
         "build_phases_ms": {"lift": float(phases[L.ICE_PHASE_LIFT]),
                             **{f"{nm}_l{lv}": float(phases[base + 4 * lv]) for lv in range(2)
                                for nm, base in (("operand", L.ICE_PHASE_OPERAND), ("parent", L.ICE_PHASE_PARENT),
