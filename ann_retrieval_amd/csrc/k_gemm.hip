@@ -182,7 +182,7 @@ __device__ inline void wait_vm_loads_le() {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, void* blob, const uint16_t* K,
+__global__ __launch_bounds__(256, 2) void k_parent_bf16(DevLayout L, WsLayout W, void* blob, const uint16_t* K,
                                                      int64_t hstride, void* ws, int level, int nbx) {
   constexpr int KP = D + 16;            // operand row length (elements)
   constexpr int KS = KP / 16;           // k-steps of 16
@@ -279,14 +279,16 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
   auto older_stage_done = [&]() { wait_vm_loads_le<RPW>(); };
 
   LaneMax am[NF];
-  // MFMAs of 32-row block rb of the stage in `cur`
-  auto mfma_block = [&](const char* cur, int rb, f32x16 (&acc)[NF]) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
-    V4 a[KS];   // the block's A pieces, all read before its first MFMA
+  // A pieces of 32-row block rb of a stage buffer
+  auto read_a = [&](const char* buf, int rb, V4 (&a)[KS]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      a[ks] = *reinterpret_cast<const V4*>(cur + (rb * 32 + (lane & 31)) * LDSB + ks * 32 + half * 16);
+      a[ks] = *reinterpret_cast<const V4*>(buf + (rb * 32 + (lane & 31)) * LDSB + ks * 32 + half * 16);
+  };
+  // MFMAs of one 32-row block from its A pieces
+  auto mfma_regs = [&](const V4 (&a)[KS], f32x16 (&acc)[NF]) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -313,32 +315,32 @@ __global__ __launch_bounds__(256) void k_parent_bf16(DevLayout L, WsLayout W, vo
   // loaded into `cur`, so each stage has two stages' time to land. The last
   // stage runs the same straight-line code: it multiplies a stage of padding
   // rows whose scores are dropped.
+  // Block 1 of a stage is read from LDS into registers while block 0's MFMAs
+  // run (a1), so its MFMAs start without waiting for LDS.
+  static_assert(NB == 2, "two blocks per stage");
   const int n_tiles = (v.n_cand + TILE - 1) / TILE;
   f32x16 accA[NF], accB[NF];
+  V4 a0[KS], a1[KS];
   load_stage(0, tile[0]);
   load_stage(min(1, n_tiles), tile[1]);
   older_stage_done();                              // stage 0 is in tile[0]
   __syncthreads();
   load_stage(min(2, n_tiles), tile[2]);
-  mfma_block(tile[0], 0, accA);
-  // blocks rb of the stage alternate between the accumulator sets A (even)
-  // and B (odd)
+  read_a(tile[0], 0, a0);
+  read_a(tile[0], 1, a1);
+  mfma_regs(a0, accA);                             // block (0, 0)
+  // blocks of a stage alternate between the accumulator sets A (block 0)
+  // and B (block 1)
   auto stage = [&](int t, char* cur, char* nxt) {
-#pragma unroll
-    for (int rb = 1; rb < NB; ++rb) {
-      if (rb & 1) {
-        mfma_block(cur, rb, accB);                 // block (t, rb)
-        epilogue(accA, NB * t + rb - 1);           // block (t, rb - 1)
-      } else {
-        mfma_block(cur, rb, accA);
-        epilogue(accB, NB * t + rb - 1);
-      }
-    }
+    mfma_regs(a1, accB);                           // block (t, 1)
+    epilogue(accA, NB * t);                        // block (t, 0)
     older_stage_done();                            // stage t + 1 is in nxt
     __syncthreads();
     load_stage(min(t + 3, n_tiles), cur);          // at most one stage past the candidates' last stage
-    mfma_block(nxt, 0, accA);                      // block (t + 1, 0)
-    epilogue(accB, NB * t + NB - 1);               // block (t, NB - 1)
+    read_a(nxt, 0, a0);
+    read_a(nxt, 1, a1);
+    mfma_regs(a0, accA);                           // block (t + 1, 0)
+    epilogue(accB, NB * t + 1);                    // block (t, 1)
   };
   // stages in threes, so each one's LDS buffers are fixed addresses
   for (int t = 0; t < n_tiles; t += 3) {
