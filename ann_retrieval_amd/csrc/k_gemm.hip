@@ -241,7 +241,8 @@ __global__ __launch_bounds__(256, 2) void k_parent_bf16(DevLayout L, WsLayout W,
 
   // Candidate stages go from global memory straight into LDS
   // (global_load_lds_dwordx4: lane i of an instruction fills 16-byte slot i
-  // of a 1 KiB run, no registers held), two stages ahead of their use. A
+  // of a 1 KiB run, no registers held) while the two stages before them are
+  // used. A
   // stage is TILE rows of 18 slots each plus one pad slot (the padded row
   // stride LDSB), TILE * 19 slots in runs of 64, split over the 4 waves; a pad
   // slot loads its row's first 16 bytes, never read. The loads carry no
