@@ -70,6 +70,17 @@ def test_edge_builds(case):
     check_decode(w, ix, refs, synth.decode_queries(w, c["G"], gen), 32, 1)
 
 
+def test_long_head_lift_scan_chunks():
+    """One head of 270,000 tokens: more than 1,024 token blocks of 256, so the
+    level-list scan carries its running counts across chunks of the block
+    scan; 2 levels with promotion 1/4096 (about 66 owners, buckets of
+    thousands of members, past the pack's LDS window)."""
+    N, d, levels, plog2 = 270000, 64, 2, 12
+    w, gen, ix = build_case(1, N, d, "bf16", 8, 3, G=2, levels=levels, plog2=plog2, capacity=N, budget=64)
+    refs = check_build(w, ix, [0], 3, levels, plog2)
+    check_decode(w, ix, refs, synth.decode_queries(w, 2, gen), 64, 4)
+
+
 def test_max_group_beam_budget():
     """The largest selection the boundary accepts: G = ICE_MAX_GROUP query heads,
     beam = ICE_MAX_BEAM, budget = ICE_MAX_BEAM pages (lists kept in LDS, the
