@@ -177,7 +177,10 @@ def summarize_mfma(path):
     counter run of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_INSTS_VALU and
     GRBM_GUI_ACTIVE. GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the
     dispatch's busy window is GRBM_GUI_ACTIVE / 8 GPU cycles; utilisation =
-    MFMA busy cycles / (window x 1024 SIMDs)."""
+    MFMA busy cycles / (window x 1024 SIMDs). SQ_INSTS_VALU counts the MFMA
+    instructions too (they are vector-ALU instructions to the sequencer: a
+    kernel of MFMAs and scalar loop control reads the same count in both), so
+    the other vector instructions are SQ_INSTS_VALU - SQ_INSTS_MFMA."""
     disp = {}
     for r in csv.DictReader(open(path)):
         k = short_name(r["Kernel_Name"])
@@ -186,8 +189,8 @@ def summarize_mfma(path):
         key = (k, r.get("Dispatch_Id", r.get("Correlation_Id", "")))
         disp.setdefault(key, {})[r["Counter_Name"]] = disp.setdefault(key, {}).get(r["Counter_Name"], 0.0) + \
             float(r["Counter_Value"])
-    out = ["| Kernel | Dispatch | GPU cycles (window) | MFMA instructions | VALU instructions | VALU / MFMA | "
-           "MFMA busy (% of 1024 SIMDs) |", "|---|---|---|---|---|---|---|"]
+    out = ["| Kernel | Dispatch | GPU cycles (window) | MFMA instructions | other VALU instructions | "
+           "other VALU / MFMA | MFMA busy (% of 1024 SIMDs) |", "|---|---|---|---|---|---|---|"]
     for (k, d), c in sorted(disp.items(), key=lambda x: (x[0][0], int(x[0][1]) if str(x[0][1]).isdigit() else 0)):
         mf = c.get("SQ_INSTS_MFMA", 0.0)
         if mf <= 0:
@@ -195,8 +198,8 @@ def summarize_mfma(path):
         win = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
         busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
         util = 100.0 * busy / (win * 1024) if win else float("nan")
-        va = c.get("SQ_INSTS_VALU", 0.0)
-        out.append(f"| `{k}` | {d} | {win:.0f} | {mf:.0f} | {va:.0f} | {va / mf:.1f} | {util:.1f} |")
+        va = c.get("SQ_INSTS_VALU", 0.0) - mf
+        out.append(f"| `{k}` | {d} | {win:.0f} | {mf:.0f} | {va:.0f} | {va / mf:.2f} | {util:.1f} |")
     return out
 
 
