@@ -45,6 +45,11 @@ struct ice_index {
   std::vector<std::vector<int32_t>> pos_ge[ICE_MAX_LEVELS];
   std::vector<std::vector<Run>> runs;
   std::vector<int32_t> ltop;
+  // Pipelined builds: the second stream and its events, made on the device
+  // current at the first such build and kept until the handle is destroyed.
+  hipStream_t side = nullptr;
+  int side_dev = -1;
+  std::vector<hipEvent_t> pev;
 };
 
 namespace {
@@ -327,7 +332,12 @@ int ice_create(const ice_params* p, void* index_dev, size_t index_bytes, ice_ind
   return ICE_OK;
 }
 
-void ice_destroy(ice_index* idx) { delete idx; }
+void ice_destroy(ice_index* idx) {
+  if (!idx) return;
+  for (hipEvent_t e : idx->pev) (void)hipEventDestroy(e);
+  if (idx->side) (void)hipStreamDestroy(idx->side);
+  delete idx;
+}
 
 int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");
@@ -357,9 +367,105 @@ int32_t ice_n_tokens(const ice_index* idx) { return idx ? idx->n_tokens : -1; }
 
 namespace {
 
+// Pipelined builds. The level-0 parent search keeps the matrix cores busy and
+// leaves HBM mostly idle, while the lift before it and the pack, page copies
+// and upper levels after it are HBM-bound. Heads are independent (each has
+// its own part of the blob and of the workspace), so a build of many heads is
+// cut into ranges of heads and run as a two-stream pipeline: the caller's
+// stream runs the ranges' level-0 searches back to back, and the side stream
+// runs each range's lift ahead of its search and the rest of its build after
+// it, overlapping the next range's search. The result is the one-stream
+// build's: every kernel sees the same heads and the same order within a head.
+#ifndef ICE_BUILD_CHUNKS
+#define ICE_BUILD_CHUNKS 4     // ranges per pipelined build
+#endif
+constexpr int kMaxBuildChunks = 16;
+constexpr int kMinChunkHeads = 8;  // fewer heads per range: one stream
+static_assert(ICE_BUILD_CHUNKS >= 2 && ICE_BUILD_CHUNKS <= kMaxBuildChunks, "build ranges");
+
+// Ranges a build of n_heads heads runs over (1: on the caller's stream alone,
+// also under stream capture and on a device other than the side stream's).
+int build_chunks(const ice_index* idx, int n_heads, hipStream_t s) {
+  if (idx->p.levels < 2) return 1;  // no parent search to overlap
+  const int c = std::min(ICE_BUILD_CHUNKS, n_heads / kMinChunkHeads);
+  if (c < 2) return 1;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return 1;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || (idx->side && dev != idx->side_dev)) return 1;
+  return c;
+}
+
+// The side stream (default priority, not synchronising with the null stream)
+// and 2 + 2 * kMaxBuildChunks events without timing, made once per handle.
+hipError_t ensure_side(ice_index* idx) {
+  if (idx->side) return hipSuccess;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::vector<hipEvent_t> ev(2 + 2 * kMaxBuildChunks, nullptr);
+  size_t made = 0;
+  for (; made < ev.size() && e == hipSuccess; ++made) e = hipEventCreateWithFlags(&ev[made], hipEventDisableTiming);
+  hipStream_t t = nullptr;
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&t, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    for (size_t i = 0; i < made; ++i)
+      if (ev[i]) (void)hipEventDestroy(ev[i]);
+    return e;
+  }
+  idx->pev = std::move(ev);
+  idx->side = t;
+  idx->side_dev = dev;
+  return hipSuccess;
+}
+
+// The build of the range L (already offset to its first head: blob, ws, K,
+// V) as `chunks` ranges on the caller's stream s and the side stream. s
+// continues after all of it (the side stream's last event), also when a
+// launch fails part way.
+hipError_t build_pipelined(ice_index* idx, const DevLayout& L, char* blob, const void* K, const void* V, int n,
+                           int64_t hstride, char* ws, bool keep, hipStream_t s, int chunks) {
+  hipError_t e = ensure_side(idx);
+  if (e != hipSuccess) return e;
+  const int per = (L.H + chunks - 1) / chunks;
+  chunks = (L.H + per - 1) / per;
+  hipStream_t t = idx->side;
+  // pev[0]: fork, pev[1]: join, pev[2 + 2c]: range c lifted, pev[3 + 2c]: range c searched
+  hipEvent_t* ev = idx->pev.data();
+  auto part = [&](int c, BuildPart what, hipStream_t st) -> hipError_t {
+    const int a = c * per;
+    DevLayout R = L;
+    R.H = std::min(per, L.H - a);
+    R.h0 = L.h0 + a;
+    if (R.vpool) R.vpool += (int64_t)a * L.vpool_head_bytes;
+    const int64_t kv = (int64_t)a * hstride * L.elt;
+    return launch_build(R, idx->W, blob + (int64_t)a * L.head_bytes, static_cast<const char*>(K) + kv,
+                        static_cast<const char*>(V) + kv, n, hstride, ws + (int64_t)a * idx->W.head_bytes, keep, st,
+                        nullptr, nullptr, what);
+  };
+  if ((e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(t, ev[0], 0)) != hipSuccess) return e;
+  // the lifts first, so that no search waits behind another range's rest
+  for (int c = 0; c < chunks && e == hipSuccess; ++c) {
+    if ((e = part(c, BuildPart::kLift, t)) != hipSuccess) break;
+    e = hipEventRecord(ev[2 + 2 * c], t);
+  }
+  for (int c = 0; c < chunks && e == hipSuccess; ++c) {
+    if ((e = hipStreamWaitEvent(s, ev[2 + 2 * c], 0)) != hipSuccess) break;
+    if ((e = part(c, BuildPart::kParent0, s)) != hipSuccess) break;
+    if ((e = hipEventRecord(ev[3 + 2 * c], s)) != hipSuccess) break;
+    if ((e = hipStreamWaitEvent(t, ev[3 + 2 * c], 0)) != hipSuccess) break;
+    e = part(c, BuildPart::kRest, t);
+  }
+  hipError_t j = hipEventRecord(ev[1], t);
+  if (j == hipSuccess) j = hipStreamWaitEvent(s, ev[1], 0);
+  return e != hipSuccess ? e : j;
+}
+
+// pipeline: allow the two-stream build (ice_build_noalloc keeps to one stream)
 int build_range(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, int32_t h0,
                 int32_t n_heads, void* ws, size_t ws_bytes, void* stream, const PdciArgs* pd,
-                hipEvent_t* ev = nullptr) {
+                hipEvent_t* ev = nullptr, bool pipeline = true) {
   if (!idx) return fail(ICE_ERR_ARG, "index is null");
   const int H = idx->p.n_heads;
   if (h0 < 0 || n_heads < 1 || h0 > H - n_heads)
@@ -391,8 +497,11 @@ int build_range(ice_index* idx, const void* K, const void* V, int32_t n_tokens, 
   if (L.vpool) L.vpool += (int64_t)h0 * L.vpool_head_bytes;
   char* blob = static_cast<char*>(idx->blob) + (int64_t)h0 * L.head_bytes;
   char* wsr = static_cast<char*>(ws) + (int64_t)h0 * idx->W.head_bytes;
-  hipError_t e = launch_build(L, idx->W, blob, K, V, n_tokens, head_stride, wsr, range_built,
-                              static_cast<hipStream_t>(stream), pd, ev);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int chunks = pipeline && !pd && !ev && n_tokens > 0 ? build_chunks(idx, n_heads, s) : 1;
+  hipError_t e = chunks > 1
+                     ? build_pipelined(idx, L, blob, K, V, n_tokens, head_stride, wsr, range_built, s, chunks)
+                     : launch_build(L, idx->W, blob, K, V, n_tokens, head_stride, wsr, range_built, s, pd, ev);
   if (e != hipSuccess) return hip_fail(e, "ice_build launch");
   if (!range_built)     // headers were cleared: no dense flags there any more
     for (int h = h0; h < h0 + n_heads; ++h) {
@@ -542,8 +651,8 @@ int ice_build_noalloc(ice_index* idx, const void* K, const void* V, int32_t n_to
   void* ptr = nullptr;
   const int rc = scratch_address(&ptr);
   if (rc != ICE_OK) return rc;
-  return ice_build_heads(idx, K, V, n_tokens, head_stride, 0, idx->p.n_heads, ptr, (size_t)ICE_NOALLOC_SCRATCH_BYTES,
-                         stream);
+  return build_range(idx, K, V, n_tokens, head_stride, 0, idx->p.n_heads, ptr, (size_t)ICE_NOALLOC_SCRATCH_BYTES,
+                     stream, nullptr, nullptr, false);
 }
 
 int ice_build_timed(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride, void* ws,

@@ -10,12 +10,18 @@ namespace ice {
 // range starts) and place their own rows into it
 hipError_t launch_build_reuse(const DevLayout& L, const WsLayout& W, void* blob, const void* src, const void* K,
                               const void* V, int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s);
+// Parts of a build, in the order they must run for a range of heads: the lift
+// (fills, norms, levels and level lists), the parent search of level 0, and
+// the rest (level 0's pack and page copies, the upper levels, the top list).
+// A pipelined build runs the parts of different head ranges on two streams.
+enum class BuildPart { kAll, kLift, kParent0, kRest };
 // keep: a rebuild, which keeps the headers' resident counts and dense flags
 // pd: parents by P-DCI instead of the exact search (nullptr: exact)
 // ev: nullable, ICE_BUILD_PHASES + 1 events recorded on s at the phase boundaries
+// pd and ev need part == kAll
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
                         int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s,
-                        const PdciArgs* pd = nullptr, hipEvent_t* ev = nullptr);
+                        const PdciArgs* pd = nullptr, hipEvent_t* ev = nullptr, BuildPart part = BuildPart::kAll);
 // k_gemm.hip: nearest parent of every level-`level` point among the level-(level+1) points
 hipError_t launch_parent_gemm(const DevLayout& L, const WsLayout& W, void* blob, const void* K,
                               int64_t head_stride, void* ws, int level, hipStream_t s);

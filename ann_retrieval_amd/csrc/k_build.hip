@@ -720,11 +720,14 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 template <int D, class T>
 hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const void* Kv, const void* Vv,
                        int n, int64_t hstride, void* ws, bool keep, hipStream_t s, const PdciArgs* pd,
-                       hipEvent_t* ev) {
+                       hipEvent_t* ev, BuildPart part) {
   const T* K = static_cast<const T*>(Kv);
   const T* V = static_cast<const T*>(Vv);
   const unsigned H = (unsigned)L.H;
   hipError_t err;
+  const bool do_lift = part == BuildPart::kAll || part == BuildPart::kLift;
+  const bool do_parent0 = part == BuildPart::kAll || part == BuildPart::kParent0;
+  const bool do_rest = part == BuildPart::kAll || part == BuildPart::kRest;
   // phase boundaries (ICE_BUILD_PHASES + 1 events when timed)
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
   if ((err = mark(0))) return err;
@@ -734,7 +737,7 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
   } while (0)
   // fresh header, parent links and owner heads; `keep` (a rebuild) keeps
   // the header's resident count and dense flag
-  {
+  if (do_lift) {
     FillSet f;
     if (!keep) {
       f.add(L.off_hdr, sizeof(Hdr) / 4, 0);
@@ -752,23 +755,25 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
     k_fill_set<<<dim3(blocks_for(L.cap + 1, 256 * 4), (unsigned)H, (unsigned)f.count), 256, 0, s>>>(blob, L.head_bytes,
                                                                                                    f);
     ICE_CHECK();
-  }
-  if (n > 0) {
-    k_norm_level<D, T><<<dim3(blocks_for(n, kNormTokens), H), kNormTokens, 0, s>>>(L, W, blob, K, hstride, n, ws,
-                                                                                   true);
+    if (n > 0) {
+      k_norm_level<D, T><<<dim3(blocks_for(n, kNormTokens), H), kNormTokens, 0, s>>>(L, W, blob, K, hstride, n, ws,
+                                                                                     true);
+      ICE_CHECK();
+    }
+    k_lift_scan<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
     ICE_CHECK();
-  }
-  k_lift_scan<<<H, kScanThreads, 0, s>>>(L, W, blob, ws, n);
-  ICE_CHECK();
-  if (n > 0) {
-    k_lift_scatter<<<dim3(blocks_for(n, kNormTokens), H), kNormTokens, 0, s>>>(L, W, blob, ws, n);
-    ICE_CHECK();
+    if (n > 0) {
+      k_lift_scatter<<<dim3(blocks_for(n, kNormTokens), H), kNormTokens, 0, s>>>(L, W, blob, ws, n);
+      ICE_CHECK();
+    }
   }
   if ((err = mark(1))) return err;
   const int last = L.L >= 2 ? L.L - 2 : 0;
   for (int level = 0; level <= last; ++level) {
     const int npts = L.ncap[level];
-    if (L.L >= 2 && n > 0) {
+    if (level == 0 ? !do_parent0 : !do_rest) {
+      // this part leaves the parent search of the level to another
+    } else if (L.L >= 2 && n > 0) {
       if (pd) {
         if ((err = mark(2 + 4 * level))) return err;
         if ((err = launch_parent_pdci(L, W, *pd, blob, Kv, hstride, ws, level, s))) return err;
@@ -783,6 +788,7 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
       return err;
     }
     if ((err = mark(3 + 4 * level))) return err;
+    if (!do_rest) continue;
     const int nown = (L.L >= 2 ? L.ncap[level + 1] : 0) + 1;
     if (nown <= kPackLdsOwners) {
       // every head's owners fit one block's LDS: count, scan and bucket in one kernel
@@ -827,7 +833,7 @@ hipError_t build_typed(const DevLayout& L, const WsLayout& W, void* blob, const 
   for (int level = last + 1; level < ICE_MAX_LEVELS - 1; ++level)
     for (int i = 2; i < 6; ++i)
       if ((err = mark(i + 4 * level))) return err;
-  if (L.L >= 2 && n > 0) {
+  if (do_rest && L.L >= 2 && n > 0) {
     using G = RowGeo<D, T>;
     k_copy_top<D, T><<<dim3(blocks_for(L.topcap, 4 * G::RPP * 4), H), 256, 0, s>>>(L, K, hstride, blob);
     ICE_CHECK();
@@ -936,13 +942,15 @@ hipError_t launch_build_reuse(const DevLayout& L, const WsLayout& W, void* blob,
 
 hipError_t launch_build(const DevLayout& L, const WsLayout& W, void* blob, const void* K, const void* V,
                         int n_tokens, int64_t head_stride, void* ws, bool keep, hipStream_t s, const PdciArgs* pd,
-                        hipEvent_t* ev) {
+                        hipEvent_t* ev, BuildPart part) {
+  if (part != BuildPart::kAll && (pd || ev)) return hipErrorInvalidValue;
   if (L.dtype == ICE_BF16) {
-    if (L.d == 128) return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev);
-    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev);
+    if (L.d == 128)
+      return build_typed<128, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev, part);
+    return build_typed<64, uint16_t>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev, part);
   }
-  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev);
-  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev);
+  if (L.d == 128) return build_typed<128, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev, part);
+  return build_typed<64, float>(L, W, blob, K, V, n_tokens, head_stride, ws, keep, s, pd, ev, part);
 }
 
 }  // namespace ice

@@ -658,15 +658,29 @@ def decode_timing(ix, Qs, budget, steps, warmup, d, elt, G, separate=True):
 
 
 def build_timing(ix, w, builds):
-    """Median over `builds` timed builds (after one untimed) of the whole build
-    and of each phase (ice_build_timed: events on the build's stream)."""
+    """After one untimed build: the median over `builds` builds of ice_build
+    (events on the caller's stream around the call; a build of many heads
+    runs as a two-stream pipeline that joins back into that stream), and the
+    median over as many one-stream builds (ice_build_timed) of each phase and
+    of their sum. Returns (build ms, phases ms, one-stream build ms, whether
+    the two kinds of build left the index blob bit-identical)."""
     import torch
     ix.ice_build(w.K, w.V)
     torch.cuda.synchronize()
+    tot = []
+    for _ in range(builds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ix.ice_build(w.K, w.V)
+        e1.record()
+        e1.synchronize()
+        tot.append(e0.elapsed_time(e1))
+    blob = ix.blob.clone()
     runs = [ix.ice_build_timed(w.K, w.V) for _ in range(builds)]
+    same = bool(torch.equal(blob, ix.blob))
+    del blob
     ph = np.median(np.stack(runs), axis=0)
-    tot = float(np.median([x.sum() for x in runs]))
-    return tot, ph
+    return float(np.median(tot)), ph, float(np.median([x.sum() for x in runs])), same
 
 
 def parent_flops(ix, H, level, d):
@@ -791,7 +805,7 @@ def workload_leg(name, a, steps, warmup, with_inserts):
     elt = 2 if dtype == "bf16" else 4
     n_ins = steps + warmup if with_inserts else 0
     ix = IceIndex(H, G, d, dtype, N + n_ins, seed=a.seed, max_budget=max(budgets), device=dev)
-    build_ms, ph = build_timing(ix, w, 3)
+    build_ms, ph, _, _ = build_timing(ix, w, 3)
     head_meta(ix, H, N + n_ins)
     if name == "qwen-gen":
         walk = synth.QueryWalk(w, G, gen, device=dev)
@@ -864,9 +878,12 @@ def main():
     ix = IceIndex(H, G, d, dtype, N + n_ins, seed=a.seed, max_budget=max(budgets), device=dev,
                   resident=max(a.resident, 0))
 
-    # ---- index build: median of a few builds, each phase timed by events on the build's stream
-    build_ms, phases = build_timing(ix, w, a.builds)
-    print(f"[bench] build {build_ms:.2f} ms; phases (ms) {np.round(phases, 3).tolist()}", file=sys.stderr, flush=True)
+    # ---- index build: median of a few builds; each phase from one-stream builds timed by events
+    build_ms, phases, build_serial_ms, build_same = build_timing(ix, w, a.builds)
+    if not build_same:
+        raise RuntimeError("the pipelined build and the one-stream build left different index blobs")
+    print(f"[bench] build {build_ms:.2f} ms (one stream {build_serial_ms:.2f} ms); phases (ms) "
+          f"{np.round(phases, 3).tolist()}", file=sys.stderr, flush=True)
     head_meta(ix, H, N + n_ins)
     from ann_retrieval_amd import _lib as L
     gemm_ms = float(phases[L.ICE_PHASE_PARENT])
@@ -875,7 +892,7 @@ def main():
     # the same keys with one level (no promotion, no parent search: the
     # virtual root owns every token in token order)
     ix1 = IceIndex(H, G, d, dtype, N + n_ins, levels=1, seed=a.seed, max_budget=max(budgets), device=dev)
-    build1_ms, _ = build_timing(ix1, w, a.builds)
+    build1_ms, _, _, _ = build_timing(ix1, w, a.builds)
     del ix1
     torch.cuda.synchronize()
     print(f"[bench] build with one level {build1_ms:.2f} ms", file=sys.stderr, flush=True)
@@ -1022,6 +1039,8 @@ def main():
                            "flop_per_launch": gemm_flop, "launch_ms": gemm_ms},
         "index_keys_per_s": H * N / (build_ms / 1000.0),
         "build_ms": build_ms,
+        "build_one_stream_ms": build_serial_ms,
+        "build_pipelined_equals_one_stream": build_same,
         "build_levels1_ms": build1_ms,
         "build_phases_ms": {"lift": float(phases[L.ICE_PHASE_LIFT]),
                             **{f"{nm}_l{lv}": float(phases[base + 4 * lv]) for lv in range(2)

@@ -137,7 +137,17 @@ int ice_attach_host_pool(ice_index* idx, void* host_pool, size_t host_pool_bytes
  * (lifted Euclidean distance, ties to the lower token id); store the points
  * sharing a parent together, ordered by distance and cut into pages of 16;
  * copy K and V rows into the page pool. Replaces any earlier content.
- * 0 <= n_tokens <= capacity. ws: workspace of ice_workspace_bytes. */
+ * 0 <= n_tokens <= capacity. ws: workspace of ice_workspace_bytes.
+ * A build of 16 or more heads with 2 or more levels runs as a pipeline over
+ * up to 4 ranges of heads on two streams: `stream` runs the ranges' level-0
+ * parent searches and a second stream, made by the handle at its first such
+ * build on the current device and destroyed with it, runs the other phases
+ * of each range. Events order it after the work enqueued on `stream` before
+ * the call and the work enqueued on `stream` after it after all of it, as a
+ * one-stream call would be; the result is the one-stream build's, bit for
+ * bit. Under stream capture, or on a device other than the one of the
+ * handle's second stream, it runs on `stream` alone. Calls on one handle
+ * come from one host thread at a time. */
 int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
               void* ws, size_t ws_bytes, void* stream);
 
@@ -154,7 +164,8 @@ int ice_build(ice_index* idx, const void* K, const void* V, int32_t n_tokens, in
  * a model at once. Every call on one device shares that device's array, so
  * calls that overlap on one device (other streams, other indexes, other host
  * threads) race; enqueue them on one stream. The build leaves nothing in the
- * array that a later call relies on. Otherwise as ice_build. */
+ * array that a later call relies on. It runs on `stream` alone (no second
+ * stream). Otherwise as ice_build. */
 #define ICE_NOALLOC_SCRATCH_BYTES 67108864  /* 64 MiB */
 int ice_build_noalloc(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
                       void* stream);
@@ -173,7 +184,8 @@ int ice_build_noalloc(ice_index* idx, const void* K, const void* V, int32_t n_to
  * for l = 0 .. ICE_MAX_LEVELS - 2 (a phase with no kernel, such as the
  * parent search of a level that does not exist, reports the few
  * microseconds between two events).
- * Everything else is as in ice_build. */
+ * It runs on `stream` alone (no pipeline), so the phases add up to the
+ * one-stream build. Everything else is as in ice_build. */
 #define ICE_BUILD_PHASES  14
 #define ICE_PHASE_LIFT     0
 #define ICE_PHASE_OPERAND  1
@@ -199,7 +211,8 @@ int ice_build_timed(ice_index* idx, const void* K, const void* V, int32_t n_toke
  * inner product (ties to the lower token id). Keys are fp64 from the stored
  * rows and fp32 lift coordinate. 1 <= l <= ICE_PDCI_MAX_L, m >= 1,
  * m*l <= ICE_PDCI_MAX_KEYS, visits >= 1, cands >= 1. The workspace of
- * ice_workspace_bytes covers it. Everything else is as in ice_build. */
+ * ice_workspace_bytes covers it. It runs on `stream` alone. Everything else
+ * is as in ice_build. */
 #define ICE_PDCI_MAX_KEYS 16
 #define ICE_PDCI_MAX_L 4
 int ice_build_pdci(ice_index* idx, const void* K, const void* V, int32_t n_tokens, int64_t head_stride,
@@ -213,7 +226,9 @@ int ice_build_pdci(ice_index* idx, const void* K, const void* V, int32_t n_token
  * Every head of an index holds the same token count: once any head is built,
  * a build of fewer than all heads must pass that count (ICE_ERR_ARG
  * otherwise). Builds of disjoint head ranges may run at the same time on
- * different streams with one workspace, each head using its own part of it.
+ * different streams with one workspace, each head using its own part of it
+ * (a range of 16 or more heads is pipelined as in ice_build; the handle's
+ * one second stream then serves the ranges in turn).
  * Select, attend, decode and insert need every head built (ICE_ERR_STATE
  * before). A range rebuilt as a whole keeps its resident tokens and dense
  * flags; heads built for the first time start with neither. */

@@ -63,6 +63,49 @@ def test_build_by_head_ranges_on_two_streams():
         part.ice_build_heads(K[:2, :N - 1], V[:2, :N - 1], 0)
 
 
+def host_pool_bytes(ix) -> np.ndarray:
+    import ctypes
+    return np.ctypeslib.as_array((ctypes.c_uint8 * ix.pool.nbytes).from_address(ix.pool.data_ptr())).copy()
+
+
+@pytest.mark.parametrize("dtype,d,host_pool", [("bf16", 128, False), ("f32", 64, False), ("bf16", 128, True)])
+def test_pipelined_build_equals_one_stream(dtype, d, host_pool):
+    """A build of 37 heads runs as a two-stream pipeline over ranges of heads
+    (10, 10, 10 and 7 heads). It leaves the blob, and the host pool, bit for
+    bit as the one-stream build leaves them (ice_build_timed, which never
+    pipelines). Work enqueued after it on its stream sees all of it. The heads
+    at the ranges' edges match the oracle."""
+    import gpu_support as gs
+    from ann_retrieval_amd.api import IceIndex
+    H, N, seed = 37, 2600, 31
+    say(f"pipelined build H={H} N={N} d={d} {dtype} host_pool={host_pool}")
+    w, gen = synth.clustered_kv(H, N, d, 24, dtype, seed, device="cpu")
+    K, V = w.K.cuda(), w.V.cuda()
+    ix = IceIndex(H, 4, d, dtype, N + 8, seed=seed, max_budget=256, host_pool=host_pool)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ix.ice_build(K, V)
+        piped = ix.blob.clone()       # on the build's stream: after all of the build
+    torch.cuda.synchronize()
+    pool_piped = host_pool_bytes(ix) if host_pool else None
+    refs = gs.check_build(w, ix, [0, 9, 10, 29, 30, 36], seed, 3, 4)
+    ix.ice_build_timed(K, V)
+    torch.cuda.synchronize()
+    assert torch.equal(piped, ix.blob), "the pipelined build differs from the one-stream build"
+    if host_pool:
+        assert np.array_equal(pool_piped, host_pool_bytes(ix)), "host pools differ"
+    # a decode right after a pipelined build on the same stream
+    Q = synth.decode_queries(w, 4, gen).cuda()
+    with torch.cuda.stream(s):
+        ix.ice_build(K, V)
+        r = ix.ice_decode(Q, 256, 16)
+    torch.cuda.synchronize()
+    out = gs.run_decode(ix, Q, 256, 16)
+    assert np.array_equal(r[0].cpu().numpy(), out["sel"]) and np.array_equal(r[1].cpu().numpy(), out["uni"])
+    gs.compare_decode(ix, refs, out)
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
 def test_reuse_layout_across_layers(dtype, d):
     """Heads 2, 3 (a second layer) take the layout of heads 0, 1 and their own
