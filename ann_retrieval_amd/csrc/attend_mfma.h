@@ -247,24 +247,6 @@ __device__ void attend_pages(const DevLayout& L, const void* hb, int h, int G, c
   for (int c = 0; c < M::VC; ++c) st.acc[c] = acc[c];
 }
 
-// One wave attends one page whose id and valid rows it already holds
-// (wave-uniform; an id outside [0, n_pages) or a page without rows adds
-// nothing). V from the head's device pool.
-template <int D>
-__device__ inline void attend_one(const DevLayout& L, const void* hb, int h, int n_pages, int pg, int n, float c2,
-                                  const float* part, WaveAcc<D>& st) {
-  using M = MGeo<D>;
-  const V4* q_lds = reinterpret_cast<const V4*>(part);
-  const int lane = threadIdx.x & 63;
-  const bool ok = pg >= 0 && pg < n_pages && n > 0;
-  n = ok ? n : 0;
-  MPage<D> a;
-  uint2 va[M::VC];
-  mload_k<D>(at<char>(hb, L.off_pgK[0]), ok ? pg : 0, n, lane, a);
-  mload_v<D>(v_pages(L, hb, h), ok ? pg : 0, n, lane, va);
-  page_update<D>(a.k, va, n, c2, q_lds, lane, st.m, st.l, st.acc);
-}
-
 // A wave's partials (m, l and o of query qn; every lane group holds m and l,
 // lane group qt holds dims 16c + 4qt + j) into slot wv (< nw) of the LDS
 // partials.

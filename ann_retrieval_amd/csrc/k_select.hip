@@ -1015,48 +1015,92 @@ __global__ __launch_bounds__(1024) void k_decode(DevLayout L, const void* blob, 
   // chunk's pages in list order into fresh sums and leaves them in the
   // chunk's partial slot; the slots are merged in chunk order, so the result
   // does not depend on which wave took which chunk (bitwise deterministic). A
-  // wave asks once its own selection has ended, and a claimed page waits for
-  // its query head to publish (a bounded wait: past kSpinLimit polls it
-  // counts a timeout and skips the page, so the kernel always ends).
+  // wave asks once its own selection has ended; it first waits for the query
+  // heads whose claims its chunk holds to publish (a bounded wait: past
+  // kSpinLimit polls it counts a timeout and skips their pages, so the
+  // kernel always ends), then keeps the next page's loads in flight while it
+  // attends the current one.
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   (void)wv;
   const void* hb = head_base(blob, L, h);
   const Hdr* hdr = at<Hdr>(hb, L.off_hdr);
   int* timeouts = const_cast<int*>(&hdr->sync_timeouts);
   const int n_pages = hdr->n_pages[0], n_res = hdr->n_resident;
-  const int n_claim = G * kpg, n_items = n_claim + (n_res + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP;
+  const int n_rp = min(L.res_pages, (n_res + ICE_PAGE_CAP - 1) / ICE_PAGE_CAP);
+  const int n_claim = G * kpg, n_items = n_claim + n_rp;
   const int cs = max(1, (n_items + nw - 1) / nw);        // items per chunk
   const int n_chunks = (n_items + cs - 1) / cs;          // <= nw partial slots
+  const char* pgK = at<char>(hb, L.off_pgK[0]);
+  const char* pgV = v_pages(L, hb, h);
+  const float c2 = scale * mfma_attend::kLog2e;
   for (;;) {
     int c = 0;
     if (lane == 0) c = atomicAdd(cl.next, 1);
     c = __builtin_amdgcn_readfirstlane(__shfl(c, 0, 64));
     if (c >= n_chunks) break;
-    mfma_attend::WaveAcc<D> st;
-    st.init();
-    const int i1 = min(n_items, (c + 1) * cs);
-    for (int i = c * cs; i < i1; ++i) {
-      if (i >= n_claim) {     // a resident page: nothing to wait for
-        const int r = i - n_claim;
-        mfma_attend::attend_one<D>(L, hb, h, L.pcap[0] + L.res_pages, L.pcap[0] + r,
-                                   min(ICE_PAGE_CAP, n_res - ICE_PAGE_CAP * r), scale * mfma_attend::kLog2e, part, st);
-        continue;
-      }
-      const int gq = i / kpg;
-      int spins = 0;
-      bool ok = true;
-      while (__atomic_load_n(&cl.count[gq], __ATOMIC_RELAXED) < 0) {
-        if (++spins > kSpinLimit) {
-          if (lane == 0) atomicAdd(timeouts, 1);
-          ok = false;
-          break;
+    const int i0 = c * cs, i1 = min(n_items, (c + 1) * cs);
+    // the query heads of the chunk's claims, each waited for once
+    uint32_t gq_ok = 0u;
+    if (i0 < n_claim) {
+      const int g1 = (min(i1, n_claim) - 1) / kpg;
+      for (int gq = i0 / kpg; gq <= g1; ++gq) {
+        int spins = 0;
+        bool ok = true;
+        while (__atomic_load_n(&cl.count[gq], __ATOMIC_RELAXED) < 0) {
+          if (++spins > kSpinLimit) {
+            if (lane == 0) atomicAdd(timeouts, 1);
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_s_sleep(1);
+        gq_ok |= ok ? 1u << gq : 0u;
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      // the page id and rows: the same LDS words in every lane
-      const int pg = __builtin_amdgcn_readfirstlane(cl.pages[i]), n = __builtin_amdgcn_readfirstlane(cl.rows[i]);
-      if (ok && pg >= 0) mfma_attend::attend_one<D>(L, hb, h, n_pages, pg, n, scale * mfma_attend::kLog2e, part, st);
+    }
+    mfma_attend::WaveAcc<D> st;
+    st.init();
+    for (int k0 = i0; k0 < i1; k0 += 64) {
+      // lane t: item k0 + t's page and valid rows (0 rows: nothing to attend)
+      int my_pg = 0, my_n = 0;
+      const int i = k0 + lane;
+      if (i < i1) {
+        if (i >= n_claim) {     // a resident page: nothing to wait for
+          const int r = i - n_claim;
+          my_pg = L.pcap[0] + r;
+          my_n = min(ICE_PAGE_CAP, n_res - ICE_PAGE_CAP * r);
+        } else if ((gq_ok >> (i / kpg)) & 1u) {
+          const int pg = cl.pages[i], n = cl.rows[i];
+          if (pg >= 0 && pg < n_pages && n > 0) {
+            my_pg = pg;
+            my_n = n;
+          }
+        }
+      }
+      const int nk = min(64, i1 - k0);
+      // two K buffers with fixed roles in each half of an unrolled pair of
+      // steps: the next page's K loads while the current page's V loads and
+      // the current page is attended. The steps are straight-line code
+      // (clamped indices, masked pages) so that the next page stays in flight.
+      mfma_attend::MPage<D> bufA, bufB;
+      auto issue = [&](int k, mfma_attend::MPage<D>& b) {
+        const int kc = min(k, nk - 1);
+        const int pg = __shfl(my_pg, kc, 64), n = k < nk ? __shfl(my_n, kc, 64) : 0;
+        mfma_attend::mload_k<D>(pgK, pg, n, lane, b);
+      };
+      auto step = [&](int k, mfma_attend::MPage<D>& cur, mfma_attend::MPage<D>& nxt) {
+        const int kc = min(k, nk - 1);
+        const int pg = __shfl(my_pg, kc, 64), n = k < nk ? __shfl(my_n, kc, 64) : 0;
+        uint2 v[mfma_attend::MGeo<D>::VC];
+        mfma_attend::mload_v<D>(pgV, pg, n, lane, v);
+        issue(k + 1, nxt);
+        mfma_attend::page_update<D>(cur.k, v, n, c2, reinterpret_cast<const V4*>(part), lane, st.m, st.l, st.acc);
+      };
+      issue(0, bufA);
+      for (int k = 0; k < nk; k += 2) {
+        step(k, bufA, bufB);
+        step(k + 1, bufB, bufA);
+      }
     }
     mfma_attend::write_partial<D>(st, c, G, part, nw);
   }
