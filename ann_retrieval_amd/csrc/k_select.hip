@@ -742,7 +742,9 @@ __device__ int select_head(const DevLayout& L, const void* blob, const T* Q, int
         if (cut >= 0) {
           if (tr && lane < beam) tr[cut * beam + lane] = id;
         } else if (lane < kpg) {
-          sel[((int64_t)h * G + g) * kpg + lane] = id;
+          // the fused step writes `sel` from sel_all once its attention is
+          // done: a global store here would hold the claim behind it
+          if (!cl) sel[((int64_t)h * G + g) * kpg + lane] = id;
           sel_all[g * kpg + lane] = id;
           if (cl) cl->sel_rows[g * kpg + lane] = lane < qc ? key_rows(ql) : 0;
         }
@@ -1107,13 +1109,14 @@ __global__ __launch_bounds__(1024) void k_decode(DevLayout L, const void* blob, 
   __syncthreads();
   mfma_attend::merge_partials<D>(G, part, nw, O + (int64_t)h * G * D, lse ? lse + (int64_t)h * G : nullptr,
                                  n_chunks);
-  // a union too long for one wave: written by the block from the selections
-  // (the selection's LDS is untouched by the attention)
-  if (G * kpg > 64) {
-    const SelLds S = sel_lds(G, max(beam, kpg), kpg, false);
+  // the selections (the selection's LDS is untouched by the attention); a
+  // union too long for one wave is written by the block from them
+  const SelLds S = sel_lds(G, max(beam, kpg), kpg, false);
+  const int32_t* sel_all = reinterpret_cast<const int32_t*>(smem + S.off_sel);
+  for (int i = threadIdx.x; i < G * kpg; i += blockDim.x) sel[(int64_t)h * G * kpg + i] = sel_all[i];
+  if (G * kpg > 64)
     write_union(G, kpg, reinterpret_cast<int32_t*>(smem + S.off_sel), reinterpret_cast<int32_t*>(smem + S.off_misc),
                 uni, n_uni, h, nullptr);
-  }
 }
 
 template <int D, class T>
