@@ -675,7 +675,12 @@ def build_timing(ix, w, builds):
         e1.record()
         e1.synchronize()
         tot.append(e0.elapsed_time(e1))
-    blob = ix.blob.clone()
+    # a copy in 128 MiB pieces: counter runs calibrate on whole 1 GiB copies
+    # and must not mistake this one for them
+    blob = torch.empty_like(ix.blob)
+    piece = 128 << 20
+    for i in range(0, ix.blob.numel(), piece):
+        blob[i:i + piece].copy_(ix.blob[i:i + piece])
     runs = [ix.ice_build_timed(w.K, w.V) for _ in range(builds)]
     same = bool(torch.equal(blob, ix.blob))
     del blob
