@@ -106,6 +106,27 @@ def test_pipelined_build_equals_one_stream(dtype, d, host_pool):
     gs.compare_decode(ix, refs, out)
 
 
+def test_pipelined_ranges_on_two_streams():
+    """Two ranges of 20 heads (each pipelined over ranges of its own) built at
+    the same time on two streams share the handle's one second stream; the
+    index equals a one-stream build bit for bit."""
+    from ann_retrieval_amd.api import IceIndex
+    H, N, d, seed = 40, 2400, 128, 33
+    say(f"pipelined ranges on two streams H={H} N={N} d={d} bf16")
+    w, gen = synth.clustered_kv(H, N, d, 24, "bf16", seed, device="cpu")
+    K, V = w.K.cuda(), w.V.cuda()
+    ix = IceIndex(H, 4, d, "bf16", N + 8, seed=seed, max_budget=256)
+    ix.ice_build_timed(K, V)
+    torch.cuda.synchronize()
+    one = ix.blob.clone()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(2):
+        for i, h0 in enumerate((0, 20)):
+            ix.ice_build_heads(K[h0:h0 + 20], V[h0:h0 + 20], h0, stream=streams[i])
+        torch.cuda.synchronize()
+        assert torch.equal(one, ix.blob), "concurrent pipelined range builds differ from the one-stream build"
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
 def test_reuse_layout_across_layers(dtype, d):
     """Heads 2, 3 (a second layer) take the layout of heads 0, 1 and their own
