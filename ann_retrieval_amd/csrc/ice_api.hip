@@ -383,21 +383,29 @@ constexpr int kMaxBuildChunks = 16;
 constexpr int kMinChunkHeads = 8;  // fewer heads per range: one stream
 static_assert(ICE_BUILD_CHUNKS >= 2 && ICE_BUILD_CHUNKS <= kMaxBuildChunks, "build ranges");
 
+hipError_t ensure_side(ice_index* idx);
+
 // Ranges a build of n_heads heads runs over (1: on the caller's stream alone,
-// also under stream capture and on a device other than the side stream's).
-int build_chunks(const ice_index* idx, int n_heads, hipStream_t s) {
+// also under stream capture, on a device other than the side stream's, and
+// when the side stream cannot be made). A query that fails leaves no error
+// behind for the build's own launch checks.
+int build_chunks(ice_index* idx, int n_heads, hipStream_t s) {
   if (idx->p.levels < 2) return 1;  // no parent search to overlap
   const int c = std::min(ICE_BUILD_CHUNKS, n_heads / kMinChunkHeads);
   if (c < 2) return 1;
   hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return 1;
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || (idx->side && dev != idx->side_dev)) return 1;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess || hipGetDevice(&dev) != hipSuccess || ensure_side(idx) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  if (st != hipStreamCaptureStatusNone || dev != idx->side_dev) return 1;
   return c;
 }
 
 // The side stream (default priority, not synchronising with the null stream)
-// and 2 + 2 * kMaxBuildChunks events without timing, made once per handle.
+// and 2 + 2 * kMaxBuildChunks events without timing, made once per handle on
+// the current device.
 hipError_t ensure_side(ice_index* idx) {
   if (idx->side) return hipSuccess;
   int dev = -1;
@@ -420,13 +428,13 @@ hipError_t ensure_side(ice_index* idx) {
 }
 
 // The build of the range L (already offset to its first head: blob, ws, K,
-// V) as `chunks` ranges on the caller's stream s and the side stream. s
+// V) as `chunks` ranges on the caller's stream s and the side stream (made
+// by build_chunks). s
 // continues after all of it (the side stream's last event), also when a
 // launch fails part way.
 hipError_t build_pipelined(ice_index* idx, const DevLayout& L, char* blob, const void* K, const void* V, int n,
                            int64_t hstride, char* ws, bool keep, hipStream_t s, int chunks) {
-  hipError_t e = ensure_side(idx);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   const int per = (L.H + chunks - 1) / chunks;
   chunks = (L.H + per - 1) / per;
   hipStream_t t = idx->side;
