@@ -94,3 +94,26 @@ def test_resident_argument_errors():
         ix.set_dense([True])                           # wrong length
     assert ix.stats(0)["n_resident"] == 0
 
+
+
+def test_pipelined_rebuild_keeps_resident_and_dense():
+    """A rebuild of 24 heads runs as the two-stream pipeline over 3 ranges; it
+    keeps every head's resident tokens and dense flag like the one-stream
+    rebuild, and the heads at the ranges' edges decode as the oracle does."""
+    H, N, G = 24, 2000, 4
+    w, gen, ix = build_case(H, N, 128, "bf16", 16, 23, G=G, budget=128, resident=48)
+    heads = [0, 7, 8, 15, 16, 23]
+    refs = check_build(w, ix, heads, 23, 3, 4)
+    Kr, Vr = synth.resident_tokens(w, 40, gen)
+    dense = [h % 5 == 3 for h in range(H)]
+    say(f"pipelined rebuild H={H}: resident 40, dense heads {[h for h in range(H) if dense[h]]}")
+    ix.set_dense(dense)
+    ix.set_resident(Kr.cuda(), Vr.cuda())
+    ix.ice_build(w.K.cuda(), w.V.cuda())
+    torch.cuda.synchronize()
+    assert [bool(ix.stats(h)["dense"]) for h in range(H)] == dense
+    assert all(ix.stats(h)["n_resident"] == 40 for h in range(H))
+    Q = synth.decode_queries(w, G, gen)
+    out = gs.run_decode(ix, Q, 128, 8)
+    gs.compare_decode(ix, {h: refs[h] for h in heads}, out, resident=(Kr, Vr),
+                      dense={h for h in heads if dense[h]})
