@@ -99,6 +99,7 @@ def test_max_group_beam_budget():
     dict(dtype="bf16", G=8, budget=256, beam=16, d=128),      # union longer than a wave (G*k = 128)
     dict(dtype="bf16", G=16, budget=128, beam=8, d=64),       # union longer than a wave (G*k = 128)
     dict(dtype="bf16", G=16, budget=64, beam=4, d=64),
+    dict(dtype="bf16", G=16, budget=256, beam=16, d=64),      # the longest fused union (G*k = 256)
     dict(dtype="bf16", G=5, budget=128, beam=8, d=128),       # 3 waves per query head
     dict(dtype="bf16", G=2, budget=256, beam=100, d=128),     # long lists: the two-kernel path
     dict(dtype="bf16", G=16, budget=128, beam=8, d=128),      # LDS too small for one kernel: two kernels
